@@ -1,0 +1,331 @@
+/*
+ * CPU oracle for block-scaled FP8 (E4M3) quantization and FP8 GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow reference that the
+ * GPU library is checked against.  Only the test suite, the smoke entry point
+ * and the CPU-baseline leg of the benchmark may load it; the product path
+ * never does.  It shares no code, header, table or constant generator with
+ * the HIP kernels.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC
+ *   (no FMA contraction, no flush-to-zero: every float operation below rounds
+ *   once, to nearest-even, exactly as written).
+ *
+ * Sources of each definition (the web pages on FP8 training):
+ *  - E4M3 = 4 exponent bits + 3 mantissa bits, finite range [-448, 448]:
+ *    "FP8-RL" article, section 一 (weight sync); FP8-LM review, section 三
+ *    (FP8 data formats); Introl FP8 infrastructure guide, section on the
+ *    numerical-precision landscape.
+ *  - Quantization is x_fp8 = Cast_FP8(x / s): FP8-LM review, section 三
+ *    (tensor scaling formula).
+ *  - A BF16 tensor becomes an FP8 tensor plus a smaller, wider-range scale
+ *    tensor: Ling 2.0 FP8 blog, "where does the precision worry come from".
+ *  - Fine-grained tile/block scales, one scale per tile: Ling 2.0 FP8 blog,
+ *    "fine-grained quantization (per-tile/block wise scaling)"; 128x128
+ *    weight blocks: "FP8-RL" article, section 一.
+ *  - FP8 GEMM accumulates in FP32: Ling 2.0 FP8 blog, "where is error
+ *    introduced".
+ * Readings where the pages are silent (each listed in the design notes):
+ *  scale s = amax/448 in fp32, stored as the dequantisation multiplier;
+ *  x/s is an IEEE fp32 quotient, then rounded to E4M3 nearest-even with
+ *  saturation at 448 (two-step rounding); OCP E4M3FN encoding (bias 7,
+ *  subnormals, no infinities, NaN = S.1111.111); a zero tile (or a scale that
+ *  underflows to 0) gets s = 0 and signed-zero codes; the GEMM adds each
+ *  128-wide K chunk's fp32 partial sum, times SA*SB, into an fp32
+ *  accumulator, in ascending k and chunk order, without FMA.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* E4M3 codec (OCP E4M3FN)                                              */
+/* ------------------------------------------------------------------ */
+
+/* Decode: sign s, exponent field e (4 bits, bias 7), mantissa m (3 bits).
+ * e == 0 is subnormal: m * 2^-9.  e == 15 && m == 7 is NaN. */
+float orc_e4m3_decode(uint8_t c)
+{
+    int s = c >> 7;
+    int e = (c >> 3) & 15;
+    int m = c & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return s ? -NAN : NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return (float)(s ? -v : v);
+}
+
+/* Round a non-negative double t (with few significant bits) to the nearest
+ * integer, ties to even. */
+static double round_half_even(double t)
+{
+    double fl = floor(t);
+    double fr = t - fl;
+    if (fr > 0.5)
+        return fl + 1.0;
+    if (fr < 0.5)
+        return fl;
+    return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+}
+
+/* Encode an fp32 value: round to nearest E4M3 value, ties to the code with
+ * an even mantissa LSB; magnitudes above 448 saturate to 448; the sign bit
+ * of the code is the sign bit of v (so -0 and negative underflow give 0x80).
+ * NaN maps to the NaN code with v's sign (outside the GPU contract). */
+uint8_t orc_e4m3_encode(float v)
+{
+    uint32_t bits;
+    memcpy(&bits, &v, 4);
+    uint8_t sign = (uint8_t)((bits >> 31) << 7);
+    if (isnan(v))
+        return sign | 0x7F;
+    double a = fabs((double)v);
+    if (a > 448.0)
+        return sign | 0x7E;
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal range: multiples of 2^-9; q == 8 is the min normal */
+        double q = round_half_even(a * 512.0);
+        return sign | (uint8_t)q;
+    }
+    int ex;
+    double f = frexp(a, &ex);   /* a = f * 2^ex, f in [0.5, 1) */
+    int e = ex - 1;             /* a = (2f) * 2^e, 2f in [1, 2) */
+    double q = round_half_even((2.0 * f - 1.0) * 8.0);
+    if (q == 8.0) {
+        e += 1;
+        q = 0.0;
+    }
+    return sign | (uint8_t)((e + 7) << 3) | (uint8_t)q;
+}
+
+void orc_decode_array(const uint8_t* c, int64_t n, float* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_e4m3_decode(c[i]);
+}
+
+void orc_encode_array(const float* v, int64_t n, uint8_t* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_e4m3_encode(v[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* Tile quantization                                                    */
+/* ------------------------------------------------------------------ */
+
+/* Quantize X[rows][cols] (row-major, contiguous fp32) with tiles of
+ * tr rows x tc cols.  Tiles start at row 0 / col 0; tiles on the bottom and
+ * right edges are clipped to the matrix.  For every tile:
+ *   amax = max |x| over the tile (fp32),  s = amax / 448 (fp32 division),
+ *   q    = encode(fp32(x / s))            (or signed zero if s == 0).
+ * Outputs: q[rows][cols], s[ceil(rows/tr)][ceil(cols/tc)]. */
+void orc_quant_tiles(const float* x, int64_t rows, int64_t cols, int64_t tr,
+                     int64_t tc, uint8_t* q, float* s)
+{
+    int64_t tiles_r = (rows + tr - 1) / tr;
+    int64_t tiles_c = (cols + tc - 1) / tc;
+#pragma omp parallel for collapse(2) schedule(dynamic, 16)
+    for (int64_t ti = 0; ti < tiles_r; ++ti) {
+        for (int64_t tj = 0; tj < tiles_c; ++tj) {
+            int64_t r0 = ti * tr, r1 = r0 + tr < rows ? r0 + tr : rows;
+            int64_t c0 = tj * tc, c1 = c0 + tc < cols ? c0 + tc : cols;
+            float amax = 0.0f;
+            for (int64_t r = r0; r < r1; ++r)
+                for (int64_t c = c0; c < c1; ++c) {
+                    float a = fabsf(x[r * cols + c]);
+                    if (a > amax)
+                        amax = a;
+                }
+            float scale = amax / 448.0f;
+            s[ti * tiles_c + tj] = scale;
+            for (int64_t r = r0; r < r1; ++r)
+                for (int64_t c = c0; c < c1; ++c) {
+                    float v = x[r * cols + c];
+                    uint8_t code;
+                    if (scale == 0.0f) {
+                        code = signbit(v) ? 0x80 : 0x00;
+                    } else {
+                        float t = v / scale;
+                        code = orc_e4m3_encode(t);
+                    }
+                    q[r * cols + c] = code;
+                }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Block-scaled GEMM                                                    */
+/* ------------------------------------------------------------------ */
+
+/* C[i][n] for the requested rows m = rows[i] (all rows if rows == NULL):
+ *   C[m][n] = sum over chunks kb (ascending) of
+ *             (sum over k in chunk kb (ascending) of dec(A[m][k]) * dec(B[n][k]))
+ *             * (SA[m][kb] * SB[n][kb])
+ * A[M][K] and B[N][K] are E4M3 codes with the contraction axis contiguous.
+ * SA[M][KB] and SB[N][KB] are the scales already expanded to one value per
+ * (row, chunk) and (column, chunk); KB = ceil(K / 128) and the last chunk
+ * may be shorter than 128.  Every product of two E4M3 values is exact in
+ * fp32; each addition and multiplication below rounds once (fp32). */
+void orc_gemm_f32(int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                  const float* SA, const uint8_t* B, const float* SB,
+                  const int64_t* rows, int64_t nrows, float* C)
+{
+    (void)M;
+    const int64_t KB = (K + 127) / 128;
+    float dec[256];
+    for (int c = 0; c < 256; ++c)
+        dec[c] = orc_e4m3_decode((uint8_t)c);
+    /* B decoded and stored k-major so the n loop is contiguous */
+    float* BT = (float*)malloc(sizeof(float) * (size_t)K * (size_t)N);
+    float* SBT = (float*)malloc(sizeof(float) * (size_t)KB * (size_t)N);
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            BT[k * N + n] = dec[B[n * K + k]];
+    for (int64_t kb = 0; kb < KB; ++kb)
+        for (int64_t n = 0; n < N; ++n)
+            SBT[kb * N + n] = SB[n * KB + kb];
+#pragma omp parallel
+    {
+        float* p = (float*)malloc(sizeof(float) * (size_t)N);
+        float* acc = (float*)malloc(sizeof(float) * (size_t)N);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < nrows; ++i) {
+            int64_t m = rows ? rows[i] : i;
+            for (int64_t n = 0; n < N; ++n)
+                acc[n] = 0.0f;
+            for (int64_t kb = 0; kb < KB; ++kb) {
+                int64_t k0 = kb * 128, k1 = k0 + 128 < K ? k0 + 128 : K;
+                for (int64_t n = 0; n < N; ++n)
+                    p[n] = 0.0f;
+                for (int64_t k = k0; k < k1; ++k) {
+                    float a = dec[A[m * K + k]];
+                    const float* bt = BT + k * N;
+                    for (int64_t n = 0; n < N; ++n)
+                        p[n] = p[n] + a * bt[n];
+                }
+                float sa = SA[m * KB + kb];
+                const float* sb = SBT + kb * N;
+                for (int64_t n = 0; n < N; ++n) {
+                    float t = sa * sb[n];
+                    acc[n] = acc[n] + p[n] * t;
+                }
+            }
+            memcpy(C + i * N, acc, sizeof(float) * (size_t)N);
+        }
+        free(p);
+        free(acc);
+    }
+    free(BT);
+    free(SBT);
+}
+
+/* The same sum carried out in fp64 (the near-exact value of the definition),
+ * plus the absolute-product sum
+ *   R[m][n] = sum_kb |SA[m][kb] * SB[n][kb]| * sum_k |dec(A[m][k]) * dec(B[n][k])|
+ * which bounds the rounding error of any fp32 evaluation order. */
+void orc_gemm_f64(int64_t M, int64_t N, int64_t K, const uint8_t* A,
+                  const float* SA, const uint8_t* B, const float* SB,
+                  const int64_t* rows, int64_t nrows, double* C, double* R)
+{
+    (void)M;
+    const int64_t KB = (K + 127) / 128;
+    double dec[256];
+    for (int c = 0; c < 256; ++c)
+        dec[c] = (double)orc_e4m3_decode((uint8_t)c);
+    double* BT = (double*)malloc(sizeof(double) * (size_t)K * (size_t)N);
+    double* SBT = (double*)malloc(sizeof(double) * (size_t)KB * (size_t)N);
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n)
+            BT[k * N + n] = dec[B[n * K + k]];
+    for (int64_t kb = 0; kb < KB; ++kb)
+        for (int64_t n = 0; n < N; ++n)
+            SBT[kb * N + n] = (double)SB[n * KB + kb];
+#pragma omp parallel
+    {
+        double* p = (double*)malloc(sizeof(double) * (size_t)N);
+        double* pa = (double*)malloc(sizeof(double) * (size_t)N);
+        double* acc = (double*)malloc(sizeof(double) * (size_t)N);
+        double* racc = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < nrows; ++i) {
+            int64_t m = rows ? rows[i] : i;
+            for (int64_t n = 0; n < N; ++n) {
+                acc[n] = 0.0;
+                racc[n] = 0.0;
+            }
+            for (int64_t kb = 0; kb < KB; ++kb) {
+                int64_t k0 = kb * 128, k1 = k0 + 128 < K ? k0 + 128 : K;
+                for (int64_t n = 0; n < N; ++n) {
+                    p[n] = 0.0;
+                    pa[n] = 0.0;
+                }
+                for (int64_t k = k0; k < k1; ++k) {
+                    double a = dec[A[m * K + k]];
+                    const double* bt = BT + k * N;
+                    for (int64_t n = 0; n < N; ++n) {
+                        p[n] += a * bt[n];
+                        pa[n] += fabs(a * bt[n]);
+                    }
+                }
+                double sa = (double)SA[m * KB + kb];
+                const double* sb = SBT + kb * N;
+                for (int64_t n = 0; n < N; ++n) {
+                    double t = sa * sb[n];
+                    acc[n] += p[n] * t;
+                    racc[n] += pa[n] * fabs(t);
+                }
+            }
+            memcpy(C + i * N, acc, sizeof(double) * (size_t)N);
+            memcpy(R + i * N, racc, sizeof(double) * (size_t)N);
+        }
+        free(p);
+        free(pa);
+        free(acc);
+        free(racc);
+    }
+    free(BT);
+    free(SBT);
+}
+
+/* fp32 -> bf16 bit pattern, round to nearest even (finite inputs). */
+void orc_f32_to_bf16(const float* x, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t u;
+        memcpy(&u, &x[i], 4);
+        uint32_t lower = u & 0xFFFFu;
+        uint32_t upper = u >> 16;
+        if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+            upper += 1u;
+        out[i] = (uint16_t)upper;
+    }
+}
+
+/* Number of elements with x != 0 whose code decodes to zero (underflow),
+ * and the number of non-zero x.  Underflow as defined in the Ling 2.0 FP8
+ * blog ("where is error introduced"): a non-zero element that becomes 0
+ * after quantization. */
+void orc_underflow_count(const float* x, const uint8_t* q, int64_t n,
+                         int64_t* n_underflow, int64_t* n_nonzero)
+{
+    int64_t u = 0, nz = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (x[i] != 0.0f) {
+            nz++;
+            if ((q[i] & 0x7F) == 0)
+                u++;
+        }
+    }
+    *n_underflow = u;
+    *n_nonzero = nz;
+}
