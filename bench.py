@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 linear-layer hot path on one MI355X.
+
+One step = one training pass of an FP8 Linear with block-scaled E4M3
+operands on the MLP up-projection shape (x [4096 x 4096] bf16 ~N(0,1),
+W [14336 x 4096] bf16 ~N(0,0.02), dy [4096 x 14336] bf16 ~1e-3 N(0,1) with
+0.1% heavy-tailed outliers):
+
+  forward   qx,sx   = quant 1x128 (x)              y  = gemm(qx, qW^T)   bf16 out
+            qW,sW   = quant 128x128 (W)
+  backward  dy      -> quant + transpose (rows and columns)
+            x       -> transposed quantization (columns)
+            dx = gemm(q_row(dy), qW stored [N][K] read as KN)          bf16 out
+            dW = gemm(q_colT(dy), q_colT(x), row x row scales)          fp32 out
+
+All inputs are resident in HBM before the timed region.  `value` is the
+GEMM work of the step (3 x 2*M*N*K) divided by the wall time of the whole
+step, quantizers included.  The roofline entry covers the kernel that takes
+the most time in the step; the per-kernel breakdown is reported alongside.
+The CPU baseline times the oracle on a bounded sample of the same step.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-scaled FP8 GEMM TFLOPS (% FP8 MFMA peak); quantizer GB/s (% HBM)"
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+
+M, N, K = 4096, 14336, 4096     # tokens, out features (14336), in features
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=8,
+                   help="output rows per GEMM in the oracle's timed sample")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU; --gpus %d is not supported "
+              "(the design notes describe how the path would shard)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_precision_quant_amd as fq
+    import synthetic
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def bf16_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x_bits, w_bits = synthetic.mlp_forward(M, N, K)
+    dy_bits = synthetic.mlp_backward_dy(M, N)
+    x, w, dy = bf16_dev(x_bits), bf16_dev(w_bits), bf16_dev(dy_bits)
+
+    u8, f32 = torch.uint8, torch.float32
+    KB, NB, MB = K // 128, N // 128, M // 128
+    qx, sx = torch.empty((M, K), dtype=u8, device=dev), torch.empty((M, KB), dtype=f32, device=dev)
+    qw, sw = torch.empty((N, K), dtype=u8, device=dev), torch.empty((NB, KB), dtype=f32, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    qdy, sdy = torch.empty((M, N), dtype=u8, device=dev), torch.empty((M, NB), dtype=f32, device=dev)
+    qdyT, sdyT = torch.empty((N, M), dtype=u8, device=dev), torch.empty((N, MB), dtype=f32, device=dev)
+    qxT, sxT = torch.empty((K, M), dtype=u8, device=dev), torch.empty((K, MB), dtype=f32, device=dev)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dW = torch.empty((N, K), dtype=f32, device=dev)
+
+    gemm_flops = 2.0 * M * N * K
+    # algorithmic bytes: what each kernel must read and write at least
+    ops = [
+        ("quant_1x128 x", lambda: fq.fp8_quant_blockwise(x, fq.ROW_1x128, q=qx, s=sx),
+         "hbm", M * K * 2 + M * K + M * KB * 4),
+        ("quant_128x128 W", lambda: fq.fp8_quant_blockwise(w, fq.BLOCK_128x128, q=qw, s=sw),
+         "hbm", N * K * 2 + N * K + NB * KB * 4),
+        ("gemm fwd y=xW^T", lambda: fq.fp8_gemm_blockscaled(qx, sx, fq.ROW_1x128, qw, sw,
+                                                           fq.BLOCK_128x128, fq.B_NK, c=y),
+         "mfma", gemm_flops),
+        ("quant_transpose dy", lambda: fq.fp8_quant_transpose(dy, out=(qdy, sdy, qdyT, sdyT)),
+         "hbm", M * N * 2 + 2 * M * N + 4 * (M * NB + N * MB)),
+        ("quant_transpose x (columns)", lambda: fq.fp8_quant_transpose(
+            x, rows_out=False, out=(None, None, qxT, sxT)),
+         "hbm", M * K * 2 + M * K + 4 * K * MB),
+        ("gemm dgrad dx=dyW", lambda: fq.fp8_gemm_blockscaled(qdy, sdy, fq.ROW_1x128, qw, sw,
+                                                             fq.BLOCK_128x128, fq.B_KN, c=dx),
+         "mfma", gemm_flops),
+        ("gemm wgrad dW=dy^T x", lambda: fq.fp8_gemm_blockscaled(qdyT, sdyT, fq.ROW_1x128, qxT, sxT,
+                                                                fq.ROW_1x128, fq.B_NK, c=dW),
+         "mfma", gemm_flops),
+    ]
+
+    def step():
+        for _, fn, _, _ in ops:
+            fn()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: the whole step, K times, bracketed by synchronizations
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, (_, fn, _, _) in enumerate(ops):
+            fn()
+            ev[s][i + 1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    per_op_ms = np.zeros(len(ops))
+    for s in range(args.steps):
+        for i in range(len(ops)):
+            per_op_ms[i] += ev[s][i].elapsed_time(ev[s][i + 1])
+    per_op_ms /= args.steps
+
+    step_flops = 3 * gemm_flops
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    breakdown = []
+    for (name, _, bound, work), t in zip(ops, per_op_ms):
+        if bound == "mfma":
+            ach = work / (t * 1e-3) / 1e12
+            breakdown.append({"kernel": name, "us": round(t * 1e3, 2), "TFLOP/s": round(ach, 1),
+                              "frac_peak": round(ach / PEAK_FP8_TFLOPS, 4)})
+        else:
+            ach = work / (t * 1e-3) / 1e9
+            breakdown.append({"kernel": name, "us": round(t * 1e3, 2), "GB/s": round(ach, 1),
+                              "frac_peak": round(ach / PEAK_HBM_GBS, 4)})
+    dom = int(np.argmax(per_op_ms))
+    dname, _, dbound, dwork = ops[dom]
+    dt = per_op_ms[dom] * 1e-3
+    if dbound == "mfma":
+        roofline = {"bound": "mfma", "achieved": round(dwork / dt / 1e12, 2), "peak": PEAK_FP8_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(dwork / dt / 1e12 / PEAK_FP8_TFLOPS, 4),
+                    "traffic": None, "kernel": dname}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(dwork / dt / 1e9, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(dwork / dt / 1e9 / PEAK_HBM_GBS, 4),
+                    "traffic": None, "kernel": dname}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(x_bits, w_bits, dy_bits, args.cpu_rows)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 x fp8-e4m3 -> f32 accumulate",
+        "data": "synthetic (seeded numpy; no dataset)",
+        "config": {"workload": "FP8 linear fwd+bwd, MLP up-proj x[4096x4096] W[14336x4096] dy[4096x14336], "
+                               "1x128 act/grad tiles, 128x128 weight blocks, E4M3",
+                   "M": M, "N": N, "K": K, "gemm_flops_per_step": step_flops,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "kernels": breakdown,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline(x_bits, w_bits, dy_bits, rows_per_gemm):
+    """The oracle on a bounded sample of the same step: full-tensor quantizers
+    for x (1x128) and W (128x128) and the three GEMMs on `rows_per_gemm`
+    output rows each; reported as GEMM TFLOP/s of the sample."""
+    import oracle
+    import synthetic
+
+    t0 = time.perf_counter()
+    xf = synthetic.bf16_to_f32(x_bits)
+    wf = synthetic.bf16_to_f32(w_bits)
+    t_q0 = time.perf_counter()
+    qx, sx = oracle.quant_1x128(xf)
+    qw, sw = oracle.quant_128x128(wf)
+    t_q = time.perf_counter() - t_q0
+    q_bytes = xf.size * 3 + wf.size * 3
+    dyf = synthetic.bf16_to_f32(dy_bits)
+    t_t0 = time.perf_counter()
+    qdy, sdy, qdyT, sdyT = oracle.quant_transpose(dyf)
+    _, _, qxT, sxT = oracle.quant_transpose(xf)
+    t_t = time.perf_counter() - t_t0
+    rows = synthetic.sample_rows(M, rows_per_gemm, 7)
+    rows_w = synthetic.sample_rows(N, rows_per_gemm, 8)
+    t_g0 = time.perf_counter()
+    oracle.gemm_blockscaled(qx, sx, "row", qw, sw, "block", "NK", rows=rows)
+    oracle.gemm_blockscaled(qdy, sdy, "row", qw, sw, "block", "KN", rows=rows)
+    oracle.gemm_blockscaled(qdyT, sdyT, "row", qxT, sxT, "row", "NK", rows=rows_w)
+    t_g = time.perf_counter() - t_g0
+    flops = 2.0 * rows_per_gemm * N * K + 2.0 * rows_per_gemm * K * N + 2.0 * rows_per_gemm * K * M
+    return {"value": round(flops / t_g / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "quant 1x128 x + 128x128 W (full tensors, %.1f GB/s), quant+transpose of dy and x "
+                      "(full, %.2f s), and fwd/dgrad/wgrad GEMMs on %d sampled output rows each "
+                      "(%.2f s); value = GEMM FLOPs of the sample / GEMM time"
+                      % (q_bytes / t_q / 1e9, t_t, rows_per_gemm, t_g),
+            "total_s": round(time.perf_counter() - t0, 2)}
+
+
+if __name__ == "__main__":
+    main()

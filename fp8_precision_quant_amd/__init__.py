@@ -1,0 +1,196 @@
+"""Block-scaled FP8 (E4M3) quantization and FP8 GEMM on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libfp8q.so`` (declared in
+``include/fp8q.h``).  The functions carry the C names and only marshal
+arguments: torch supplies device memory and the current stream, every step
+of the computation runs in the HIP kernels.  There is no fallback: if the
+library is missing the import of this module raises.
+
+Codes are ``torch.uint8`` tensors holding OCP E4M3FN bytes (view them as
+``torch.float8_e4m3fn`` if desired); scales are ``torch.float32``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8q.so")
+
+# enums of include/fp8q.h
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_DEVICE, ERR_LAUNCH = range(7)
+F32, BF16 = 0, 1
+ROW_1x128, BLOCK_128x128, TENSOR = 0, 1, 2
+B_NK, B_KN = 0, 1
+
+TILE = 128
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libfp8q.so is not built (expected at %s); run "
+        "`python -m fp8_precision_quant_amd.build`" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+_i64, _int, _p = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+_lib.fp8_quant_blockwise.argtypes = [_p, _int, _i64, _i64, _i64, _int, _p, _i64, _p, _i64, _p]
+_lib.fp8_quant_transpose.argtypes = [_p, _int, _i64, _i64, _i64,
+                                     _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+_lib.fp8_gemm_blockscaled.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _int,
+                                      _p, _i64, _int, _p, _i64, _int, _p, _i64, _int, _p]
+_lib.fp8_grouped_gemm.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _p,
+                                  _p, _p, _p, _i64, _int, _p]
+for _f in ("fp8_quant_blockwise", "fp8_quant_transpose", "fp8_gemm_blockscaled",
+           "fp8_grouped_gemm"):
+    getattr(_lib, _f).restype = _int
+_lib.fp8q_status_string.argtypes = [_int]
+_lib.fp8q_status_string.restype = ctypes.c_char_p
+
+SYMBOLS = ("fp8_quant_blockwise", "fp8_quant_transpose", "fp8_gemm_blockscaled",
+           "fp8_grouped_gemm", "fp8q_status_string")
+
+
+class Fp8qError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s" % (where, fp8q_status_string(status)))
+
+
+def fp8q_status_string(status: int) -> str:
+    return _lib.fp8q_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise Fp8qError(status, where)
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _ld(t: torch.Tensor) -> int:
+    """Row stride (elements) of a 2-D tensor with unit column stride."""
+    if t.dim() != 2 or (t.size(1) > 1 and t.stride(1) != 1):
+        raise ValueError("expected a 2-D tensor with contiguous rows, got shape %s strides %s"
+                         % (tuple(t.shape), t.stride()))
+    return t.stride(0) if t.size(0) > 1 else max(t.stride(0), t.size(1))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError("unsupported input dtype %s" % t.dtype)
+
+
+def _cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def _empty_aligned(rows: int, cols: int, dtype, device, align_elems: int) -> torch.Tensor:
+    """[rows, cols] view with a row stride rounded up to `align_elems`."""
+    ld = _cdiv(max(cols, 1), align_elems) * align_elems
+    return torch.empty((rows, ld), dtype=dtype, device=device)[:, :cols]
+
+
+def fp8_quant_blockwise(x: torch.Tensor, kind: int = ROW_1x128, q: Optional[torch.Tensor] = None,
+                        s: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Quantize ``x[rows, cols]`` (bf16 or fp32) to E4M3 codes and fp32 scales.
+
+    ``kind``: ROW_1x128 -> s[rows, ceil(cols/128)]; BLOCK_128x128 ->
+    s[ceil(rows/128), ceil(cols/128)]; TENSOR -> s[1, 1].
+    """
+    rows, cols = x.shape
+    if q is None:
+        q = _empty_aligned(rows, cols, torch.uint8, x.device, 16)
+    if s is None:
+        shape = {ROW_1x128: (rows, _cdiv(cols, TILE)),
+                 BLOCK_128x128: (_cdiv(rows, TILE), _cdiv(cols, TILE)),
+                 TENSOR: (1, 1)}[kind]
+        s = torch.empty(shape, dtype=torch.float32, device=x.device)
+    st = _lib.fp8_quant_blockwise(_ptr(x), _dtype_code(x), rows, cols, _ld(x), kind,
+                                  _ptr(q), _ld(q), _ptr(s), _ld(s) if s.dim() == 2 else 1,
+                                  _stream(x.device, stream))
+    _check(st, "fp8_quant_blockwise")
+    return q, s
+
+
+def fp8_quant_transpose(x: torch.Tensor, rows_out: bool = True, cols_out: bool = True,
+                        out: Optional[tuple] = None, stream=None):
+    """One read of ``x[R, C]`` -> (q_row[R, C], s_row[R, ceil(C/128)],
+    q_colT[C, R], s_colT[C, ceil(R/128)]); a skipped pair is returned as None."""
+    R, C = x.shape
+    if out is not None:
+        q_row, s_row, q_colT, s_colT = out
+    else:
+        q_row = _empty_aligned(R, C, torch.uint8, x.device, 16) if rows_out else None
+        s_row = torch.empty((R, _cdiv(C, TILE)), dtype=torch.float32, device=x.device) if rows_out else None
+        q_colT = _empty_aligned(C, R, torch.uint8, x.device, 16) if cols_out else None
+        s_colT = torch.empty((C, _cdiv(R, TILE)), dtype=torch.float32, device=x.device) if cols_out else None
+    st = _lib.fp8_quant_transpose(
+        _ptr(x), _dtype_code(x), R, C, _ld(x),
+        _ptr(q_row), _ld(q_row) if q_row is not None else 0,
+        _ptr(s_row), _ld(s_row) if s_row is not None else 0,
+        _ptr(q_colT), _ld(q_colT) if q_colT is not None else 0,
+        _ptr(s_colT), _ld(s_colT) if s_colT is not None else 0,
+        _stream(x.device, stream))
+    _check(st, "fp8_quant_transpose")
+    return q_row, s_row, q_colT, s_colT
+
+
+def fp8_gemm_blockscaled(a: torch.Tensor, sa: torch.Tensor, sa_kind: int,
+                         b: torch.Tensor, sb: torch.Tensor, sb_kind: int, b_layout: int = B_NK,
+                         out_dtype: torch.dtype = torch.bfloat16, c: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """C[M, N] = block-scaled product of ``a[M, K]`` codes and ``b`` codes
+    (``b[N, K]`` for B_NK, ``b[K, N]`` for B_KN) with their scale grids."""
+    M, K = a.shape
+    N = b.shape[0] if b_layout == B_NK else b.shape[1]
+    if (b.shape[1] if b_layout == B_NK else b.shape[0]) != K:
+        raise ValueError("contraction sizes differ: a %s, b %s" % (tuple(a.shape), tuple(b.shape)))
+    if c is None:
+        c = _empty_aligned(M, N, out_dtype, a.device, 16 // (4 if out_dtype == torch.float32 else 2))
+    cd = F32 if c.dtype == torch.float32 else BF16
+    if c.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("output dtype must be float32 or bfloat16")
+    ldsa = _ld(sa) if sa.dim() == 2 else 1
+    ldsb = _ld(sb) if sb.dim() == 2 else 1
+    st = _lib.fp8_gemm_blockscaled(M, N, K, _ptr(a), _ld(a), _ptr(sa), ldsa, sa_kind,
+                                   _ptr(b), _ld(b), b_layout, _ptr(sb), ldsb, sb_kind,
+                                   _ptr(c), _ld(c), cd, _stream(a.device, stream))
+    _check(st, "fp8_gemm_blockscaled")
+    return c
+
+
+def fp8_grouped_gemm(a: torch.Tensor, sa: torch.Tensor, group_offsets: torch.Tensor,
+                     b: torch.Tensor, sb: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                     c: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Per group e: rows [off[e], off[e+1]) of ``a[M_pad, K]`` times ``b[e]``
+    (``b[G, N, K]`` codes, ``sb[G, ceil(N/128), ceil(K/128)]`` scales);
+    ``group_offsets`` is an int32 device tensor of G+1 entries."""
+    M_pad, K = a.shape
+    G, N, Kb = b.shape
+    if Kb != K:
+        raise ValueError("contraction sizes differ")
+    if group_offsets.dtype != torch.int32 or group_offsets.numel() != G + 1:
+        raise ValueError("group_offsets must be int32 with G+1 entries")
+    if not (b.is_contiguous() and sb.is_contiguous() and group_offsets.is_contiguous()):
+        raise ValueError("b, sb and group_offsets must be contiguous")
+    if c is None:
+        c = _empty_aligned(M_pad, N, out_dtype, a.device, 16 // (4 if out_dtype == torch.float32 else 2))
+    cd = F32 if c.dtype == torch.float32 else BF16
+    st = _lib.fp8_grouped_gemm(G, M_pad, N, K, _ptr(a), _ld(a), _ptr(sa), _ld(sa),
+                               _ptr(group_offsets), _ptr(b), _ptr(sb), _ptr(c), _ld(c), cd,
+                               _stream(a.device, stream))
+    _check(st, "fp8_grouped_gemm")
+    return c

@@ -1,0 +1,187 @@
+// C ABI of libfp8q: argument validation, device check, dispatch.
+//
+// Every entry point validates all of its arguments on the host before it
+// enqueues anything, never allocates or synchronizes, and reports a pending
+// launch error as FP8Q_ERR_LAUNCH.  Operation semantics are documented in
+// include/fp8q.h.
+#include <atomic>
+#include <cstring>
+
+#include "fp8q_internal.h"
+
+namespace {
+
+constexpr int64_t kTile = 128;
+constexpr int64_t kMaxGridY = 65535;
+constexpr int64_t kMaxIndex = (int64_t)1 << 31;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_size(int dtype) { return dtype == FP8Q_BF16 ? 2 : 4; }
+
+bool dtype_ok(int d) { return d == FP8Q_F32 || d == FP8Q_BF16; }
+
+// Per-device cache: 0 = unknown, 1 = gfx950, 2 = other / query failed.
+std::atomic<int> g_arch_state[64];
+
+int check_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return FP8Q_ERR_DEVICE;
+    }
+    if (dev >= 64) return FP8Q_ERR_DEVICE;
+    int st = g_arch_state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            st = 2;
+        } else {
+            st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        }
+        g_arch_state[dev].store(st, std::memory_order_release);
+    }
+    return st == 1 ? FP8Q_OK : FP8Q_ERR_DEVICE;
+}
+
+int launch_status()
+{
+    return hipGetLastError() == hipSuccess ? FP8Q_OK : FP8Q_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8q_status_string(int status)
+{
+    switch (status) {
+    case FP8Q_OK: return "FP8Q_OK";
+    case FP8Q_ERR_NULL: return "FP8Q_ERR_NULL: a required pointer is NULL";
+    case FP8Q_ERR_SHAPE: return "FP8Q_ERR_SHAPE: invalid size, leading dimension or grid size";
+    case FP8Q_ERR_ALIGN: return "FP8Q_ERR_ALIGN: pointer or row stride not 16-byte aligned";
+    case FP8Q_ERR_UNSUPPORTED: return "FP8Q_ERR_UNSUPPORTED: unsupported dtype, scale kind or layout";
+    case FP8Q_ERR_DEVICE: return "FP8Q_ERR_DEVICE: current device is not gfx950 or not available";
+    case FP8Q_ERR_LAUNCH: return "FP8Q_ERR_LAUNCH: kernel launch failed";
+    default: return "unknown fp8q status";
+    }
+}
+
+int fp8_quant_blockwise(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                        int kind, uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream)
+{
+    if (!dtype_ok(x_dtype)) return FP8Q_ERR_UNSUPPORTED;
+    if (kind != FP8Q_ROW_1x128 && kind != FP8Q_BLOCK_128x128 && kind != FP8Q_TENSOR)
+        return FP8Q_ERR_UNSUPPORTED;
+    if (rows < 0 || cols < 0) return FP8Q_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return FP8Q_OK;
+    if (!x || !q || !s) return FP8Q_ERR_NULL;
+    const int64_t tiles_c = cdiv(cols, kTile);
+    if (ldx < cols || ldq < cols) return FP8Q_ERR_SHAPE;
+    if (kind != FP8Q_TENSOR && lds < tiles_c) return FP8Q_ERR_SHAPE;
+    if (kind == FP8Q_ROW_1x128 && rows * tiles_c >= kMaxIndex) return FP8Q_ERR_SHAPE;
+    if (kind == FP8Q_BLOCK_128x128 && (cdiv(rows, kTile) > kMaxGridY || tiles_c >= kMaxIndex))
+        return FP8Q_ERR_SHAPE;
+    if (kind == FP8Q_TENSOR && rows * cdiv(cols, 8) >= kMaxIndex) return FP8Q_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(q) || (ldx * elem_size(x_dtype)) % 16 || ldq % 16)
+        return FP8Q_ERR_ALIGN;
+    if (kind == FP8Q_TENSOR && (reinterpret_cast<uintptr_t>(s) & 3u)) return FP8Q_ERR_ALIGN;
+    int st = check_device();
+    if (st != FP8Q_OK) return st;
+    fp8q::launch_quant_blockwise(x, x_dtype, rows, cols, ldx, kind, q, ldq, s, lds,
+                                 static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+int fp8_quant_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                        uint8_t* q_row, int64_t ldq_row, float* s_row, int64_t lds_row,
+                        uint8_t* q_colT, int64_t ldq_colT, float* s_colT, int64_t lds_colT,
+                        void* stream)
+{
+    if (!dtype_ok(x_dtype)) return FP8Q_ERR_UNSUPPORTED;
+    if (rows < 0 || cols < 0) return FP8Q_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return FP8Q_OK;
+    const bool want_row = q_row || s_row;
+    const bool want_col = q_colT || s_colT;
+    if (!x) return FP8Q_ERR_NULL;
+    if (want_row && (!q_row || !s_row)) return FP8Q_ERR_NULL;
+    if (want_col && (!q_colT || !s_colT)) return FP8Q_ERR_NULL;
+    if (!want_row && !want_col) return FP8Q_OK;
+    if (ldx < cols) return FP8Q_ERR_SHAPE;
+    if (want_row && (ldq_row < cols || lds_row < cdiv(cols, kTile))) return FP8Q_ERR_SHAPE;
+    if (want_col && (ldq_colT < rows || lds_colT < cdiv(rows, kTile))) return FP8Q_ERR_SHAPE;
+    if (cdiv(rows, kTile) > kMaxGridY || cdiv(cols, kTile) >= kMaxIndex) return FP8Q_ERR_SHAPE;
+    if (!aligned16(x) || (ldx * elem_size(x_dtype)) % 16) return FP8Q_ERR_ALIGN;
+    if (want_row && (!aligned16(q_row) || ldq_row % 16)) return FP8Q_ERR_ALIGN;
+    if (want_col && (!aligned16(q_colT) || ldq_colT % 16)) return FP8Q_ERR_ALIGN;
+    int st = check_device();
+    if (st != FP8Q_OK) return st;
+    fp8q::launch_quant_transpose(x, x_dtype, rows, cols, ldx, want_row ? q_row : nullptr, ldq_row,
+                                 s_row, lds_row, want_col ? q_colT : nullptr, ldq_colT, s_colT,
+                                 lds_colT, static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K,
+                         const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, int sa_kind,
+                         const uint8_t* b, int64_t ldb, int b_layout,
+                         const float* sb, int64_t ldsb, int sb_kind,
+                         void* c, int64_t ldc, int c_dtype, void* stream)
+{
+    if (!dtype_ok(c_dtype)) return FP8Q_ERR_UNSUPPORTED;
+    if (b_layout != FP8Q_B_NK && b_layout != FP8Q_B_KN) return FP8Q_ERR_UNSUPPORTED;
+    if (sa_kind != FP8Q_ROW_1x128 && sa_kind != FP8Q_TENSOR) return FP8Q_ERR_UNSUPPORTED;
+    if (sb_kind != FP8Q_ROW_1x128 && sb_kind != FP8Q_BLOCK_128x128 && sb_kind != FP8Q_TENSOR)
+        return FP8Q_ERR_UNSUPPORTED;
+    if (sb_kind == FP8Q_ROW_1x128 && b_layout == FP8Q_B_KN) return FP8Q_ERR_UNSUPPORTED;
+    if (M < 0 || N < 0 || K < 0) return FP8Q_ERR_SHAPE;
+    if (M == 0 || N == 0) return FP8Q_OK;
+    if (!c) return FP8Q_ERR_NULL;
+    // with K == 0 the operands and scales hold no data and are never read
+    if (K > 0 && (!a || !b || !sa || !sb)) return FP8Q_ERR_NULL;
+    const int64_t KB = cdiv(K, kTile);
+    if (lda < K || ldc < N) return FP8Q_ERR_SHAPE;
+    if (b_layout == FP8Q_B_NK ? ldb < K : ldb < N) return FP8Q_ERR_SHAPE;
+    if (sa_kind == FP8Q_ROW_1x128 && ldsa < KB) return FP8Q_ERR_SHAPE;
+    if (sb_kind == FP8Q_ROW_1x128 && ldsb < KB) return FP8Q_ERR_SHAPE;
+    if (sb_kind == FP8Q_BLOCK_128x128 && (b_layout == FP8Q_B_NK ? ldsb < KB : ldsb < cdiv(N, kTile)))
+        return FP8Q_ERR_SHAPE;
+    if (cdiv(M, 256) * cdiv(N, 128) >= kMaxIndex || KB >= kMaxIndex) return FP8Q_ERR_SHAPE;
+    if (!aligned16(c) || (ldc * elem_size(c_dtype)) % 16) return FP8Q_ERR_ALIGN;
+    if (K > 0 && (!aligned16(a) || !aligned16(b) || lda % 16 || ldb % 16)) return FP8Q_ERR_ALIGN;
+    int st = check_device();
+    if (st != FP8Q_OK) return st;
+    fp8q::launch_gemm(M, N, K, a, lda, sa, ldsa, sa_kind, b, ldb, b_layout, sb, ldsb, sb_kind, c,
+                      ldc, c_dtype, static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+int fp8_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K,
+                     const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                     const int32_t* group_offsets,
+                     const uint8_t* b, const float* sb,
+                     void* c, int64_t ldc, int c_dtype, void* stream)
+{
+    if (!dtype_ok(c_dtype)) return FP8Q_ERR_UNSUPPORTED;
+    if (G < 1 || M_pad < 0 || N < 0 || K < 0 || M_pad % kTile) return FP8Q_ERR_SHAPE;
+    if (M_pad == 0 || N == 0) return FP8Q_OK;
+    if (!group_offsets || !c) return FP8Q_ERR_NULL;
+    if (K > 0 && (!a || !sa || !b || !sb)) return FP8Q_ERR_NULL;
+    const int64_t KB = cdiv(K, kTile);
+    if (lda < K || ldc < N || ldsa < KB) return FP8Q_ERR_SHAPE;
+    if (G >= kMaxIndex || (M_pad / kTile) * cdiv(N, 128) >= kMaxIndex) return FP8Q_ERR_SHAPE;
+    if (!aligned16(c) || K % 16 || (ldc * elem_size(c_dtype)) % 16) return FP8Q_ERR_ALIGN;
+    if (K > 0 && (!aligned16(a) || !aligned16(b) || lda % 16)) return FP8Q_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(group_offsets) & 3u) return FP8Q_ERR_ALIGN;
+    int st = check_device();
+    if (st != FP8Q_OK) return st;
+    fp8q::launch_grouped_gemm(G, M_pad, N, K, a, lda, sa, ldsa, group_offsets, b, sb, c, ldc,
+                              c_dtype, static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,118 @@
+// Device-side helpers shared by the gfx950 kernels of libfp8q.
+//
+// Quantization rule (FP8-LM review, section 三: x_fp8 = Cast_FP8(x / s)),
+// with s = amax / 448 per tile; E4M3 range [-448, 448] ("FP8-RL" article,
+// section 一).  The cast is round-to-nearest-even with saturation; the fp32
+// quotient x / s is rounded once (IEEE) before the cast.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 128;
+constexpr float kE4M3Max = 448.0f;
+// Below this scale the corrected-reciprocal quotient can lose its exact
+// residual; such tiles divide with the IEEE quotient instead.
+constexpr float kFastScaleMin = 0x1p-90f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+// |x| max across the 16 lanes of a DPP row (lanes 16r .. 16r+15).  All lanes
+// of the wave must be active.
+__device__ __forceinline__ float dpp_max16(float v)
+{
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));  // quad [1,0,3,2]
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));  // quad [2,3,0,1]
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false))); // half-row mirror
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false))); // row mirror
+    return v;
+}
+
+// Per-tile quantization constants: the scale s, its correctly rounded
+// reciprocal y, and which division path the tile takes.
+struct TileScale {
+    float s;
+    float y;
+    int mode;   // 0: s == 0 (signed zeros), 1: corrected reciprocal, 2: IEEE quotient
+};
+
+__device__ __forceinline__ TileScale make_scale(float amax)
+{
+    TileScale t;
+    t.s = amax / kE4M3Max;                 // IEEE fp32 division
+    t.mode = t.s == 0.0f ? 0 : (t.s >= kFastScaleMin ? 1 : 2);
+    t.y = t.mode == 1 ? 1.0f / t.s : 0.0f; // IEEE fp32 reciprocal
+    return t;
+}
+
+// RN_fp32(x / s).  mode 1: q0 = RN(x*y) is within an ulp of x/s, the
+// residual e = q0*s - x is exact (FMA, no underflow for s >= 2^-90 and the
+// quotients that can round to a non-zero code), and RN(q0 - e*y) is the
+// correctly rounded quotient (Markstein's theorem; Muller et al., Handbook
+// of Floating-Point Arithmetic, division with an FMA).  The residual is
+// formed as q0*s - x rather than x - q0*s so that x = -0 yields -0 (the sum
+// of opposite zeros rounds to +0).
+__device__ __forceinline__ float quotient(float x, const TileScale& t)
+{
+    if (t.mode == 1) {
+        float q0 = x * t.y;
+        float e = __builtin_fmaf(q0, t.s, -x);
+        return __builtin_fmaf(-e, t.y, q0);
+    }
+    return x / t.s;
+}
+
+// Four fp32 values -> four E4M3 codes packed little-endian in a dword.
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d)
+{
+    a = __builtin_amdgcn_fmed3f(a, -kE4M3Max, kE4M3Max);
+    b = __builtin_amdgcn_fmed3f(b, -kE4M3Max, kE4M3Max);
+    c = __builtin_amdgcn_fmed3f(c, -kE4M3Max, kE4M3Max);
+    d = __builtin_amdgcn_fmed3f(d, -kE4M3Max, kE4M3Max);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+// Quantize four values of one tile.
+__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, const TileScale& t)
+{
+    if (t.mode == 0) {
+        return ((__float_as_uint(a) >> 31) << 7) | ((__float_as_uint(b) >> 31) << 15) |
+               ((__float_as_uint(c) >> 31) << 23) | ((__float_as_uint(d) >> 31) << 31);
+    }
+    return pack4_e4m3(quotient(a, t), quotient(b, t), quotient(c, t), quotient(d, t));
+}
+
+// Magic-number unsigned division by a runtime constant (Granlund-Montgomery),
+// for 32-bit numerators.
+struct FastDiv {
+    uint32_t d, m, sh;
+};
+
+__host__ inline FastDiv make_fastdiv(uint32_t d)
+{
+    FastDiv f;
+    f.d = d;
+    uint32_t s = 0;
+    while ((1ull << s) < d) ++s;
+    f.sh = s;
+    f.m = (uint32_t)((((1ull << 32) * ((1ull << s) - d)) / d) + 1);
+    return f;
+}
+
+__host__ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f)
+{
+    if (f.d == 1)
+        return n;
+    uint32_t t = (uint32_t)(((uint64_t)n * f.m) >> 32);
+    return (t + ((n - t) >> 1)) >> (f.sh - 1);
+}
+
+}  // namespace fp8q

@@ -1,0 +1,32 @@
+// Internal launcher declarations of libfp8q (host side).  Every launcher
+// assumes its arguments were validated by the C-ABI layer and only enqueues
+// kernels on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fp8q.h"
+
+namespace fp8q {
+
+void launch_quant_blockwise(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                            int kind, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                            hipStream_t st);
+
+void launch_quant_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                            uint8_t* q_row, int64_t ldq_row, float* s_row, int64_t lds_row,
+                            uint8_t* q_colT, int64_t ldq_colT, float* s_colT, int64_t lds_colT,
+                            hipStream_t st);
+
+void launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const float* sa,
+                 int64_t ldsa, int sa_kind, const uint8_t* b, int64_t ldb, int b_layout,
+                 const float* sb, int64_t ldsb, int sb_kind, void* c, int64_t ldc, int c_dtype,
+                 hipStream_t st);
+
+void launch_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K, const uint8_t* a,
+                         int64_t lda, const float* sa, int64_t ldsa, const int32_t* offsets,
+                         const uint8_t* b, const float* sb, void* c, int64_t ldc, int c_dtype,
+                         hipStream_t st);
+
+}  // namespace fp8q

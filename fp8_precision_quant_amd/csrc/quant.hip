@@ -1,0 +1,291 @@
+// Tile quantizers for gfx950: 1x128 row tiles, 128x128 blocks and one scale
+// per tensor.
+//
+// Per tile: amax = max |x|, s = amax / 448, code = E4M3(RN(x / s)) (FP8-LM
+// review, section 三, tensor scaling; Ling 2.0 FP8 blog, fine-grained
+// per-tile/block scaling; 128x128 weight blocks: "FP8-RL" article, section
+// 一).  These kernels are HBM-bound streams: 16-byte loads and stores, the
+// amax reduction in registers and DPP, no LDS round trip for row tiles.
+#include "fp8q_device.h"
+#include "fp8q_internal.h"
+
+namespace fp8q {
+
+// ---------------------------------------------------------------------------
+// loading 8 consecutive elements as fp32
+// ---------------------------------------------------------------------------
+
+// Loads elements [c, c+8) of a row into v[0..7]; elements at or beyond `cols`
+// read as 0 (the 16-byte vectors never cross ld, see the ABI).
+template <typename T>
+__device__ __forceinline__ void load8(const T* row, int64_t c, int64_t cols, float v[8]);
+
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* row, int64_t c, int64_t cols, float v[8])
+{
+    if (c >= cols) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+        return;
+    }
+    uint4 p = *reinterpret_cast<const uint4*>(row + c);
+    v[0] = bf16_lo(p.x); v[1] = bf16_hi(p.x);
+    v[2] = bf16_lo(p.y); v[3] = bf16_hi(p.y);
+    v[4] = bf16_lo(p.z); v[5] = bf16_hi(p.z);
+    v[6] = bf16_lo(p.w); v[7] = bf16_hi(p.w);
+    if (c + 8 > cols) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (c + i >= cols) v[i] = 0.0f;
+    }
+}
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* row, int64_t c, int64_t cols, float v[8])
+{
+    if (c >= cols) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+        return;
+    }
+    float4 a = *reinterpret_cast<const float4*>(row + c);
+    float4 b = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c + 4 < cols) b = *reinterpret_cast<const float4*>(row + c + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    if (c + 8 > cols) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (c + i >= cols) v[i] = 0.0f;
+    }
+}
+
+__device__ __forceinline__ float absmax8(const float v[8])
+{
+    float m = fmaxf(fabsf(v[0]), fabsf(v[1]));
+    m = fmaxf(m, fmaxf(fabsf(v[2]), fabsf(v[3])));
+    m = fmaxf(m, fmaxf(fabsf(v[4]), fabsf(v[5])));
+    m = fmaxf(m, fmaxf(fabsf(v[6]), fabsf(v[7])));
+    return m;
+}
+
+// Stores 8 codes at q[c..c+8), clipped at `cols`.
+__device__ __forceinline__ void store8(uint8_t* qrow, int64_t c, int64_t cols, uint32_t lo, uint32_t hi)
+{
+    if (c + 8 <= cols) {
+        *reinterpret_cast<uint2*>(qrow + c) = make_uint2(lo, hi);
+    } else {
+        for (int i = 0; i < 8 && c + i < cols; ++i)
+            qrow[c + i] = (uint8_t)((i < 4 ? lo >> (8 * i) : hi >> (8 * (i - 4))) & 0xFF);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 1x128 row tiles
+// ---------------------------------------------------------------------------
+// A 16-lane DPP row owns one tile (8 elements per lane).  A 256-thread
+// workgroup covers 16 consecutive tiles per step and runs kRowUnroll steps
+// with all loads issued first, so each lane keeps kRowUnroll 16-byte loads
+// (32 for fp32 input) in flight.
+
+constexpr int kRowThreads = 256;
+constexpr int kRowUnroll = 4;
+constexpr int kRowTilesPerBlock = (kRowThreads / 16) * kRowUnroll;
+
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void quant_row_kernel(
+    const T* __restrict__ x, int64_t cols, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+    float* __restrict__ s, int64_t lds, uint32_t total_tiles, FastDiv tiles_per_row)
+{
+    const int lane16 = threadIdx.x & 15;
+    const int group = threadIdx.x >> 4;
+    const uint32_t base = blockIdx.x * kRowTilesPerBlock;
+
+    float v[kRowUnroll][8];
+    uint32_t row[kRowUnroll], tcol[kRowUnroll];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+        uint32_t t = base + u * (kRowThreads / 16) + group;
+        bool live = t < total_tiles;
+        uint32_t r = fdiv(live ? t : 0, tiles_per_row);
+        row[u] = r;
+        tcol[u] = (live ? t : 0) - r * tiles_per_row.d;
+        int64_t c = (int64_t)tcol[u] * kTile + lane16 * 8;
+        load8<T>(x + (int64_t)r * ldx, live ? c : cols, cols, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+        uint32_t t = base + u * (kRowThreads / 16) + group;
+        float amax = dpp_max16(absmax8(v[u]));
+        TileScale ts = make_scale(amax);
+        if (t < total_tiles) {
+            int64_t c = (int64_t)tcol[u] * kTile + lane16 * 8;
+            uint32_t lo = quant4(v[u][0], v[u][1], v[u][2], v[u][3], ts);
+            uint32_t hi = quant4(v[u][4], v[u][5], v[u][6], v[u][7], ts);
+            if (c < cols)
+                store8(q + (int64_t)row[u] * ldq, c, cols, lo, hi);
+            if (lane16 == 0)
+                s[(int64_t)row[u] * lds + tcol[u]] = ts.s;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 blocks
+// ---------------------------------------------------------------------------
+// One 256-thread workgroup per block: thread (g = tid/16, l = tid%16) holds
+// rows g, g+16, ..., g+112 at columns 8l..8l+7 (64 values in registers), the
+// block amax is reduced with DPP, readlane and LDS, then every value is cast.
+
+constexpr int kBlockThreads = 256;
+
+template <typename T>
+__global__ __launch_bounds__(kBlockThreads) void quant_block_kernel(
+    const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ s, int64_t lds)
+{
+    __shared__ float wave_max[kBlockThreads / 64];
+    const int l = threadIdx.x & 15;
+    const int g = threadIdx.x >> 4;
+    const int64_t r0 = (int64_t)blockIdx.y * kTile;
+    const int64_t c = (int64_t)blockIdx.x * kTile + l * 8;
+
+    float v[8][8];
+    float m = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        int64_t r = r0 + g + 16 * u;
+        load8<T>(x + (r < rows ? r : 0) * ldx, r < rows ? c : cols, cols, v[u]);
+        m = fmaxf(m, absmax8(v[u]));
+    }
+    m = dpp_max16(m);
+    m = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0)),
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16))),
+              fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32)),
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 48))));
+    if ((threadIdx.x & 63) == 0)
+        wave_max[threadIdx.x >> 6] = m;
+    __syncthreads();
+    float amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+    TileScale ts = make_scale(amax);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        int64_t r = r0 + g + 16 * u;
+        uint32_t lo = quant4(v[u][0], v[u][1], v[u][2], v[u][3], ts);
+        uint32_t hi = quant4(v[u][4], v[u][5], v[u][6], v[u][7], ts);
+        if (r < rows && c < cols)
+            store8(q + r * ldq, c, cols, lo, hi);
+    }
+    if (threadIdx.x == 0)
+        s[(int64_t)blockIdx.y * lds + blockIdx.x] = ts.s;
+}
+
+// ---------------------------------------------------------------------------
+// one scale per tensor: fill -> amax (atomic max on the fp32 bits, which
+// order like the values for non-negative floats) -> cast -> store the scale.
+// s[0] holds the amax bits until the last kernel replaces it by amax/448.
+// ---------------------------------------------------------------------------
+
+__global__ void tensor_fill_kernel(uint32_t* cell) { *cell = 0u; }
+
+constexpr int kTensorThreads = 256;
+
+template <typename T>
+__global__ __launch_bounds__(kTensorThreads) void tensor_amax_kernel(
+    const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, uint32_t* cell,
+    FastDiv chunks_per_row, uint32_t total_chunks)
+{
+    __shared__ float wave_max[kTensorThreads / 64];
+    float m = 0.0f;
+    for (uint32_t i = blockIdx.x * kTensorThreads + threadIdx.x; i < total_chunks;
+         i += gridDim.x * kTensorThreads) {
+        uint32_t r = fdiv(i, chunks_per_row);
+        int64_t c = (int64_t)(i - r * chunks_per_row.d) * 8;
+        float v[8];
+        load8<T>(x + (int64_t)r * ldx, c, cols, v);
+        m = fmaxf(m, absmax8(v));
+    }
+    m = dpp_max16(m);
+    m = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0)),
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16))),
+              fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32)),
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 48))));
+    if ((threadIdx.x & 63) == 0)
+        wave_max[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float b = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+        atomicMax(cell, __float_as_uint(b));
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kTensorThreads) void tensor_cast_kernel(
+    const T* __restrict__ x, int64_t cols, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+    const uint32_t* cell, FastDiv chunks_per_row, uint32_t total_chunks)
+{
+    TileScale ts = make_scale(__uint_as_float(*cell));
+    for (uint32_t i = blockIdx.x * kTensorThreads + threadIdx.x; i < total_chunks;
+         i += gridDim.x * kTensorThreads) {
+        uint32_t r = fdiv(i, chunks_per_row);
+        int64_t c = (int64_t)(i - r * chunks_per_row.d) * 8;
+        float v[8];
+        load8<T>(x + (int64_t)r * ldx, c, cols, v);
+        uint32_t lo = quant4(v[0], v[1], v[2], v[3], ts);
+        uint32_t hi = quant4(v[4], v[5], v[6], v[7], ts);
+        store8(q + (int64_t)r * ldq, c, cols, lo, hi);
+    }
+}
+
+__global__ void tensor_finish_kernel(uint32_t* cell)
+{
+    float amax = __uint_as_float(*cell);
+    *reinterpret_cast<float*>(cell) = amax / kE4M3Max;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+template <typename T>
+static void launch_quant(const void* xv, int64_t rows, int64_t cols, int64_t ldx, int kind,
+                         uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st)
+{
+    const T* x = static_cast<const T*>(xv);
+    const int64_t tiles_c = (cols + kTile - 1) / kTile;
+    if (kind == FP8Q_ROW_1x128) {
+        uint32_t total = (uint32_t)(rows * tiles_c);
+        uint32_t blocks = (total + kRowTilesPerBlock - 1) / kRowTilesPerBlock;
+        hipLaunchKernelGGL(quant_row_kernel<T>, dim3(blocks), dim3(kRowThreads), 0, st, x, cols,
+                           ldx, q, ldq, s, lds, total, make_fastdiv((uint32_t)tiles_c));
+    } else if (kind == FP8Q_BLOCK_128x128) {
+        dim3 grid((uint32_t)tiles_c, (uint32_t)((rows + kTile - 1) / kTile));
+        hipLaunchKernelGGL(quant_block_kernel<T>, grid, dim3(kBlockThreads), 0, st, x, rows, cols,
+                           ldx, q, ldq, s, lds);
+    } else {
+        uint32_t* cell = reinterpret_cast<uint32_t*>(s);
+        int64_t cpr = (cols + 7) / 8;
+        uint32_t total = (uint32_t)(rows * cpr);
+        uint32_t blocks = (total + kTensorThreads - 1) / kTensorThreads;
+        if (blocks > 4096) blocks = 4096;
+        FastDiv fd = make_fastdiv((uint32_t)cpr);
+        hipLaunchKernelGGL(tensor_fill_kernel, dim3(1), dim3(1), 0, st, cell);
+        hipLaunchKernelGGL(tensor_amax_kernel<T>, dim3(blocks), dim3(kTensorThreads), 0, st, x,
+                           rows, cols, ldx, cell, fd, total);
+        hipLaunchKernelGGL(tensor_cast_kernel<T>, dim3(blocks), dim3(kTensorThreads), 0, st, x,
+                           cols, ldx, q, ldq, cell, fd, total);
+        hipLaunchKernelGGL(tensor_finish_kernel, dim3(1), dim3(1), 0, st, cell);
+    }
+}
+
+void launch_quant_blockwise(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                            int kind, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                            hipStream_t st)
+{
+    if (x_dtype == FP8Q_BF16)
+        launch_quant<uint16_t>(x, rows, cols, ldx, kind, q, ldq, s, lds, st);
+    else
+        launch_quant<float>(x, rows, cols, ldx, kind, q, ldq, s, lds, st);
+}
+
+}  // namespace fp8q

@@ -1,0 +1,185 @@
+/*
+ * fp8q.h -- block-scaled FP8 (E4M3) quantization and FP8 GEMM for AMD
+ * Instinct MI355X (gfx950).  C ABI of libfp8q.so.
+ *
+ * What is computed (the web pages on FP8 training):
+ *  - A high-precision tensor becomes an FP8 tensor plus a much smaller,
+ *    wider-range scale tensor ("quantization"); dequantization is the inverse
+ *    (Ling 2.0 FP8 blog, "where does the precision worry come from").
+ *  - The rule is x_fp8 = Cast_FP8(x / s) (FP8-LM review, section 三, tensor
+ *    scaling).  E4M3 has 4 exponent bits and 3 mantissa bits and covers
+ *    [-448, 448] ("FP8-RL" article, section 一; FP8-LM review, section 三).
+ *  - Scales are kept per tile / per block so that outliers only affect their
+ *    own tile (Ling 2.0 FP8 blog, "fine-grained quantization"); weights use
+ *    128x128 blocks ("FP8-RL" article, section 一); activations and gradients
+ *    are quantized dynamically (same section) with 1x128 tiles.
+ *  - The FP8 GEMM accumulates in FP32 (Ling 2.0 FP8 blog, "where is error
+ *    introduced").  dgrad reads the weight in its stored layout instead of a
+ *    cached transposed copy, and wgrad consumes a transposed re-quantization
+ *    of the gradient (Ling 2.0 FP8 blog, "FP8 on-demand transpose weight" and
+ *    the underflow monitor of "grad (transpose)").  MoE experts run as one
+ *    grouped GEMM over groups padded to the kernel's row multiple (Ling 2.0
+ *    FP8 blog, "FP8 padding routing map").
+ *
+ * Numerics (exact contract; the CPU oracle implements the same definitions):
+ *  - Codes are OCP E4M3FN bytes (bias 7, subnormals, no infinities, NaN =
+ *    S.1111.111), the same bytes as torch.float8_e4m3fn.
+ *  - Per tile: amax = max |x| (fp32; bf16 inputs widen exactly),
+ *    s = amax / 448 (IEEE fp32 division), code = E4M3(RN_fp32(x / s)) with
+ *    round-to-nearest-even and saturation at +-448; the code's sign bit is the
+ *    sign bit of x.  If s == 0 (zero tile, or amax so small that amax/448
+ *    underflows) every code is a signed zero.  s is stored as-is: it is the
+ *    dequantization multiplier (x ~= dec(code) * s).
+ *  - GEMM: C[m][n] = sum over K-chunks kb of 128 (the last may be shorter) of
+ *    SA(m,kb) * SB(n,kb) * sum_{k in kb} dec(A[m][k]) * dec(B^[n][k]),
+ *    products exact, fp32 partial sums, fp32 accumulator; summation order
+ *    inside a chunk is the hardware's.  BF16 output is the fp32 result
+ *    rounded to nearest even.
+ *  - Inputs must be finite; NaN/Inf inputs give unspecified codes.
+ *
+ * Conventions for every entry point:
+ *  - All data pointers are DEVICE pointers to memory on the current HIP
+ *    device.  The library never allocates, frees, synchronizes or keeps a
+ *    pointer after returning; all work is enqueued on `stream` (a
+ *    hipStream_t, or NULL for the default stream).  The caller keeps every
+ *    buffer alive until the stream has finished the work.
+ *  - Matrices are row-major with a leading dimension `ld*` in ELEMENTS.
+ *    Every matrix pointer must be 16-byte aligned and ld * element_size must
+ *    be a multiple of 16 bytes.  Inputs may be read up to the 16-byte
+ *    boundary past the last column of a row (never past ld); outputs are
+ *    written exactly in [0, rows) x [0, cols).  Scale grids have no alignment
+ *    requirement (4-byte floats).
+ *  - Shapes may be any size >= 0 (ragged edge tiles are clipped); a call with
+ *    an empty output returns FP8Q_OK without launching anything.  A GEMM
+ *    with K == 0 writes zeros; its operand and scale pointers may then be
+ *    NULL (they are not read).
+ *  - Arguments are validated on the host before any launch; a failing call
+ *    returns its status and enqueues nothing.  After launching, a pending
+ *    launch error is reported as FP8Q_ERR_LAUNCH.
+ *  - Calls are stateless and thread-safe (the only state is a per-device
+ *    architecture check cached at first use).
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP8Q_OK = 0,
+    FP8Q_ERR_NULL = 1,        /* a required pointer is NULL */
+    FP8Q_ERR_SHAPE = 2,       /* negative size, ld too small, or grid/offset size mismatch */
+    FP8Q_ERR_ALIGN = 3,       /* pointer not 16-byte aligned or ld*elem not a multiple of 16 */
+    FP8Q_ERR_UNSUPPORTED = 4, /* unsupported dtype / scale kind / layout combination */
+    FP8Q_ERR_DEVICE = 5,      /* current device is not gfx950, or a HIP query failed */
+    FP8Q_ERR_LAUNCH = 6       /* a kernel launch failed */
+} fp8q_status;
+
+typedef enum { FP8Q_F32 = 0, FP8Q_BF16 = 1 } fp8q_dtype;
+
+typedef enum {
+    FP8Q_ROW_1x128 = 0,     /* tile = 1 row x 128 columns; s[r * lds + c/128] */
+    FP8Q_BLOCK_128x128 = 1, /* tile = 128 x 128;           s[(r/128) * lds + c/128] */
+    FP8Q_TENSOR = 2         /* one tile = the whole matrix; s[0] */
+} fp8q_scale_kind;
+
+typedef enum {
+    FP8Q_B_NK = 0, /* B stored [N][K]: B^[n][k] = b[n * ldb + k]  (y = x W^T, wgrad) */
+    FP8Q_B_KN = 1  /* B stored [K][N]: B^[n][k] = b[k * ldb + n]  (dgrad: dx = dy W)  */
+} fp8q_b_layout;
+
+/*
+ * fp8_quant_blockwise -- quantize X[rows][cols] to E4M3 codes + fp32 scales.
+ *
+ *  x       : input, x_dtype (FP8Q_F32 or FP8Q_BF16), row stride ldx >= cols.
+ *  kind    : FP8Q_ROW_1x128 (activations, gradients), FP8Q_BLOCK_128x128
+ *            (weights) or FP8Q_TENSOR (one scale; comparison baseline).
+ *  q       : output codes [rows][cols], row stride ldq >= cols.
+ *  s       : output scales.  ROW: [rows][ceil(cols/128)] with row stride
+ *            lds >= ceil(cols/128).  BLOCK: [ceil(rows/128)][ceil(cols/128)]
+ *            with row stride lds.  TENSOR: s[0] (lds ignored); s[0] is also
+ *            used as the amax cell while the call runs.
+ * Tiles start at row 0 / column 0 and are clipped at the matrix edge.
+ */
+int fp8_quant_blockwise(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                        int kind, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                        void* stream);
+
+/*
+ * fp8_quant_transpose -- one read of X[rows][cols] produces both
+ *   (i)  row tiles along cols:   q_row[rows][cols],   s_row[rows][ceil(cols/128)]
+ *   (ii) column tiles along rows, stored transposed, i.e. the 1x128 row tiles
+ *        of X^T:                 q_colT[cols][rows],  s_colT[cols][ceil(rows/128)]
+ * (ii) is the operand of the weight-gradient GEMM (contraction over tokens);
+ * it is re-quantized from the high-precision input, never transposed codes.
+ * Either output pair may be NULL (both pointers of the pair) to skip it.
+ * Strides: ldq_row >= cols, lds_row >= ceil(cols/128), ldq_colT >= rows,
+ * lds_colT >= ceil(rows/128).  x_dtype is FP8Q_F32 or FP8Q_BF16.
+ */
+int fp8_quant_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                        uint8_t* q_row, int64_t ldq_row, float* s_row, int64_t lds_row,
+                        uint8_t* q_colT, int64_t ldq_colT, float* s_colT, int64_t lds_colT,
+                        void* stream);
+
+/*
+ * fp8_gemm_blockscaled -- C[M][N] = block-scaled FP8 product (see Numerics).
+ *
+ *  a, lda        : A codes [M][K], contraction axis contiguous.
+ *  sa, ldsa      : A scales. sa_kind FP8Q_ROW_1x128: SA(m,kb) = sa[m*ldsa + kb]
+ *                  (ldsa >= ceil(K/128)); FP8Q_TENSOR: SA = sa[0].
+ *  b, ldb        : B codes, b_layout FP8Q_B_NK ([N][K], ldb >= K) or
+ *                  FP8Q_B_KN ([K][N], ldb >= N).
+ *  sb, ldsb      : B scales. sb_kind
+ *                  FP8Q_BLOCK_128x128, NK: SB(n,kb) = sb[(n/128)*ldsb + kb]
+ *                  FP8Q_BLOCK_128x128, KN: SB(n,kb) = sb[kb*ldsb + n/128]
+ *                     (the block grid follows B's storage, so the weight's
+ *                      own scales serve dgrad without a transposed copy)
+ *                  FP8Q_ROW_1x128, NK only: SB(n,kb) = sb[n*ldsb + kb] (wgrad)
+ *                  FP8Q_TENSOR: SB = sb[0].
+ *  c, ldc, c_dtype : output [M][N], FP8Q_F32 or FP8Q_BF16, ldc >= N.
+ * Typical uses: forward y = x W^T (ROW x BLOCK, NK); dgrad dx = dy W
+ * (ROW x BLOCK, KN); wgrad dW = dy^T x (ROW x ROW, NK, operands from
+ * fp8_quant_transpose's column outputs).
+ */
+int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K,
+                         const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, int sa_kind,
+                         const uint8_t* b, int64_t ldb, int b_layout,
+                         const float* sb, int64_t ldsb, int sb_kind,
+                         void* c, int64_t ldc, int c_dtype, void* stream);
+
+/*
+ * fp8_grouped_gemm -- MoE expert GEMM over padded groups.
+ *
+ * For each group e in [0, G): rows [off[e], off[e+1]) of A times expert
+ * weights B[e]:  C[m][n] = block-scaled product of A[m][:] (1x128 scales) and
+ * B[e][n][:] (128x128 block scales).
+ *  a, lda, sa, ldsa : A codes [M_pad][K] (contiguous groups), scales
+ *                     sa[m*ldsa + kb].
+ *  group_offsets    : DEVICE int32[G+1]; off[0] = 0, off[G] = M_pad,
+ *                     non-decreasing, every off[e] a multiple of 128 (the
+ *                     caller pads each group with zero rows; zero codes with
+ *                     s = 0 give zero output rows).  This device-side
+ *                     contract is the caller's: rows outside [0, off[G]) are
+ *                     not written.
+ *  b                : B codes [G][N][K] (each expert NK, row stride K; K % 16 == 0).
+ *  sb               : B scales [G][ceil(N/128)][ceil(K/128)], contiguous.
+ *  c, ldc, c_dtype  : output [M_pad][N].
+ * M_pad must be a multiple of 128.
+ */
+int fp8_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K,
+                     const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                     const int32_t* group_offsets,
+                     const uint8_t* b, const float* sb,
+                     void* c, int64_t ldc, int c_dtype, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* fp8q_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

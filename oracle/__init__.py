@@ -69,8 +69,14 @@ def lib() -> ctypes.CDLL:
             L.orc_gemm_f64.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p, p]
             L.orc_f32_to_bf16.argtypes = [p, i64, p]
             L.orc_underflow_count.argtypes = [p, p, i64, p, p]
+            L.orc_num_threads.restype = ctypes.c_int
             _lib = L
     return _lib
+
+
+def num_threads() -> int:
+    """Threads the oracle's parallel loops use."""
+    return int(lib().orc_num_threads())
 
 
 def _ptr(a: np.ndarray) -> int:

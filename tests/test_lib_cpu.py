@@ -1,0 +1,144 @@
+"""The C-ABI library on the host: it loads, exports every function that
+include/fp8q.h declares, and rejects bad arguments with the documented
+status before touching a device (no kernel is launched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import fp8_precision_quant_amd as fq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8q.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert names == sorted(["fp8_quant_blockwise", "fp8_quant_transpose", "fp8_gemm_blockscaled",
+                            "fp8_grouped_gemm", "fp8q_status_string"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fq.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(fq.SYMBOLS) == set(declared_functions())
+
+
+def test_status_strings():
+    for st in range(7):
+        assert fq.fp8q_status_string(st).startswith("FP8Q_")
+    assert "unknown" in fq.fp8q_status_string(99)
+
+
+L = fq._lib
+A16 = 0x10000          # fake, 16-byte aligned device addresses: never dereferenced
+MIS = 0x10004          # misaligned
+
+
+def q_blockwise(**kw):
+    args = dict(x=A16, dt=fq.BF16, rows=4, cols=256, ldx=256, kind=fq.ROW_1x128,
+                q=A16, ldq=256, s=A16, lds=2, stream=None)
+    args.update(kw)
+    return L.fp8_quant_blockwise(args["x"], args["dt"], args["rows"], args["cols"], args["ldx"],
+                                 args["kind"], args["q"], args["ldq"], args["s"], args["lds"],
+                                 args["stream"])
+
+
+def test_quant_blockwise_validation():
+    assert q_blockwise(dt=7) == fq.ERR_UNSUPPORTED
+    assert q_blockwise(kind=9) == fq.ERR_UNSUPPORTED
+    assert q_blockwise(rows=-1) == fq.ERR_SHAPE
+    assert q_blockwise(rows=0, x=None, q=None, s=None) == fq.OK      # empty: nothing launched
+    assert q_blockwise(cols=0, x=None, q=None, s=None) == fq.OK
+    assert q_blockwise(x=None) == fq.ERR_NULL
+    assert q_blockwise(s=None) == fq.ERR_NULL
+    assert q_blockwise(ldx=200) == fq.ERR_SHAPE
+    assert q_blockwise(lds=1) == fq.ERR_SHAPE
+    assert q_blockwise(kind=fq.BLOCK_128x128, lds=1) == fq.ERR_SHAPE
+    assert q_blockwise(x=MIS) == fq.ERR_ALIGN
+    assert q_blockwise(q=A16 + 8) == fq.ERR_ALIGN
+    assert q_blockwise(ldx=260, cols=256) == fq.ERR_ALIGN             # 520 bytes per row
+    assert q_blockwise(ldq=264) == fq.ERR_ALIGN
+    assert q_blockwise(kind=fq.BLOCK_128x128, rows=128 * 65536) == fq.ERR_SHAPE
+
+
+def test_quant_transpose_validation():
+    f = L.fp8_quant_transpose
+    base = [A16, fq.BF16, 256, 384, 384, A16, 384, A16, 3, A16, 256, A16, 2, None]
+    def call(**ch):
+        a = list(base)
+        for i, v in ch.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a1=5) == fq.ERR_UNSUPPORTED
+    assert call(a2=-3) == fq.ERR_SHAPE
+    assert call(a2=0, a0=None) == fq.OK
+    assert call(a0=None) == fq.ERR_NULL
+    assert call(a5=None) == fq.ERR_NULL                   # half a pair
+    assert call(a5=None, a7=None, a9=None, a11=None) == fq.OK   # nothing requested
+    assert call(a6=200) == fq.ERR_SHAPE
+    assert call(a12=1) == fq.ERR_SHAPE
+    assert call(a9=MIS) == fq.ERR_ALIGN
+    assert call(a10=264) == fq.ERR_ALIGN
+
+
+def test_gemm_validation():
+    f = L.fp8_gemm_blockscaled
+    # M, N, K, a, lda, sa, ldsa, sa_kind, b, ldb, layout, sb, ldsb, sb_kind, c, ldc, cdt, stream
+    base = [256, 256, 512, A16, 512, A16, 4, fq.ROW_1x128, A16, 512, fq.B_NK, A16, 4,
+            fq.BLOCK_128x128, A16, 256, fq.BF16, None]
+    def call(**ch):
+        a = list(base)
+        for i, v in ch.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a16=3) == fq.ERR_UNSUPPORTED
+    assert call(a10=2) == fq.ERR_UNSUPPORTED
+    assert call(a7=fq.BLOCK_128x128) == fq.ERR_UNSUPPORTED
+    assert call(a13=fq.ROW_1x128, a10=fq.B_KN, a9=256) == fq.ERR_UNSUPPORTED
+    assert call(a0=-1) == fq.ERR_SHAPE
+    assert call(a0=0, a3=None) == fq.OK
+    assert call(a3=None) == fq.ERR_NULL
+    assert call(a11=None) == fq.ERR_NULL
+    assert call(a4=500) == fq.ERR_SHAPE
+    assert call(a6=3) == fq.ERR_SHAPE
+    assert call(a12=3) == fq.ERR_SHAPE
+    assert call(a10=fq.B_KN, a9=128) == fq.ERR_SHAPE      # ldb < N for KN
+    assert call(a10=fq.B_KN, a9=256, a12=1) == fq.ERR_SHAPE  # KN grid row stride < ceil(N/128)
+    assert call(a15=200) == fq.ERR_SHAPE
+    assert call(a3=MIS) == fq.ERR_ALIGN
+    assert call(a14=A16 + 4) == fq.ERR_ALIGN
+    assert call(a4=520, a2=512) == fq.ERR_ALIGN
+
+
+def test_grouped_validation():
+    f = L.fp8_grouped_gemm
+    # G, M_pad, N, K, a, lda, sa, ldsa, off, b, sb, c, ldc, cdt, stream
+    base = [4, 512, 256, 256, A16, 256, A16, 2, A16, A16, A16, A16, 256, fq.BF16, None]
+    def call(**ch):
+        a = list(base)
+        for i, v in ch.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a13=4) == fq.ERR_UNSUPPORTED
+    assert call(a0=0) == fq.ERR_SHAPE
+    assert call(a1=500) == fq.ERR_SHAPE                    # M_pad not a multiple of 128
+    assert call(a1=0, a4=None) == fq.OK
+    assert call(a8=None) == fq.ERR_NULL
+    assert call(a7=1) == fq.ERR_SHAPE
+    assert call(a3=200, a5=256, a7=2) == fq.ERR_ALIGN      # K % 16 != 0
+    assert call(a8=A16 + 2) == fq.ERR_ALIGN
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is present: valid fake pointers would launch")
+def test_valid_arguments_without_gpu_report_device_error():
+    assert q_blockwise() == fq.ERR_DEVICE
