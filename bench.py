@@ -49,11 +49,30 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=8,
                    help="output rows per GEMM in the oracle's timed sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain 1 GiB device-to-device copy (5 times), the reference "
+                        "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters")
     return p.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "launches": 5}))
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py: this build measures one GPU; --gpus %d is not supported "
               "(the design notes describe how the path would shard)" % args.gpus, file=sys.stderr)

@@ -21,6 +21,7 @@
 // operands.
 #include "fp8q_device.h"
 #include "fp8q_internal.h"
+#include "gemm_common.h"
 
 namespace fp8q {
 
@@ -29,49 +30,6 @@ constexpr int BK = 128;
 constexpr int kGemmThreads = 512;
 constexpr int WM = 64;       // wave tile rows
 constexpr int MI = WM / 16;  // 16x16 blocks per wave along M
-
-enum { SA_ROW = 0, SA_TENSOR = 2 };
-enum { SB_ROW = 0, SB_BLOCK = 1, SB_TENSOR = 2 };
-
-struct GemmArgs {
-    int64_t M, N, K;
-    const uint8_t* a;
-    int64_t lda;
-    const float* sa;
-    int64_t ldsa;
-    const uint8_t* b;
-    int64_t ldb;
-    const float* sb;
-    int64_t ldsb;
-    void* c;
-    int64_t ldc;
-    int KB;
-    int tiles_m, tiles_n;
-    // grouped GEMM: per-group B/SB strides and device group offsets
-    const int32_t* offsets;
-    int G;
-    int64_t b_group_stride, sb_group_stride;
-};
-
-__device__ __forceinline__ uint32_t bf16_rne(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-// Zero the bytes of a 16-byte chunk at or beyond `valid` (0..16).
-__device__ __forceinline__ uint4 mask_bytes(uint4 v, int valid)
-{
-    if (valid >= 16) return v;
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        int keep = valid - 4 * i;
-        uint32_t m = keep >= 4 ? 0xFFFFFFFFu : (keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u));
-        w[i] &= m;
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
-}
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
 
@@ -379,6 +337,12 @@ void launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
     g.tiles_n = (int)((N + BN - 1) / BN);
     const bool bf = c_dtype == FP8Q_BF16;
     const bool kn = b_layout == FP8Q_B_KN;
+    if (!kn) {
+        const int sa_mode = sa_kind == FP8Q_ROW_1x128 ? SA_ROW : SA_TENSOR;
+        const int sb_mode = sb_kind == FP8Q_ROW_1x128 ? SB_ROW
+                          : (sb_kind == FP8Q_BLOCK_128x128 ? SB_BLOCK : SB_TENSOR);
+        if (launch_gemm_nk(g, sa_mode, sb_mode, bf, st)) return;
+    }
     if (sa_kind == FP8Q_ROW_1x128) {
         if (sb_kind == FP8Q_BLOCK_128x128) {
             if (kn) launch_typed<SA_ROW, SB_BLOCK, true>(g, bf, st);

@@ -1,0 +1,57 @@
+// Shared definitions of the block-scaled GEMM kernels (host and device).
+#pragma once
+
+#include "fp8q_device.h"
+
+namespace fp8q {
+
+enum { SA_ROW = 0, SA_TENSOR = 2 };
+enum { SB_ROW = 0, SB_BLOCK = 1, SB_TENSOR = 2 };
+
+struct GemmArgs {
+    int64_t M, N, K;
+    const uint8_t* a;
+    int64_t lda;
+    const float* sa;
+    int64_t ldsa;
+    const uint8_t* b;
+    int64_t ldb;
+    const float* sb;
+    int64_t ldsb;
+    void* c;
+    int64_t ldc;
+    int KB;
+    int tiles_m, tiles_n;
+    // grouped GEMM: per-group B/SB strides and device group offsets
+    const int32_t* offsets;
+    int G;
+    int64_t b_group_stride, sb_group_stride;
+};
+
+__device__ __forceinline__ uint32_t bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Zero the bytes of a 16-byte chunk at or beyond `valid` (0..16).
+__device__ __forceinline__ uint4 mask_bytes(uint4 v, int valid)
+{
+    if (valid >= 16) return v;
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int keep = valid - 4 * i;
+        uint32_t m = keep >= 4 ? 0xFFFFFFFFu : (keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u));
+        w[i] &= m;
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+
+// Launch of the [N][K]-operand kernel (forward, wgrad, per-tensor); returns
+// false if that kernel does not cover the call (the caller then uses the
+// general kernel).
+bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool out_bf16, hipStream_t st);
+
+}  // namespace fp8q

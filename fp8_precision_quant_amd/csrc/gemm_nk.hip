@@ -1,0 +1,401 @@
+// Block-scaled FP8 GEMM for operands with the contraction axis contiguous
+// (A [M][K], B [N][K]): the forward y = x W^T, the weight gradient
+// dW = dy^T x on transposed re-quantized operands, and per-tensor scaling.
+//
+//   C[m][n] = sum_kb SA(m,kb) * SB(n,kb) * sum_{k in chunk kb} dec(A[m][k]) * dec(B[n][k])
+//
+// (FP8 Linear with an FP32 accumulator: Ling 2.0 FP8 blog, "where does the
+// worry come from" and "where is error introduced"; tile scales: same blog,
+// "fine-grained quantization"; 128x128 weight blocks: "FP8-RL" article, 一.)
+//
+// gfx950 mapping:
+//  * workgroup tile 128 (M) x 256 (N), K chunk 128 = one scale chunk; 8 waves
+//    of 64 x 64; one v_mfma_f32_16x16x128_f8f6f4 per 16x16 block per chunk
+//    gives that chunk's fp32 partial, which one VALU FMA scales into the fp32
+//    accumulator; MFMAs and FMAs are interleaved so the matrix core keeps
+//    working while earlier partials are scaled;
+//  * operands and per-chunk scales go global -> LDS with buffer loads that
+//    write LDS directly (no VGPR staging), through a ring of 3 LDS stages of
+//    48 KB: chunk kb+2 is in flight while chunk kb computes.  Every wave
+//    issues the same number of loads per chunk, so waiting for a chunk is an
+//    exact vmcnt.  Buffer resources bound every load to its operand;
+//  * 16-byte LDS slots are XOR-swizzled per row so fragment reads are free
+//    of bank conflicts;
+//  * tile order: workgroups are dealt to the 8 XCDs round-robin, so each XCD
+//    gets a contiguous range of tiles, walked in groups of 16 M-tiles so
+//    neighbouring workgroups share A and B panels in that XCD's L2.
+#include "fp8q_device.h"
+#include "fp8q_internal.h"
+#include "gemm_common.h"
+
+namespace fp8q {
+
+namespace {
+
+constexpr int TBM = 128;
+constexpr int TBN = 256;
+constexpr int TBK = 128;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int WTM = 64;              // wave tile
+constexpr int WTN = 64;
+constexpr int NMI = WTM / 16;        // 16x16 blocks per wave
+constexpr int NNI = WTN / 16;
+constexpr int kStages = 3;
+constexpr int kGroupM = 16;
+constexpr int kAStage = TBM * TBK;   // bytes
+constexpr int kBStage = TBN * TBK;
+// tile DMAs per wave per chunk (1 KB each) plus one scale DMA
+constexpr int kLoadsPerChunk = (TBM + TBN) * TBK / 1024 / kWaves + 1;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16-byte slot of logical chunk `chunk` in LDS row `row`.  The XOR key
+// (row & 7) ^ ((row >> 3) & 1) makes the fragment reads (lane l: row
+// 16 b + l % 16, chunk 2 (l / 16) + h) free of bank conflicts on gfx950
+// (measured with SQ_LDS_BANK_CONFLICT; the keys row & 7 and (row >> 1) & 7
+// conflict on a quarter of the cycles).  It depends on the row's low 4 bits
+// only, so the fragment of block b is the fragment of block 0 plus b rows of 16.
+__device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int sw(int row, int chunk) { return row * TBK + ((chunk ^ swz_key(row)) << 4); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                             (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF), 0x00020000);
+}
+
+// One DMA wave-instruction fills 8 LDS rows (1 KB): lane l writes slot l & 7
+// of row r0 + l / 8, which holds logical chunk (l & 7) ^ key(row).  The
+// per-lane source offset (relative to the operand base, without the chunk's
+// k0) is fixed for the whole K loop.  Rows past the operand's last row
+// re-read the last row: they only feed outputs that are never stored.
+__device__ __forceinline__ uint32_t dma_src_off(int r0, int lane, int64_t row0, int64_t rows_valid, int64_t ld)
+{
+    const int r = r0 + (lane >> 3);
+    int64_t g = row0 + r;
+    g = g < rows_valid ? g : rows_valid - 1;
+    return (uint32_t)(g * ld + 16 * ((lane & 7) ^ swz_key(r)));
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint8_t* lds_rows, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds_rows, 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, float* lds_words, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds_words, 4, voff, soff, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS reads of the compute phase are issued as inline asm, outside the
+// compiler's view of LDS: otherwise it cannot tell the three stages apart
+// and waits for every in-flight LDS DMA (vmcnt(0)) before each read, which
+// serialises the load pipeline.  The one explicit lgkmcnt(0) below takes the
+// loaded registers as operands, so every consumer is ordered after it.
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t lds_addr(const void* ptr) { return (uint32_t)(uintptr_t)(const lds_u8_t*)ptr; }
+
+template <int OFF>
+__device__ __forceinline__ v4i ds128(uint32_t addr)
+{
+    v4i v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+
+template <int OFF>
+__device__ __forceinline__ float ds32(uint32_t addr)
+{
+    float v;
+    asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+
+__device__ __forceinline__ v8i cat(v4i lo, v4i hi)
+{
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Zero the bytes at or beyond `valid` (1..127) of every row of an A and a B
+// stage (the last, partial K chunk).
+__device__ __forceinline__ void zero_k_tail(uint8_t* As, uint8_t* Bs, int valid, int tid)
+{
+    for (int row = tid; row < TBM + TBN; row += kThreads) {
+        uint8_t* t = row < TBM ? As : Bs;
+        const int r = row < TBM ? row : row - TBM;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int v = valid - 16 * c;
+            if (v >= 16) continue;
+            uint4* p = reinterpret_cast<uint4*>(t + sw(r, c));
+            *p = v <= 0 ? make_uint4(0, 0, 0, 0) : mask_bytes(*p, v);
+        }
+    }
+}
+
+}  // namespace
+
+template <int SA_MODE, int SB_MODE, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t As[kStages][kAStage];
+    __shared__ __attribute__((aligned(16))) uint8_t Bs[kStages][kBStage];
+    __shared__ __attribute__((aligned(16))) float SAs[kStages][TBM];
+    __shared__ __attribute__((aligned(16))) float SBs[kStages][TBN];
+    __shared__ __attribute__((aligned(16))) float Sdummy[64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // XCD-contiguous tile ranges, grouped along M inside each range
+    const int T = p.tiles_m * p.tiles_n;
+    const int xcd = blockIdx.x & 7;
+    const int local = blockIdx.x >> 3;
+    const int pid = xcd * (T >> 3) + min(xcd, T & 7) + local;
+    const int span = kGroupM * p.tiles_n;
+    const int group = pid / span;
+    const int first_m = group * kGroupM;
+    const int gsz = min(p.tiles_m - first_m, kGroupM);
+    const int idx = pid - group * span;
+    const int tile_m = first_m + idx % gsz;
+    const int tile_n = idx / gsz;
+
+    const int64_t m0 = (int64_t)tile_m * TBM;
+    const int64_t n0 = (int64_t)tile_n * TBN;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int KB = p.KB;
+    const int k_tail = (int)(K - (int64_t)(KB - 1) * TBK);   // bytes in the last chunk (1..128)
+
+    // ---- load plan: wave w fills A rows [16w, 16w+16) (2 DMAs) and B rows
+    // [32w, 32w+32) (4 DMAs) of each stage, plus one 64-lane scale DMA:
+    // waves 0-1 the A-row scales, waves 2-5 the B-column scales (row-scaled
+    // B), the rest a dummy copy so every wave issues the same count.
+    const int64_t ext_a = (M - 1) * p.lda + ((K + 15) & ~(int64_t)15);
+    const int64_t ext_b = (N - 1) * p.ldb + ((K + 15) & ~(int64_t)15);
+    const __amdgpu_buffer_rsrc_t ra = rsrc(p.a, ext_a);
+    const __amdgpu_buffer_rsrc_t rb = rsrc(p.b, ext_b);
+    uint32_t offa[2], offb[4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) offa[t] = dma_src_off(16 * wave + 8 * t, lane, m0, M, p.lda);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) offb[t] = dma_src_off(32 * wave + 8 * t, lane, n0, N, p.ldb);
+
+    // scale DMA: source words sc[row * ld + kb].  Waves 0-1: SA of the
+    // tile's 128 rows (row-scaled A).  Wave 2-5: SB of the tile's 256
+    // columns (row-scaled B); with 128x128-block B scales wave 2 instead
+    // loads the scales of the tile's two 128-column blocks into SBs[0..1].
+    // Everything else (and lanes past the scale grid) re-reads a valid word.
+    __amdgpu_buffer_rsrc_t rsc;
+    uint32_t sc_off;
+    int sc_kind;   // 0: A rows, 1: B columns, 2: B blocks, 3: dummy
+    if (wave < 2 && SA_MODE == SA_ROW) {
+        sc_kind = 0;
+        int64_t row = m0 + 64 * wave + lane;
+        row = row < M ? row : M - 1;
+        rsc = rsrc(p.sa, ((M - 1) * p.ldsa + KB) * 4);
+        sc_off = (uint32_t)(row * p.ldsa * 4);
+    } else if (wave >= 2 && wave < 6 && SB_MODE == SB_ROW) {
+        sc_kind = 1;
+        int64_t row = n0 + 64 * (wave - 2) + lane;
+        row = row < N ? row : N - 1;
+        rsc = rsrc(p.sb, ((N - 1) * p.ldsb + KB) * 4);
+        sc_off = (uint32_t)(row * p.ldsb * 4);
+    } else if (wave == 2 && SB_MODE == SB_BLOCK) {
+        sc_kind = 2;
+        const int64_t nblocks = (N + 127) / 128;
+        int64_t blk = n0 / 128 + (lane < 2 ? lane : 1);
+        blk = blk < nblocks ? blk : nblocks - 1;
+        rsc = rsrc(p.sb, ((nblocks - 1) * p.ldsb + KB) * 4);
+        sc_off = (uint32_t)(blk * p.ldsb * 4);
+    } else {
+        sc_kind = 3;
+        rsc = rsrc(p.sa, 4);
+        sc_off = 0;
+    }
+
+    auto issue = [&](int kb) {
+        const int st = kb % kStages;
+        const uint32_t k0 = (uint32_t)kb * TBK;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) dma16(ra, &As[st][(16 * wave + 8 * t) * TBK], offa[t], k0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) dma16(rb, &Bs[st][(32 * wave + 8 * t) * TBK], offb[t], k0);
+        float* dst = sc_kind == 0 ? &SAs[st][64 * wave]
+                   : sc_kind == 1 ? &SBs[st][64 * (wave - 2)]
+                   : sc_kind == 2 ? &SBs[st][0] : Sdummy;
+        dma4(rsc, dst, sc_off, sc_kind == 3 ? 0u : (uint32_t)kb * 4);
+    };
+
+    v4f acc[NMI][NNI];
+#pragma unroll
+    for (int i = 0; i < NMI; ++i)
+#pragma unroll
+        for (int j = 0; j < NNI; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    const int lrow = lane & 15;
+    const int kgrp = lane >> 4;
+    const int wm0 = (wave >> 2) * WTM;            // 2 waves along M
+    const int wn0 = (wave & 3) * WTN;             // 4 waves along N
+    const float sa_t = (SA_MODE == SA_TENSOR && KB > 0) ? p.sa[0] : 0.0f;
+    const float sb_t = (SB_MODE == SB_TENSOR && KB > 0) ? p.sb[0] : 0.0f;
+    const int a_off0 = sw(wm0 + lrow, 2 * kgrp), a_off1 = sw(wm0 + lrow, 2 * kgrp + 1);
+    const int b_off0 = sw(wn0 + lrow, 2 * kgrp), b_off1 = sw(wn0 + lrow, 2 * kgrp + 1);
+
+    if (KB > 0) issue(0);
+    if (KB > 1) issue(1);
+
+    const uint32_t lds_a = lds_addr(As), lds_b = lds_addr(Bs);
+    const uint32_t lds_sa = lds_addr(SAs) + 4 * (wm0 + 4 * kgrp);
+    const uint32_t lds_sb = lds_addr(SBs) + 4 * (wn0 + lrow);
+    // the wave's 64 columns lie in one 128-column block of B's scale grid
+    const uint32_t lds_sblk = lds_addr(SBs) + 4 * (wn0 / 128);
+
+    for (int kb = 0; kb < KB; ++kb) {
+        const int st = kb % kStages;
+        // chunk kb has landed once only chunk kb+1's loads may be pending
+        if (kb + 1 < KB)
+            wait_vm<kLoadsPerChunk>();
+        else
+            wait_vm<0>();
+        // every wave's chunk-kb loads landed and every wave is done reading
+        // the stage of chunk kb-1 (its reads fed MFMAs that have issued)
+        __builtin_amdgcn_s_barrier();
+        if (kb == KB - 1 && k_tail < TBK) {
+            zero_k_tail(As[st], Bs[st], k_tail, tid);
+            __syncthreads();
+        }
+        if (kb + 2 < KB) issue(kb + 2);
+
+        // ---- compute chunk kb
+        float sb_blk = SB_MODE == SB_TENSOR ? sb_t : 1.0f;
+        if (SB_MODE == SB_BLOCK) sb_blk = ds32<0>(lds_sblk + st * TBN * 4);
+
+        const uint32_t a0 = lds_a + st * kAStage + a_off0, a1 = lds_a + st * kAStage + a_off1;
+        const uint32_t b0 = lds_b + st * kBStage + b_off0, b1 = lds_b + st * kBStage + b_off1;
+        v8i af[NMI], bf[NNI];
+        af[0] = cat(ds128<0 * 16 * TBK>(a0), ds128<0 * 16 * TBK>(a1));
+        af[1] = cat(ds128<1 * 16 * TBK>(a0), ds128<1 * 16 * TBK>(a1));
+        af[2] = cat(ds128<2 * 16 * TBK>(a0), ds128<2 * 16 * TBK>(a1));
+        af[3] = cat(ds128<3 * 16 * TBK>(a0), ds128<3 * 16 * TBK>(a1));
+        bf[0] = cat(ds128<0 * 16 * TBK>(b0), ds128<0 * 16 * TBK>(b1));
+        bf[1] = cat(ds128<1 * 16 * TBK>(b0), ds128<1 * 16 * TBK>(b1));
+        bf[2] = cat(ds128<2 * 16 * TBK>(b0), ds128<2 * 16 * TBK>(b1));
+        bf[3] = cat(ds128<3 * 16 * TBK>(b0), ds128<3 * 16 * TBK>(b1));
+        v4f sa4[NMI];
+        float cs[NNI];
+        if (SA_MODE == SA_ROW) {
+            const uint32_t sa = lds_sa + st * TBM * 4;
+            sa4[0] = (v4f)ds128<0>(sa);
+            sa4[1] = (v4f)ds128<64>(sa);
+            sa4[2] = (v4f)ds128<128>(sa);
+            sa4[3] = (v4f)ds128<192>(sa);
+        } else {
+#pragma unroll
+            for (int i = 0; i < NMI; ++i) sa4[i] = v4f{sa_t, sa_t, sa_t, sa_t};
+        }
+        if (SB_MODE == SB_ROW) {
+            const uint32_t sbp = lds_sb + st * TBN * 4;
+            cs[0] = ds32<0>(sbp);
+            cs[1] = ds32<64>(sbp);
+            cs[2] = ds32<128>(sbp);
+            cs[3] = ds32<192>(sbp);
+        } else {
+#pragma unroll
+            for (int j = 0; j < NNI; ++j) cs[j] = 1.0f;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]),
+                       "+v"(bf[0]), "+v"(bf[1]), "+v"(bf[2]), "+v"(bf[3]),
+                       "+v"(sa4[0]), "+v"(sa4[1]), "+v"(sa4[2]), "+v"(sa4[3]),
+                       "+v"(cs[0]), "+v"(cs[1]), "+v"(cs[2]), "+v"(cs[3]), "+v"(sb_blk));
+
+        float rs[NMI][4];
+#pragma unroll
+        for (int i = 0; i < NMI; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rs[i][r] = SB_MODE != SB_ROW ? sa4[i][r] * sb_blk : sa4[i][r];
+
+#pragma unroll
+        for (int j = 0; j < NNI; ++j) {
+#pragma unroll
+            for (int i = 0; i < NMI; ++i) {
+                v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], zero, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float t = SB_MODE == SB_ROW ? rs[i][r] * cs[j] : rs[i][r];
+                    acc[i][j][r] = __builtin_fmaf(part[r], t, acc[i][j][r]);
+                }
+            }
+        }
+        // interleave: one MFMA, then the VALU work of earlier partials
+#pragma unroll
+        for (int u = 0; u < NMI * NNI; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, SB_MODE == SB_ROW ? 8 : 4, 0);    // VALU
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < NMI; ++i) {
+#pragma unroll
+        for (int j = 0; j < NNI; ++j) {
+            const int64_t n = n0 + wn0 + 16 * j + lrow;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t m = m0 + wm0 + 16 * i + 4 * kgrp + r;
+                if (m < M && n < N) {
+                    if (OUT_BF16)
+                        reinterpret_cast<uint16_t*>(p.c)[m * p.ldc + n] = (uint16_t)bf16_rne(acc[i][j][r]);
+                    else
+                        reinterpret_cast<float*>(p.c)[m * p.ldc + n] = acc[i][j][r];
+                }
+            }
+        }
+    }
+}
+
+template <int SA_MODE, int SB_MODE>
+static void launch2(const GemmArgs& g, bool bf, hipStream_t st)
+{
+    GemmArgs a = g;
+    a.tiles_m = (int)((g.M + TBM - 1) / TBM);
+    a.tiles_n = (int)((g.N + TBN - 1) / TBN);
+    dim3 grid((uint32_t)(a.tiles_m * a.tiles_n));
+    if (bf)
+        hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, true>), grid, dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, false>), grid, dim3(kThreads), 0, st, a);
+}
+
+bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool out_bf16, hipStream_t st)
+{
+    // 32-bit buffer offsets: every operand and scale grid must span < 2 GiB
+    const int64_t lim = (int64_t)1 << 31;
+    if (g.M * g.lda >= lim || g.N * g.ldb >= lim || g.M * g.ldsa * 4 >= lim ||
+        g.N * g.ldsb * 4 >= lim || (int64_t)g.KB * TBK >= lim)
+        return false;
+    if (sa_mode == SA_ROW) {
+        if (sb_mode == SB_BLOCK) launch2<SA_ROW, SB_BLOCK>(g, out_bf16, st);
+        else if (sb_mode == SB_ROW) launch2<SA_ROW, SB_ROW>(g, out_bf16, st);
+        else launch2<SA_ROW, SB_TENSOR>(g, out_bf16, st);
+    } else {
+        if (sb_mode == SB_BLOCK) launch2<SA_TENSOR, SB_BLOCK>(g, out_bf16, st);
+        else if (sb_mode == SB_ROW) launch2<SA_TENSOR, SB_ROW>(g, out_bf16, st);
+        else launch2<SA_TENSOR, SB_TENSOR>(g, out_bf16, st);
+    }
+    return true;
+}
+
+}  // namespace fp8q
