@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=8,
+    p.add_argument("--cpu-rows", type=int, default=96,
                    help="output rows per GEMM in the oracle's timed sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB device-to-device copy (5 times), the reference "
