@@ -337,11 +337,11 @@ void launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
     g.tiles_n = (int)((N + BN - 1) / BN);
     const bool bf = c_dtype == FP8Q_BF16;
     const bool kn = b_layout == FP8Q_B_KN;
-    if (!kn) {
+    {
         const int sa_mode = sa_kind == FP8Q_ROW_1x128 ? SA_ROW : SA_TENSOR;
         const int sb_mode = sb_kind == FP8Q_ROW_1x128 ? SB_ROW
                           : (sb_kind == FP8Q_BLOCK_128x128 ? SB_BLOCK : SB_TENSOR);
-        if (launch_gemm_nk(g, sa_mode, sb_mode, bf, st)) return;
+        if (launch_gemm_nk(g, sa_mode, sb_mode, kn, bf, st)) return;
     }
     if (sa_kind == FP8Q_ROW_1x128) {
         if (sb_kind == FP8Q_BLOCK_128x128) {

@@ -49,9 +49,9 @@ __device__ __forceinline__ uint4 mask_bytes(uint4 v, int valid)
 }
 
 
-// Launch of the [N][K]-operand kernel (forward, wgrad, per-tensor); returns
-// false if that kernel does not cover the call (the caller then uses the
-// general kernel).
-bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool out_bf16, hipStream_t st);
+// Launch of the LDS-DMA pipelined kernel (forward, dgrad, wgrad,
+// per-tensor); returns false if that kernel does not cover the call (the
+// caller then uses the general kernel).
+bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, bool out_bf16, hipStream_t st);
 
 }  // namespace fp8q

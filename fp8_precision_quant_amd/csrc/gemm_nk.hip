@@ -1,5 +1,6 @@
-// Block-scaled FP8 GEMM for operands with the contraction axis contiguous
-// (A [M][K], B [N][K]): the forward y = x W^T, the weight gradient
+// Block-scaled FP8 GEMM on gfx950: the forward y = x W^T (B = W stored
+// [N][K]), dgrad dx = dy W (B = W read as stored, [K][N], no transposed copy:
+// Ling 2.0 FP8 blog, "FP8 on-demand transpose weight"), the weight gradient
 // dW = dy^T x on transposed re-quantized operands, and per-tensor scaling.
 //
 //   C[m][n] = sum_kb SA(m,kb) * SB(n,kb) * sum_{k in chunk kb} dec(A[m][k]) * dec(B[n][k])
@@ -20,7 +21,9 @@
 //    issues the same number of loads per chunk, so waiting for a chunk is an
 //    exact vmcnt.  Buffer resources bound every load to its operand;
 //  * 16-byte LDS slots are XOR-swizzled per row so fragment reads are free
-//    of bank conflicts;
+//    of bank conflicts; a [K][N] operand is staged as stored (K rows of 256
+//    bytes) and read with ds_read_b64_tr_b8, which returns each lane 8
+//    consecutive K values of its own column -- the MFMA operand layout;
 //  * tile order: workgroups are dealt to the 8 XCDs round-robin, so each XCD
 //    gets a contiguous range of tiles, walked in groups of 16 M-tiles so
 //    neighbouring workgroups share A and B panels in that XCD's L2.
@@ -121,16 +124,48 @@ __device__ __forceinline__ float ds32(uint32_t addr)
     return v;
 }
 
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+// Transposing LDS read: within each 16-lane group, lane i receives byte
+// (i & 7) of the 8-byte rows addressed by lanes 2j + (i >> 3), j = 0..7
+// (measured on gfx950).  With those lanes pointing at 8 consecutive K rows of
+// a [K][N] tile at columns n0 + 8 (i >> 3), lane i gets 8 consecutive K
+// values of column n0 + i.
+template <int OFF>
+__device__ __forceinline__ v2i ds64tr(uint32_t addr)
+{
+    v2i v;
+    asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+
+__device__ __forceinline__ v8i cat4(v2i a, v2i b, v2i c, v2i d)
+{
+    return v8i{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+// [K][N] operand stage: row r (a K index) holds 256 column bytes as 16
+// slots of 16; slot = chunk ^ key(r).  The low 3 key bits spread the 8 rows
+// one 16-lane group reads over distinct banks; bit 3 (from r & 32) puts
+// neighbouring groups, 32 rows apart, in opposite halves of the bank space.
+__device__ __forceinline__ int kn_key(int row) { return (row & 7) ^ ((row >> 2) & 8); }
+
 __device__ __forceinline__ v8i cat(v4i lo, v4i hi)
 {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // Zero the bytes at or beyond `valid` (1..127) of every row of an A and a B
-// stage (the last, partial K chunk).
+// stage (the last, partial K chunk).  A [K][N] B stage has K rows instead:
+// rows at or beyond `valid` are cleared whole.
+template <bool B_KN>
 __device__ __forceinline__ void zero_k_tail(uint8_t* As, uint8_t* Bs, int valid, int tid)
 {
-    for (int row = tid; row < TBM + TBN; row += kThreads) {
+    if (B_KN) {
+        for (int i = valid * (TBN / 16) + tid; i < TBK * (TBN / 16); i += kThreads)
+            reinterpret_cast<uint4*>(Bs)[i] = make_uint4(0, 0, 0, 0);
+    }
+    for (int row = tid; row < (B_KN ? TBM : TBM + TBN); row += kThreads) {
         uint8_t* t = row < TBM ? As : Bs;
         const int r = row < TBM ? row : row - TBM;
 #pragma unroll
@@ -145,7 +180,7 @@ __device__ __forceinline__ void zero_k_tail(uint8_t* As, uint8_t* Bs, int valid,
 
 }  // namespace
 
-template <int SA_MODE, int SB_MODE, bool OUT_BF16>
+template <int SA_MODE, int SB_MODE, bool B_KN, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
 {
     __shared__ __attribute__((aligned(16))) uint8_t As[kStages][kAStage];
@@ -182,14 +217,25 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     // waves 0-1 the A-row scales, waves 2-5 the B-column scales (row-scaled
     // B), the rest a dummy copy so every wave issues the same count.
     const int64_t ext_a = (M - 1) * p.lda + ((K + 15) & ~(int64_t)15);
-    const int64_t ext_b = (N - 1) * p.ldb + ((K + 15) & ~(int64_t)15);
+    const int64_t ext_b = B_KN ? (K - 1) * p.ldb + ((N + 15) & ~(int64_t)15)
+                               : (N - 1) * p.ldb + ((K + 15) & ~(int64_t)15);
     const __amdgpu_buffer_rsrc_t ra = rsrc(p.a, ext_a);
     const __amdgpu_buffer_rsrc_t rb = rsrc(p.b, ext_b);
     uint32_t offa[2], offb[4];
 #pragma unroll
     for (int t = 0; t < 2; ++t) offa[t] = dma_src_off(16 * wave + 8 * t, lane, m0, M, p.lda);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) offb[t] = dma_src_off(32 * wave + 8 * t, lane, n0, N, p.ldb);
+    for (int t = 0; t < 4; ++t) {
+        if (B_KN) {
+            // K rows 16w + 4t + l/16 of the chunk, 16-byte slot l % 16; rows
+            // past K lie outside the buffer resource and read as zero
+            const int r = 16 * wave + 4 * t + (lane >> 4);
+            const int c = (lane & 15) ^ kn_key(r);
+            offb[t] = (uint32_t)(r * p.ldb + n0 + 16 * c);
+        } else {
+            offb[t] = dma_src_off(32 * wave + 8 * t, lane, n0, N, p.ldb);
+        }
+    }
 
     // scale DMA: source words sc[row * ld + kb].  Waves 0-1: SA of the
     // tile's 128 rows (row-scaled A).  Wave 2-5: SB of the tile's 256
@@ -216,8 +262,13 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
         const int64_t nblocks = (N + 127) / 128;
         int64_t blk = n0 / 128 + (lane < 2 ? lane : 1);
         blk = blk < nblocks ? blk : nblocks - 1;
-        rsc = rsrc(p.sb, ((nblocks - 1) * p.ldsb + KB) * 4);
-        sc_off = (uint32_t)(blk * p.ldsb * 4);
+        if (B_KN) {
+            rsc = rsrc(p.sb, ((int64_t)(KB - 1) * p.ldsb + nblocks) * 4);
+            sc_off = (uint32_t)(blk * 4);
+        } else {
+            rsc = rsrc(p.sb, ((nblocks - 1) * p.ldsb + KB) * 4);
+            sc_off = (uint32_t)(blk * p.ldsb * 4);
+        }
     } else {
         sc_kind = 3;
         rsc = rsrc(p.sa, 4);
@@ -230,11 +281,18 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
 #pragma unroll
         for (int t = 0; t < 2; ++t) dma16(ra, &As[st][(16 * wave + 8 * t) * TBK], offa[t], k0);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) dma16(rb, &Bs[st][(32 * wave + 8 * t) * TBK], offb[t], k0);
+        for (int t = 0; t < 4; ++t) {
+            if (B_KN)
+                dma16(rb, &Bs[st][(16 * wave + 4 * t) * TBN], offb[t], k0 * (uint32_t)p.ldb);
+            else
+                dma16(rb, &Bs[st][(32 * wave + 8 * t) * TBK], offb[t], k0);
+        }
         float* dst = sc_kind == 0 ? &SAs[st][64 * wave]
                    : sc_kind == 1 ? &SBs[st][64 * (wave - 2)]
                    : sc_kind == 2 ? &SBs[st][0] : Sdummy;
-        dma4(rsc, dst, sc_off, sc_kind == 3 ? 0u : (uint32_t)kb * 4);
+        const uint32_t sc_soff = sc_kind == 3 ? 0u
+                               : (sc_kind == 2 && B_KN) ? (uint32_t)(kb * p.ldsb * 4) : (uint32_t)kb * 4;
+        dma4(rsc, dst, sc_off, sc_soff);
     };
 
     v4f acc[NMI][NNI];
@@ -252,6 +310,15 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     const float sb_t = (SB_MODE == SB_TENSOR && KB > 0) ? p.sb[0] : 0.0f;
     const int a_off0 = sw(wm0 + lrow, 2 * kgrp), a_off1 = sw(wm0 + lrow, 2 * kgrp + 1);
     const int b_off0 = sw(wn0 + lrow, 2 * kgrp), b_off1 = sw(wn0 + lrow, 2 * kgrp + 1);
+    // [K][N] B: lane (group g = kgrp, i = lrow) addresses K row 32g + i/2 at
+    // column wn0 + 16j + 8 (i & 1); reads t = 0..3 step 8 K rows (2048 bytes)
+    int kn_off[NNI];
+#pragma unroll
+    for (int j = 0; j < NNI; ++j) {
+        const int r = 32 * kgrp + (lrow >> 1);
+        const int c = (wn0 >> 4) + j;
+        kn_off[j] = r * TBN + ((c ^ kn_key(r)) << 4) + 8 * (lrow & 1);
+    }
 
     if (KB > 0) issue(0);
     if (KB > 1) issue(1);
@@ -273,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
         // the stage of chunk kb-1 (its reads fed MFMAs that have issued)
         __builtin_amdgcn_s_barrier();
         if (kb == KB - 1 && k_tail < TBK) {
-            zero_k_tail(As[st], Bs[st], k_tail, tid);
+            zero_k_tail<B_KN>(As[st], Bs[st], k_tail, tid);
             __syncthreads();
         }
         if (kb + 2 < KB) issue(kb + 2);
@@ -289,10 +356,19 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
         af[1] = cat(ds128<1 * 16 * TBK>(a0), ds128<1 * 16 * TBK>(a1));
         af[2] = cat(ds128<2 * 16 * TBK>(a0), ds128<2 * 16 * TBK>(a1));
         af[3] = cat(ds128<3 * 16 * TBK>(a0), ds128<3 * 16 * TBK>(a1));
-        bf[0] = cat(ds128<0 * 16 * TBK>(b0), ds128<0 * 16 * TBK>(b1));
-        bf[1] = cat(ds128<1 * 16 * TBK>(b0), ds128<1 * 16 * TBK>(b1));
-        bf[2] = cat(ds128<2 * 16 * TBK>(b0), ds128<2 * 16 * TBK>(b1));
-        bf[3] = cat(ds128<3 * 16 * TBK>(b0), ds128<3 * 16 * TBK>(b1));
+        if (B_KN) {
+            const uint32_t bs = lds_b + st * kBStage;
+#pragma unroll
+            for (int j = 0; j < NNI; ++j) {
+                const uint32_t ad = bs + kn_off[j];
+                bf[j] = cat4(ds64tr<0>(ad), ds64tr<8 * TBN>(ad), ds64tr<16 * TBN>(ad), ds64tr<24 * TBN>(ad));
+            }
+        } else {
+            bf[0] = cat(ds128<0 * 16 * TBK>(b0), ds128<0 * 16 * TBK>(b1));
+            bf[1] = cat(ds128<1 * 16 * TBK>(b0), ds128<1 * 16 * TBK>(b1));
+            bf[2] = cat(ds128<2 * 16 * TBK>(b0), ds128<2 * 16 * TBK>(b1));
+            bf[3] = cat(ds128<3 * 16 * TBK>(b0), ds128<3 * 16 * TBK>(b1));
+        }
         v4f sa4[NMI];
         float cs[NNI];
         if (SA_MODE == SA_ROW) {
@@ -366,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     }
 }
 
-template <int SA_MODE, int SB_MODE>
+template <int SA_MODE, int SB_MODE, bool B_KN>
 static void launch2(const GemmArgs& g, bool bf, hipStream_t st)
 {
     GemmArgs a = g;
@@ -374,26 +450,38 @@ static void launch2(const GemmArgs& g, bool bf, hipStream_t st)
     a.tiles_n = (int)((g.N + TBN - 1) / TBN);
     dim3 grid((uint32_t)(a.tiles_m * a.tiles_n));
     if (bf)
-        hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, true>), grid, dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, B_KN, true>), grid, dim3(kThreads), 0, st, a);
     else
-        hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, false>), grid, dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, B_KN, false>), grid, dim3(kThreads), 0, st, a);
 }
 
-bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool out_bf16, hipStream_t st)
+bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, bool out_bf16, hipStream_t st)
 {
     // 32-bit buffer offsets: every operand and scale grid must span < 2 GiB
     const int64_t lim = (int64_t)1 << 31;
-    if (g.M * g.lda >= lim || g.N * g.ldb >= lim || g.M * g.ldsa * 4 >= lim ||
-        g.N * g.ldsb * 4 >= lim || (int64_t)g.KB * TBK >= lim)
+    const int64_t b_rows = b_kn ? g.K : g.N;
+    if (g.M * g.lda >= lim || (b_rows + TBK) * g.ldb >= lim || g.M * g.ldsa * 4 >= lim ||
+        (g.N + (int64_t)g.KB) * g.ldsb * 4 >= lim || (int64_t)g.KB * TBK >= lim)
         return false;
+    if (b_kn) {
+        if (sb_mode == SB_ROW) return false;
+        if (sa_mode == SA_ROW) {
+            if (sb_mode == SB_BLOCK) launch2<SA_ROW, SB_BLOCK, true>(g, out_bf16, st);
+            else launch2<SA_ROW, SB_TENSOR, true>(g, out_bf16, st);
+        } else {
+            if (sb_mode == SB_BLOCK) launch2<SA_TENSOR, SB_BLOCK, true>(g, out_bf16, st);
+            else launch2<SA_TENSOR, SB_TENSOR, true>(g, out_bf16, st);
+        }
+        return true;
+    }
     if (sa_mode == SA_ROW) {
-        if (sb_mode == SB_BLOCK) launch2<SA_ROW, SB_BLOCK>(g, out_bf16, st);
-        else if (sb_mode == SB_ROW) launch2<SA_ROW, SB_ROW>(g, out_bf16, st);
-        else launch2<SA_ROW, SB_TENSOR>(g, out_bf16, st);
+        if (sb_mode == SB_BLOCK) launch2<SA_ROW, SB_BLOCK, false>(g, out_bf16, st);
+        else if (sb_mode == SB_ROW) launch2<SA_ROW, SB_ROW, false>(g, out_bf16, st);
+        else launch2<SA_ROW, SB_TENSOR, false>(g, out_bf16, st);
     } else {
-        if (sb_mode == SB_BLOCK) launch2<SA_TENSOR, SB_BLOCK>(g, out_bf16, st);
-        else if (sb_mode == SB_ROW) launch2<SA_TENSOR, SB_ROW>(g, out_bf16, st);
-        else launch2<SA_TENSOR, SB_TENSOR>(g, out_bf16, st);
+        if (sb_mode == SB_BLOCK) launch2<SA_TENSOR, SB_BLOCK, false>(g, out_bf16, st);
+        else if (sb_mode == SB_ROW) launch2<SA_TENSOR, SB_ROW, false>(g, out_bf16, st);
+        else launch2<SA_TENSOR, SB_TENSOR, false>(g, out_bf16, st);
     }
     return true;
 }
