@@ -14,8 +14,10 @@ W [14336 x 4096] bf16 ~N(0,0.02), dy [4096 x 14336] bf16 ~1e-3 N(0,1) with
             dW = gemm(q_colT(dy), q_colT(x), row x row scales)          fp32 out
 
 All inputs are resident in HBM before the timed region.  `value` is the
-GEMM work of the step (3 x 2*M*N*K) divided by the wall time of the whole
-step, quantizers included.  The roofline entry covers the kernel that takes
+GEMM work of the step (3 x 2*M*N*K) divided by the GPU time of the whole
+step, quantizers included (K steps between two events, nothing else in
+between).  A second pass over K steps brackets each launch with events for
+the per-kernel breakdown.  The roofline entry covers the kernel that takes
 the most time in the step; the per-kernel breakdown is reported alongside.
 The CPU baseline times the oracle on a bounded sample of the same step.
 
@@ -40,6 +42,17 @@ PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 
 M, N, K = 4096, 14336, 4096     # tokens, out features (14336), in features
 
+# HBM traffic per launch comes from rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
+# scaled by the same counters on a plain copy of known size, and is recorded
+# with a hash of the kernel's sources; a changed kernel reports null.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_mlp_fwd_bwd_step.txt")
+CSRC = os.path.join(ROOT, "fp8_precision_quant_amd", "csrc")
+KERNEL_SOURCES = {
+    "quant": ["quant.hip", "fp8q_device.h"],
+    "quant_transpose": ["quant_transpose.hip", "fp8q_device.h"],
+    "gemm": ["gemm_nk.hip", "gemm.hip", "gemm_common.h", "fp8q_device.h"],
+}
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -47,12 +60,34 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=96,
+    p.add_argument("--cpu-rows", type=int, default=4096,
                    help="output rows per GEMM in the oracle's timed sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 1 GiB device-to-device copy (5 times), the reference "
                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters")
     return p.parse_args()
+
+
+def source_hash(group):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[group]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(op_name, group):
+    """HBM bytes per launch of `op_name` from the recorded counter summary,
+    or None if absent or taken on different kernel sources."""
+    import configparser
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    cp = configparser.ConfigParser(comment_prefixes=("#",), interpolation=None)
+    cp.read(TRAFFIC_FILE)
+    if op_name not in cp or cp[op_name].get("source_sha256") != source_hash(group):
+        return None
+    return int(cp[op_name]["hbm_bytes_per_launch"])
 
 
 def copy_calibration():
@@ -126,6 +161,9 @@ def main():
          "mfma", gemm_flops),
     ]
 
+    group_of = {"quant_1x128 x": "quant", "quant_128x128 W": "quant",
+                "quant_transpose dy": "quant_transpose", "quant_transpose x (columns)": "quant_transpose"}
+
     def step():
         for _, fn, _, _ in ops:
             fn()
@@ -134,24 +172,33 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: the whole step, K times, bracketed by synchronizations
+    # timed region 1: the whole step, K times, bracketed by synchronizations;
+    # no events inside the step
     stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     start.record(stream)
-    for s in range(args.steps):
-        ev[s][0].record(stream)
-        for i, (_, fn, _, _) in enumerate(ops):
-            fn()
-            ev[s][i + 1].record(stream)
+    for _ in range(args.steps):
+        step()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
+
+    # timed region 2: the same K steps with an event pair around every launch
+    # (on the launch stream) for per-kernel durations; events add a few us to
+    # each launch, which matters only for the short quantizer kernels
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, (_, fn, _, _) in enumerate(ops):
+            fn()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
 
     per_op_ms = np.zeros(len(ops))
     for s in range(args.steps):
@@ -175,14 +222,16 @@ def main():
     dom = int(np.argmax(per_op_ms))
     dname, _, dbound, dwork = ops[dom]
     dt = per_op_ms[dom] * 1e-3
+    traffic = recorded_traffic(dname, group_of.get(dname, "gemm"))
     if dbound == "mfma":
         roofline = {"bound": "mfma", "achieved": round(dwork / dt / 1e12, 2), "peak": PEAK_FP8_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(dwork / dt / 1e12 / PEAK_FP8_TFLOPS, 4),
-                    "traffic": None, "kernel": dname}
+                    "traffic": traffic, "kernel": dname}
     else:
         roofline = {"bound": "hbm", "achieved": round(dwork / dt / 1e9, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(dwork / dt / 1e9 / PEAK_HBM_GBS, 4),
-                    "traffic": None, "kernel": dname}
+                    "traffic": traffic, "kernel": dname}
+    roofline["traffic_unit"] = "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -240,13 +289,13 @@ def cpu_baseline(x_bits, w_bits, dy_bits, rows_per_gemm):
     oracle.gemm_blockscaled(qdy, sdy, "row", qw, sw, "block", "KN", rows=rows)
     oracle.gemm_blockscaled(qdyT, sdyT, "row", qxT, sxT, "row", "NK", rows=rows_w)
     t_g = time.perf_counter() - t_g0
-    flops = 2.0 * rows_per_gemm * N * K + 2.0 * rows_per_gemm * K * N + 2.0 * rows_per_gemm * K * M
+    flops = 2.0 * len(rows) * N * K + 2.0 * len(rows) * K * N + 2.0 * len(rows_w) * K * M
     return {"value": round(flops / t_g / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": "quant 1x128 x + 128x128 W (full tensors, %.1f GB/s), quant+transpose of dy and x "
-                      "(full, %.2f s), and fwd/dgrad/wgrad GEMMs on %d sampled output rows each "
+                      "(full, %.2f s), and fwd/dgrad/wgrad GEMMs on min(M, %d) sampled output rows each "
                       "(%.2f s); value = GEMM FLOPs of the sample / GEMM time"
-                      % (q_bytes / t_q / 1e9, t_t, rows_per_gemm, t_g),
+                      % (q_bytes / t_q / 1e9, t_t, len(rows_w), t_g),
             "total_s": round(time.perf_counter() - t0, 2)}
 
 
