@@ -19,6 +19,8 @@
 // on-demand transpose weight") is transposed in registers (4x4 byte blocks)
 // on its way into LDS, so LDS always holds K-contiguous rows for both
 // operands.
+#include <atomic>
+
 #include "fp8q_device.h"
 #include "fp8q_internal.h"
 #include "gemm_common.h"
@@ -322,6 +324,26 @@ static void launch_typed(const GemmArgs& a, bool out_bf16, hipStream_t st)
                            dim3(kGemmThreads), 0, st, a);
 }
 
+// Compute-unit count of the current device, cached per device (the query
+// is not free).  Falls back to 256 (MI355X) if the query fails.
+static int device_cu_count()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        n = 256;
+    }
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 void launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const float* sa,
                  int64_t ldsa, int sa_kind, const uint8_t* b, int64_t ldb, int b_layout,
                  const float* sb, int64_t ldsb, int sb_kind, void* c, int64_t ldc, int c_dtype,
@@ -335,6 +357,7 @@ void launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
     g.KB = (int)((K + BK - 1) / BK);
     g.tiles_m = (int)((M + 255) / 256);
     g.tiles_n = (int)((N + BN - 1) / BN);
+    g.num_cus = device_cu_count();
     const bool bf = c_dtype == FP8Q_BF16;
     const bool kn = b_layout == FP8Q_B_KN;
     {

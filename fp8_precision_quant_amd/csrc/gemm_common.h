@@ -22,6 +22,7 @@ struct GemmArgs {
     int64_t ldc;
     int KB;
     int tiles_m, tiles_n;
+    int num_cus;             // compute units of the device (persistent grid size)
     // grouped GEMM: per-group B/SB strides and device group offsets
     const int32_t* offsets;
     int G;

@@ -180,6 +180,14 @@ __device__ __forceinline__ void zero_k_tail(uint8_t* As, uint8_t* Bs, int valid,
 
 }  // namespace
 
+// one chunk's operand fragments and scales in registers
+struct Frags {
+    v8i a[NMI], b[NNI];
+    float sa[NMI];   // SA of the lane's row in block i (row-scaled A)
+    v4f sbc[NNI];    // SB of the lane's 4 columns in block j (row-scaled B)
+    float sbk;       // SB of the wave's 128-column block (block-scaled B)
+};
+
 template <int SA_MODE, int SB_MODE, bool B_KN, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
 {
@@ -193,21 +201,33 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    // XCD-contiguous tile ranges, grouped along M inside each range
+    // Persistent workgroups.  Workgroups are dealt to the 8 XCDs
+    // round-robin; XCD x owns a contiguous range of tile ids, walked by its
+    // workgroups in lockstep (tile id = start + local + i * count), in
+    // groups of kGroupM M-tiles so that concurrently running tiles share A
+    // and B panels in that XCD's L2.
     const int T = p.tiles_m * p.tiles_n;
     const int xcd = blockIdx.x & 7;
     const int local = blockIdx.x >> 3;
-    const int pid = xcd * (T >> 3) + min(xcd, T & 7) + local;
+    const int G = gridDim.x;
+    const int nwg = (G >> 3) + (xcd < (G & 7) ? 1 : 0);     // workgroups on this XCD
+    const int range_start = xcd * (T >> 3) + min(xcd, T & 7);
+    const int range_len = (T >> 3) + (xcd < (T & 7) ? 1 : 0);
     const int span = kGroupM * p.tiles_n;
-    const int group = pid / span;
-    const int first_m = group * kGroupM;
-    const int gsz = min(p.tiles_m - first_m, kGroupM);
-    const int idx = pid - group * span;
-    const int tile_m = first_m + idx % gsz;
-    const int tile_n = idx / gsz;
+    auto tile_origin = [&](int i, int64_t& tm0, int64_t& tn0) {
+        const int pid = range_start + i;
+        const int group = pid / span;
+        const int first_m = group * kGroupM;
+        const int gsz = min(p.tiles_m - first_m, kGroupM);
+        const int idx = pid - group * span;
+        tm0 = (int64_t)(first_m + idx % gsz) * TBM;
+        tn0 = (int64_t)(idx / gsz) * TBN;
+    };
+    int ti = local;                // index into this XCD's range
+    if (ti >= range_len) return;
+    int64_t m0, n0;
+    tile_origin(ti, m0, n0);
 
-    const int64_t m0 = (int64_t)tile_m * TBM;
-    const int64_t n0 = (int64_t)tile_n * TBN;
     const int64_t M = p.M, N = p.N, K = p.K;
     const int KB = p.KB;
     const int k_tail = (int)(K - (int64_t)(KB - 1) * TBK);   // bytes in the last chunk (1..128)
@@ -222,20 +242,24 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     const __amdgpu_buffer_rsrc_t ra = rsrc(p.a, ext_a);
     const __amdgpu_buffer_rsrc_t rb = rsrc(p.b, ext_b);
     uint32_t offa[2], offb[4];
+    // per-lane source offsets of the tile at (tm0, tn0), without the chunk's k0
+    auto set_tile_offsets = [&](int64_t tm0, int64_t tn0) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) offa[t] = dma_src_off(16 * wave + 8 * t, lane, m0, M, p.lda);
+        for (int t = 0; t < 2; ++t) offa[t] = dma_src_off(16 * wave + 8 * t, lane, tm0, M, p.lda);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        if (B_KN) {
-            // K rows 16w + 4t + l/16 of the chunk, 16-byte slot l % 16; rows
-            // past K lie outside the buffer resource and read as zero
-            const int r = 16 * wave + 4 * t + (lane >> 4);
-            const int c = (lane & 15) ^ kn_key(r);
-            offb[t] = (uint32_t)(r * p.ldb + n0 + 16 * c);
-        } else {
-            offb[t] = dma_src_off(32 * wave + 8 * t, lane, n0, N, p.ldb);
+        for (int t = 0; t < 4; ++t) {
+            if (B_KN) {
+                // K rows 16w + 4t + l/16 of the chunk, 16-byte slot l % 16;
+                // rows past K lie outside the buffer resource and read as zero
+                const int r = 16 * wave + 4 * t + (lane >> 4);
+                const int c = (lane & 15) ^ kn_key(r);
+                offb[t] = (uint32_t)(r * p.ldb + tn0 + 16 * c);
+            } else {
+                offb[t] = dma_src_off(32 * wave + 8 * t, lane, tn0, N, p.ldb);
+            }
         }
-    }
+    };
+    set_tile_offsets(m0, n0);
 
     // scale DMA: source words sc[row * ld + kb].  Waves 0-1: SA of the
     // tile's 128 rows (row-scaled A).  Wave 2-5: SB of the tile's 256
@@ -243,37 +267,41 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     // loads the scales of the tile's two 128-column blocks into SBs[0..1].
     // Everything else (and lanes past the scale grid) re-reads a valid word.
     __amdgpu_buffer_rsrc_t rsc;
-    uint32_t sc_off;
+    uint32_t sc_off = 0;
     int sc_kind;   // 0: A rows, 1: B columns, 2: B blocks, 3: dummy
+    const int64_t nblocks = (N + 127) / 128;
     if (wave < 2 && SA_MODE == SA_ROW) {
         sc_kind = 0;
-        int64_t row = m0 + 64 * wave + lane;
-        row = row < M ? row : M - 1;
         rsc = rsrc(p.sa, ((M - 1) * p.ldsa + KB) * 4);
-        sc_off = (uint32_t)(row * p.ldsa * 4);
     } else if (wave >= 2 && wave < 6 && SB_MODE == SB_ROW) {
         sc_kind = 1;
-        int64_t row = n0 + 64 * (wave - 2) + lane;
-        row = row < N ? row : N - 1;
         rsc = rsrc(p.sb, ((N - 1) * p.ldsb + KB) * 4);
-        sc_off = (uint32_t)(row * p.ldsb * 4);
     } else if (wave == 2 && SB_MODE == SB_BLOCK) {
         sc_kind = 2;
-        const int64_t nblocks = (N + 127) / 128;
-        int64_t blk = n0 / 128 + (lane < 2 ? lane : 1);
-        blk = blk < nblocks ? blk : nblocks - 1;
-        if (B_KN) {
+        if (B_KN)
             rsc = rsrc(p.sb, ((int64_t)(KB - 1) * p.ldsb + nblocks) * 4);
-            sc_off = (uint32_t)(blk * 4);
-        } else {
+        else
             rsc = rsrc(p.sb, ((nblocks - 1) * p.ldsb + KB) * 4);
-            sc_off = (uint32_t)(blk * p.ldsb * 4);
-        }
     } else {
         sc_kind = 3;
         rsc = rsrc(p.sa, 4);
-        sc_off = 0;
     }
+    auto set_scale_offset = [&](int64_t tm0, int64_t tn0) {
+        if (sc_kind == 0) {
+            int64_t row = tm0 + 64 * wave + lane;
+            row = row < M ? row : M - 1;
+            sc_off = (uint32_t)(row * p.ldsa * 4);
+        } else if (sc_kind == 1) {
+            int64_t row = tn0 + 64 * (wave - 2) + lane;
+            row = row < N ? row : N - 1;
+            sc_off = (uint32_t)(row * p.ldsb * 4);
+        } else if (sc_kind == 2) {
+            int64_t blk = tn0 / 128 + (lane < 2 ? lane : 1);
+            blk = blk < nblocks ? blk : nblocks - 1;
+            sc_off = B_KN ? (uint32_t)(blk * 4) : (uint32_t)(blk * p.ldsb * 4);
+        }
+    };
+    set_scale_offset(m0, n0);
 
     auto issue = [&](int kb) {
         const int st = kb % kStages;
@@ -296,15 +324,12 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     };
 
     v4f acc[NMI][NNI];
-#pragma unroll
-    for (int i = 0; i < NMI; ++i)
-#pragma unroll
-        for (int j = 0; j < NNI; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
     const int lrow = lane & 15;
     const int kgrp = lane >> 4;
-    const int wm0 = (wave >> 2) * WTM;            // 2 waves along M
+    const int grp = wave >> 2;                    // ping-pong group
+    const int wm0 = grp * WTM;                    // group g: rows [64g, 64g+64)
     const int wn0 = (wave & 3) * WTN;             // 4 waves along N
     const float sa_t = (SA_MODE == SA_TENSOR && KB > 0) ? p.sa[0] : 0.0f;
     const float sb_t = (SB_MODE == SB_TENSOR && KB > 0) ? p.sb[0] : 0.0f;
@@ -320,97 +345,80 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
         kn_off[j] = r * TBN + ((c ^ kn_key(r)) << 4) + 8 * (lrow & 1);
     }
 
-    if (KB > 0) issue(0);
-    if (KB > 1) issue(1);
-
     const uint32_t lds_a = lds_addr(As), lds_b = lds_addr(Bs);
-    const uint32_t lds_sa = lds_addr(SAs) + 4 * (wm0 + 4 * kgrp);
-    const uint32_t lds_sb = lds_addr(SBs) + 4 * (wn0 + lrow);
+    // the MFMA takes the B fragment as its first operand, so lane l's outputs
+    // are C[m = .. + l % 16][n = .. + 4 (l / 16) + r]: four adjacent columns
+    const uint32_t lds_sa = lds_addr(SAs) + 4 * (wm0 + lrow);
+    const uint32_t lds_sb = lds_addr(SBs) + 4 * (wn0 + 4 * kgrp);
     // the wave's 64 columns lie in one 128-column block of B's scale grid
     const uint32_t lds_sblk = lds_addr(SBs) + 4 * (wn0 / 128);
 
-    for (int kb = 0; kb < KB; ++kb) {
-        const int st = kb % kStages;
-        // chunk kb has landed once only chunk kb+1's loads may be pending
-        if (kb + 1 < KB)
-            wait_vm<kLoadsPerChunk>();
-        else
-            wait_vm<0>();
-        // every wave's chunk-kb loads landed and every wave is done reading
-        // the stage of chunk kb-1 (its reads fed MFMAs that have issued)
-        __builtin_amdgcn_s_barrier();
-        if (kb == KB - 1 && k_tail < TBK) {
-            zero_k_tail<B_KN>(As[st], Bs[st], k_tail, tid);
-            __syncthreads();
-        }
-        if (kb + 2 < KB) issue(kb + 2);
-
-        // ---- compute chunk kb
-        float sb_blk = SB_MODE == SB_TENSOR ? sb_t : 1.0f;
-        if (SB_MODE == SB_BLOCK) sb_blk = ds32<0>(lds_sblk + st * TBN * 4);
-
+    // issue the LDS reads of one chunk's operands and scales (no wait)
+    auto read_frags = [&](int st, Frags& f) {
         const uint32_t a0 = lds_a + st * kAStage + a_off0, a1 = lds_a + st * kAStage + a_off1;
-        const uint32_t b0 = lds_b + st * kBStage + b_off0, b1 = lds_b + st * kBStage + b_off1;
-        v8i af[NMI], bf[NNI];
-        af[0] = cat(ds128<0 * 16 * TBK>(a0), ds128<0 * 16 * TBK>(a1));
-        af[1] = cat(ds128<1 * 16 * TBK>(a0), ds128<1 * 16 * TBK>(a1));
-        af[2] = cat(ds128<2 * 16 * TBK>(a0), ds128<2 * 16 * TBK>(a1));
-        af[3] = cat(ds128<3 * 16 * TBK>(a0), ds128<3 * 16 * TBK>(a1));
+        f.a[0] = cat(ds128<0 * 16 * TBK>(a0), ds128<0 * 16 * TBK>(a1));
+        f.a[1] = cat(ds128<1 * 16 * TBK>(a0), ds128<1 * 16 * TBK>(a1));
+        f.a[2] = cat(ds128<2 * 16 * TBK>(a0), ds128<2 * 16 * TBK>(a1));
+        f.a[3] = cat(ds128<3 * 16 * TBK>(a0), ds128<3 * 16 * TBK>(a1));
         if (B_KN) {
             const uint32_t bs = lds_b + st * kBStage;
 #pragma unroll
             for (int j = 0; j < NNI; ++j) {
                 const uint32_t ad = bs + kn_off[j];
-                bf[j] = cat4(ds64tr<0>(ad), ds64tr<8 * TBN>(ad), ds64tr<16 * TBN>(ad), ds64tr<24 * TBN>(ad));
+                f.b[j] = cat4(ds64tr<0>(ad), ds64tr<8 * TBN>(ad), ds64tr<16 * TBN>(ad), ds64tr<24 * TBN>(ad));
             }
         } else {
-            bf[0] = cat(ds128<0 * 16 * TBK>(b0), ds128<0 * 16 * TBK>(b1));
-            bf[1] = cat(ds128<1 * 16 * TBK>(b0), ds128<1 * 16 * TBK>(b1));
-            bf[2] = cat(ds128<2 * 16 * TBK>(b0), ds128<2 * 16 * TBK>(b1));
-            bf[3] = cat(ds128<3 * 16 * TBK>(b0), ds128<3 * 16 * TBK>(b1));
+            const uint32_t b0 = lds_b + st * kBStage + b_off0, b1 = lds_b + st * kBStage + b_off1;
+            f.b[0] = cat(ds128<0 * 16 * TBK>(b0), ds128<0 * 16 * TBK>(b1));
+            f.b[1] = cat(ds128<1 * 16 * TBK>(b0), ds128<1 * 16 * TBK>(b1));
+            f.b[2] = cat(ds128<2 * 16 * TBK>(b0), ds128<2 * 16 * TBK>(b1));
+            f.b[3] = cat(ds128<3 * 16 * TBK>(b0), ds128<3 * 16 * TBK>(b1));
         }
-        v4f sa4[NMI];
-        float cs[NNI];
         if (SA_MODE == SA_ROW) {
             const uint32_t sa = lds_sa + st * TBM * 4;
-            sa4[0] = (v4f)ds128<0>(sa);
-            sa4[1] = (v4f)ds128<64>(sa);
-            sa4[2] = (v4f)ds128<128>(sa);
-            sa4[3] = (v4f)ds128<192>(sa);
-        } else {
-#pragma unroll
-            for (int i = 0; i < NMI; ++i) sa4[i] = v4f{sa_t, sa_t, sa_t, sa_t};
+            f.sa[0] = ds32<0>(sa);
+            f.sa[1] = ds32<64>(sa);
+            f.sa[2] = ds32<128>(sa);
+            f.sa[3] = ds32<192>(sa);
         }
         if (SB_MODE == SB_ROW) {
             const uint32_t sbp = lds_sb + st * TBN * 4;
-            cs[0] = ds32<0>(sbp);
-            cs[1] = ds32<64>(sbp);
-            cs[2] = ds32<128>(sbp);
-            cs[3] = ds32<192>(sbp);
-        } else {
-#pragma unroll
-            for (int j = 0; j < NNI; ++j) cs[j] = 1.0f;
+            f.sbc[0] = (v4f)ds128<0>(sbp);
+            f.sbc[1] = (v4f)ds128<64>(sbp);
+            f.sbc[2] = (v4f)ds128<128>(sbp);
+            f.sbc[3] = (v4f)ds128<192>(sbp);
         }
+        if (SB_MODE == SB_BLOCK) f.sbk = ds32<0>(lds_sblk + st * TBN * 4);
+    };
+    // wait for them; the registers are operands so that no use moves above
+    // (volatile asm keeps its order, so the scale pins stay behind the wait;
+    // only the scales the mode reads are pinned, the rest stay dead)
+    auto wait_frags = [&](Frags& f) {
         asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]),
-                       "+v"(bf[0]), "+v"(bf[1]), "+v"(bf[2]), "+v"(bf[3]),
-                       "+v"(sa4[0]), "+v"(sa4[1]), "+v"(sa4[2]), "+v"(sa4[3]),
-                       "+v"(cs[0]), "+v"(cs[1]), "+v"(cs[2]), "+v"(cs[3]), "+v"(sb_blk));
+                     : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]),
+                       "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3]));
+        if (SA_MODE == SA_ROW) asm volatile("" : "+v"(f.sa[0]), "+v"(f.sa[1]), "+v"(f.sa[2]), "+v"(f.sa[3]));
+        if (SB_MODE == SB_ROW) asm volatile("" : "+v"(f.sbc[0]), "+v"(f.sbc[1]), "+v"(f.sbc[2]), "+v"(f.sbc[3]));
+        if (SB_MODE == SB_BLOCK) asm volatile("" : "+v"(f.sbk));
+    };
 
-        float rs[NMI][4];
+    // one MFMA per 16x16 block gives the chunk's fp32 partial, one FMA per
+    // output scales it into the accumulator
+    auto compute = [&](const Frags& f) {
+        float rs[NMI];
 #pragma unroll
-        for (int i = 0; i < NMI; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) rs[i][r] = SB_MODE != SB_ROW ? sa4[i][r] * sb_blk : sa4[i][r];
-
+        for (int i = 0; i < NMI; ++i) {
+            const float sa_i = SA_MODE == SA_ROW ? f.sa[i] : sa_t;
+            rs[i] = SB_MODE == SB_BLOCK ? sa_i * f.sbk : SB_MODE == SB_TENSOR ? sa_i * sb_t : sa_i;
+        }
 #pragma unroll
         for (int j = 0; j < NNI; ++j) {
 #pragma unroll
             for (int i = 0; i < NMI; ++i) {
-                v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], zero, 0, 0, 0, 0, 0, 0);
+                v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[j], f.a[i], zero, 0, 0, 0, 0, 0, 0);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float t = SB_MODE == SB_ROW ? rs[i][r] * cs[j] : rs[i][r];
+                    const float t = SB_MODE == SB_ROW ? rs[i] * f.sbc[j][r] : rs[i];
                     acc[i][j][r] = __builtin_fmaf(part[r], t, acc[i][j][r]);
                 }
             }
@@ -421,25 +429,99 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            // MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, SB_MODE == SB_ROW ? 8 : 4, 0);    // VALU
         }
-    }
+        // keep the FMAs here: sunk past the next chunk's branches they would
+        // hold every partial live across them
+#pragma unroll
+        for (int i = 0; i < NMI; ++i)
+#pragma unroll
+            for (int j = 0; j < NNI; ++j) asm volatile("" : "+v"(acc[i][j]));
+    };
 
+    // Chunk kb+1 is made ready (its loads landed in every wave, the stage of
+    // chunk kb is free because every wave has its fragments in registers,
+    // chunk kb+3 is issued into that stage) and its fragment reads are in
+    // flight while the MFMAs of chunk kb run from the other register set.
+    auto ready = [&](int kb) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (kb + 1 < KB)
+            wait_vm<kLoadsPerChunk>();
+        else
+            wait_vm<0>();
+        __builtin_amdgcn_s_barrier();
+        if (kb == KB - 1 && k_tail < TBK) {
+            zero_k_tail<B_KN>(As[kb % kStages], Bs[kb % kStages], k_tail, tid);
+            __syncthreads();
+        }
+        if (kb + 2 < KB) issue(kb + 2);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // first tile's first two chunks
+    if (KB > 0) issue(0);
+    if (KB > 1) issue(1);
+    for (;;) {
 #pragma unroll
-    for (int i = 0; i < NMI; ++i) {
+        for (int i = 0; i < NMI; ++i)
 #pragma unroll
-        for (int j = 0; j < NNI; ++j) {
-            const int64_t n = n0 + wn0 + 16 * j + lrow;
+            for (int j = 0; j < NNI; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        if (KB > 0) {
+            Frags f;
+            for (int kb = 0; kb < KB; ++kb) {
+                ready(kb);
+                read_frags(kb % kStages, f);
+                wait_frags(f);
+                compute(f);
+            }
+        }
+        // Store this tile, then start the next tile's loads.  The stores go
+        // first so that waiting for the next tile's first chunk (vmcnt) does
+        // not also wait for its second chunk.
+        const int64_t cm0 = m0, cn0 = n0;
+        ti += nwg;
+        const bool more = ti < range_len;
+        // epilogue: lane l holds C[m][n .. n+3] of each block
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t m = m0 + wm0 + 16 * i + 4 * kgrp + r;
-                if (m < M && n < N) {
-                    if (OUT_BF16)
-                        reinterpret_cast<uint16_t*>(p.c)[m * p.ldc + n] = (uint16_t)bf16_rne(acc[i][j][r]);
-                    else
-                        reinterpret_cast<float*>(p.c)[m * p.ldc + n] = acc[i][j][r];
+        for (int i = 0; i < NMI; ++i) {
+            const int64_t m = cm0 + wm0 + 16 * i + lrow;
+            if (m >= M) continue;
+#pragma unroll
+            for (int j = 0; j < NNI; ++j) {
+                const int64_t n = cn0 + wn0 + 16 * j + 4 * kgrp;
+                const v4f v = acc[i][j];
+                if (n + 3 < N) {
+                    if (OUT_BF16) {
+                        const uint32_t lo = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+                        const uint32_t hi = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+                        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.c) + m * p.ldc + n) = make_uint2(lo, hi);
+                    } else {
+                        *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.c) + m * p.ldc + n) = v;
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (n + r < N) {
+                            if (OUT_BF16)
+                                reinterpret_cast<uint16_t*>(p.c)[m * p.ldc + n + r] = (uint16_t)bf16_rne(v[r]);
+                            else
+                                reinterpret_cast<float*>(p.c)[m * p.ldc + n + r] = v[r];
+                        }
+                    }
                 }
             }
         }
+        if (more) {
+            tile_origin(ti, m0, n0);
+            set_tile_offsets(m0, n0);
+            set_scale_offset(m0, n0);
+            // every wave is done reading this tile's stages
+            __builtin_amdgcn_s_barrier();
+            if (KB > 0) issue(0);
+            if (KB > 1) issue(1);
+        }
+        if (!more) break;
     }
+    // drain the stores before the wave ends
+    wait_vm<0>();
 }
 
 template <int SA_MODE, int SB_MODE, bool B_KN>
@@ -448,7 +530,9 @@ static void launch2(const GemmArgs& g, bool bf, hipStream_t st)
     GemmArgs a = g;
     a.tiles_m = (int)((g.M + TBM - 1) / TBM);
     a.tiles_n = (int)((g.N + TBN - 1) / TBN);
-    dim3 grid((uint32_t)(a.tiles_m * a.tiles_n));
+    // one persistent workgroup per CU (the LDS ring allows one per CU)
+    const int tiles = a.tiles_m * a.tiles_n;
+    dim3 grid((uint32_t)(tiles < g.num_cus ? tiles : g.num_cus));
     if (bf)
         hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, B_KN, true>), grid, dim3(kThreads), 0, st, a);
     else
