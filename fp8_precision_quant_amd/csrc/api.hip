@@ -84,8 +84,7 @@ int fp8_quant_blockwise(const void* x, int x_dtype, int64_t rows, int64_t cols, 
     if (ldx < cols || ldq < cols) return FP8Q_ERR_SHAPE;
     if (kind != FP8Q_TENSOR && lds < tiles_c) return FP8Q_ERR_SHAPE;
     if (kind == FP8Q_ROW_1x128 && rows * tiles_c >= kMaxIndex) return FP8Q_ERR_SHAPE;
-    if (kind == FP8Q_BLOCK_128x128 && (cdiv(rows, kTile) > kMaxGridY || tiles_c >= kMaxIndex))
-        return FP8Q_ERR_SHAPE;
+    if (kind == FP8Q_BLOCK_128x128 && cdiv(rows, kTile) * tiles_c >= kMaxIndex) return FP8Q_ERR_SHAPE;
     if (kind == FP8Q_TENSOR && rows * cdiv(cols, 8) >= kMaxIndex) return FP8Q_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(q) || (ldx * elem_size(x_dtype)) % 16 || ldq % 16)
         return FP8Q_ERR_ALIGN;
@@ -114,7 +113,7 @@ int fp8_quant_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols, 
     if (ldx < cols) return FP8Q_ERR_SHAPE;
     if (want_row && (ldq_row < cols || lds_row < cdiv(cols, kTile))) return FP8Q_ERR_SHAPE;
     if (want_col && (ldq_colT < rows || lds_colT < cdiv(rows, kTile))) return FP8Q_ERR_SHAPE;
-    if (cdiv(rows, kTile) > kMaxGridY || cdiv(cols, kTile) >= kMaxIndex) return FP8Q_ERR_SHAPE;
+    if (cdiv(rows, kTile) > kMaxGridY || cdiv(rows, kTile) * cdiv(cols, kTile) >= kMaxIndex) return FP8Q_ERR_SHAPE;
     if (!aligned16(x) || (ldx * elem_size(x_dtype)) % 16) return FP8Q_ERR_ALIGN;
     if (want_row && (!aligned16(q_row) || ldq_row % 16)) return FP8Q_ERR_ALIGN;
     if (want_col && (!aligned16(q_colT) || ldq_colT % 16)) return FP8Q_ERR_ALIGN;

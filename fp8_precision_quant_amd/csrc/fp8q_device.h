@@ -90,6 +90,29 @@ __device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, c
     return pack4_e4m3(quotient(a, t), quotient(b, t), quotient(c, t), quotient(d, t));
 }
 
+// Eight values of one tile -> eight codes (lo: values 0-3, hi: 4-7).  Tiles
+// with s >= 2^-90 and zero tiles (s = 0, y = 0: the corrected reciprocal
+// then yields x's signed zero) take the branch-free corrected reciprocal;
+// only if some lane of the wave holds a tile with 0 < s < 2^-90 does the
+// wave take the general path.
+__device__ __forceinline__ void quant8(const float v[8], const TileScale& t, uint32_t& lo, uint32_t& hi)
+{
+    if (__builtin_amdgcn_ballot_w64(t.mode == 2) == 0) {
+        float q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float q0 = v[i] * t.y;
+            const float e = __builtin_fmaf(q0, t.s, -v[i]);
+            q[i] = __builtin_fmaf(-e, t.y, q0);
+        }
+        lo = pack4_e4m3(q[0], q[1], q[2], q[3]);
+        hi = pack4_e4m3(q[4], q[5], q[6], q[7]);
+    } else {
+        lo = quant4(v[0], v[1], v[2], v[3], t);
+        hi = quant4(v[4], v[5], v[6], v[7], t);
+    }
+}
+
 // Magic-number unsigned division by a runtime constant (Granlund-Montgomery),
 // for 32-bit numerators.
 struct FastDiv {

@@ -10,6 +10,9 @@
 
 namespace fp8q {
 
+// compute units of the current device (cached per device)
+int device_cu_count();
+
 void launch_quant_blockwise(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
                             int kind, uint8_t* q, int64_t ldq, float* s, int64_t lds,
                             hipStream_t st);

@@ -326,7 +326,7 @@ static void launch_typed(const GemmArgs& a, bool out_bf16, hipStream_t st)
 
 // Compute-unit count of the current device, cached per device (the query
 // is not free).  Falls back to 256 (MI355X) if the query fails.
-static int device_cu_count()
+int device_cu_count()
 {
     static std::atomic<int> cache[64];
     int dev = 0;

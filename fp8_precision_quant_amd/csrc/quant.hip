@@ -80,6 +80,50 @@ __device__ __forceinline__ void store8(uint8_t* qrow, int64_t c, int64_t cols, u
     }
 }
 
+// Raw registers of 8 consecutive elements, so that loads can be issued a
+// step ahead of their use and converted afterwards.
+template <typename T> struct Raw8;
+template <> struct Raw8<uint16_t> { uint4 v; };
+template <> struct Raw8<float> { uint4 a, b; };
+
+// Loads elements [c, c+8) of a row (c a multiple of 8).  For c < cols the
+// 16-byte vectors lie within ld (see the ABI); c >= cols loads nothing.
+__device__ __forceinline__ void raw_load(const uint16_t* row, int64_t c, int64_t cols, Raw8<uint16_t>& r)
+{
+    r.v = c < cols ? *reinterpret_cast<const uint4*>(row + c) : make_uint4(0, 0, 0, 0);
+}
+__device__ __forceinline__ void raw_load(const float* row, int64_t c, int64_t cols, Raw8<float>& r)
+{
+    r.a = c < cols ? *reinterpret_cast<const uint4*>(row + c) : make_uint4(0, 0, 0, 0);
+    r.b = c + 4 < cols ? *reinterpret_cast<const uint4*>(row + c + 4) : make_uint4(0, 0, 0, 0);
+}
+
+// fp32 values of a raw load; elements at or beyond `cols` become 0.
+__device__ __forceinline__ void raw_f32(const Raw8<uint16_t>& r, int64_t c, int64_t cols, float v[8])
+{
+    v[0] = bf16_lo(r.v.x); v[1] = bf16_hi(r.v.x);
+    v[2] = bf16_lo(r.v.y); v[3] = bf16_hi(r.v.y);
+    v[4] = bf16_lo(r.v.z); v[5] = bf16_hi(r.v.z);
+    v[6] = bf16_lo(r.v.w); v[7] = bf16_hi(r.v.w);
+    if (c + 8 > cols) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (c + i >= cols) v[i] = 0.0f;
+    }
+}
+__device__ __forceinline__ void raw_f32(const Raw8<float>& r, int64_t c, int64_t cols, float v[8])
+{
+    v[0] = __uint_as_float(r.a.x); v[1] = __uint_as_float(r.a.y);
+    v[2] = __uint_as_float(r.a.z); v[3] = __uint_as_float(r.a.w);
+    v[4] = __uint_as_float(r.b.x); v[5] = __uint_as_float(r.b.y);
+    v[6] = __uint_as_float(r.b.z); v[7] = __uint_as_float(r.b.w);
+    if (c + 8 > cols) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (c + i >= cols) v[i] = 0.0f;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // 1x128 row tiles
 // ---------------------------------------------------------------------------
@@ -118,10 +162,10 @@ __global__ __launch_bounds__(kRowThreads) void quant_row_kernel(
         uint32_t t = base + u * (kRowThreads / 16) + group;
         float amax = dpp_max16(absmax8(v[u]));
         TileScale ts = make_scale(amax);
+        uint32_t lo, hi;
+        quant8(v[u], ts, lo, hi);
         if (t < total_tiles) {
             int64_t c = (int64_t)tcol[u] * kTile + lane16 * 8;
-            uint32_t lo = quant4(v[u][0], v[u][1], v[u][2], v[u][3], ts);
-            uint32_t hi = quant4(v[u][4], v[u][5], v[u][6], v[u][7], ts);
             if (c < cols)
                 store8(q + (int64_t)row[u] * ldq, c, cols, lo, hi);
             if (lane16 == 0)
@@ -133,51 +177,89 @@ __global__ __launch_bounds__(kRowThreads) void quant_row_kernel(
 // ---------------------------------------------------------------------------
 // 128x128 blocks
 // ---------------------------------------------------------------------------
-// One 256-thread workgroup per block: thread (g = tid/16, l = tid%16) holds
-// rows g, g+16, ..., g+112 at columns 8l..8l+7 (64 values in registers), the
-// block amax is reduced with DPP, readlane and LDS, then every value is cast.
+// A 256-thread workgroup quantizes blocks b = blockIdx.x + i * gridDim.x:
+// thread (g = tid/16, l = tid%16) holds rows g, g+16, ..., g+112 at columns
+// 8l..8l+7 (64 values), the block amax is reduced with DPP, readlane and LDS,
+// then every value is cast.  The next block's loads are issued before the
+// current block is reduced.
 
 constexpr int kBlockThreads = 256;
 
 template <typename T>
 __global__ __launch_bounds__(kBlockThreads) void quant_block_kernel(
     const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* __restrict__ q,
-    int64_t ldq, float* __restrict__ s, int64_t lds)
+    int64_t ldq, float* __restrict__ s, int64_t lds, uint32_t total_blocks, FastDiv blocks_per_row)
 {
-    __shared__ float wave_max[kBlockThreads / 64];
+    __shared__ float wave_max[2][kBlockThreads / 64];
     const int l = threadIdx.x & 15;
     const int g = threadIdx.x >> 4;
-    const int64_t r0 = (int64_t)blockIdx.y * kTile;
-    const int64_t c = (int64_t)blockIdx.x * kTile + l * 8;
 
-    float v[8][8];
-    float m = 0.0f;
+    auto origin = [&](uint32_t b, int64_t& r0, int64_t& c) {
+        const uint32_t br = fdiv(b, blocks_per_row);
+        r0 = (int64_t)br * kTile;
+        c = (int64_t)(b - br * blocks_per_row.d) * kTile + l * 8;
+    };
+    auto load = [&](uint32_t b, Raw8<T>* R) {
+        int64_t r0, c;
+        origin(b, r0, c);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        int64_t r = r0 + g + 16 * u;
-        load8<T>(x + (r < rows ? r : 0) * ldx, r < rows ? c : cols, cols, v[u]);
-        m = fmaxf(m, absmax8(v[u]));
-    }
-    m = dpp_max16(m);
-    m = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0)),
-                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16))),
-              fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32)),
-                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 48))));
-    if ((threadIdx.x & 63) == 0)
-        wave_max[threadIdx.x >> 6] = m;
-    __syncthreads();
-    float amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
-    TileScale ts = make_scale(amax);
+        for (int u = 0; u < 8; ++u) {
+            const int64_t r = r0 + g + 16 * u;
+            raw_load(x + (r < rows ? r : 0) * ldx, r < rows ? c : cols, cols, R[u]);
+        }
+    };
+    auto quantize = [&](uint32_t b, const Raw8<T>* R, int parity) {
+        int64_t r0, c;
+        origin(b, r0, c);
+        float m = 0.0f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        int64_t r = r0 + g + 16 * u;
-        uint32_t lo = quant4(v[u][0], v[u][1], v[u][2], v[u][3], ts);
-        uint32_t hi = quant4(v[u][4], v[u][5], v[u][6], v[u][7], ts);
-        if (r < rows && c < cols)
-            store8(q + r * ldq, c, cols, lo, hi);
+        for (int u = 0; u < 8; ++u) {
+            float v[8];
+            raw_f32(R[u], c, cols, v);
+            m = fmaxf(m, absmax8(v));
+        }
+        m = dpp_max16(m);
+        m = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0)),
+                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16))),
+                  fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 32)),
+                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 48))));
+        // two alternating slots: a wave that runs ahead into the next block
+        // writes the other slot, so one barrier per block suffices
+        if ((threadIdx.x & 63) == 0)
+            wave_max[parity][threadIdx.x >> 6] = m;
+        __syncthreads();
+        const float amax = fmaxf(fmaxf(wave_max[parity][0], wave_max[parity][1]),
+                                 fmaxf(wave_max[parity][2], wave_max[parity][3]));
+        const TileScale ts = make_scale(amax);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t r = r0 + g + 16 * u;
+            float v[8];
+            raw_f32(R[u], c, cols, v);
+            uint32_t lo, hi;
+            quant8(v, ts, lo, hi);
+            if (r < rows && c < cols)
+                store8(q + r * ldq, c, cols, lo, hi);
+        }
+        if (threadIdx.x == 0)
+            s[(int64_t)(r0 / kTile) * lds + (c - l * 8) / kTile] = ts.s;
+    };
+
+    Raw8<T> A[8], B[8];
+    uint32_t b = blockIdx.x;
+    if (b >= total_blocks) return;
+    load(b, A);
+    for (;;) {
+        const uint32_t b1 = b + gridDim.x;
+        if (b1 < total_blocks) load(b1, B);
+        quantize(b, A, 0);
+        if (b1 >= total_blocks) break;
+        const uint32_t b2 = b1 + gridDim.x;
+        if (b2 < total_blocks) load(b2, A);
+        quantize(b1, B, 1);
+        if (b2 >= total_blocks) break;
+        b = b2;
     }
-    if (threadIdx.x == 0)
-        s[(int64_t)blockIdx.y * lds + blockIdx.x] = ts.s;
 }
 
 // ---------------------------------------------------------------------------
@@ -231,8 +313,8 @@ __global__ __launch_bounds__(kTensorThreads) void tensor_cast_kernel(
         int64_t c = (int64_t)(i - r * chunks_per_row.d) * 8;
         float v[8];
         load8<T>(x + (int64_t)r * ldx, c, cols, v);
-        uint32_t lo = quant4(v[0], v[1], v[2], v[3], ts);
-        uint32_t hi = quant4(v[4], v[5], v[6], v[7], ts);
+        uint32_t lo, hi;
+        quant8(v, ts, lo, hi);
         store8(q + (int64_t)r * ldq, c, cols, lo, hi);
     }
 }
@@ -253,15 +335,18 @@ static void launch_quant(const void* xv, int64_t rows, int64_t cols, int64_t ldx
 {
     const T* x = static_cast<const T*>(xv);
     const int64_t tiles_c = (cols + kTile - 1) / kTile;
+    const int64_t cus = device_cu_count();
     if (kind == FP8Q_ROW_1x128) {
         uint32_t total = (uint32_t)(rows * tiles_c);
         uint32_t blocks = (total + kRowTilesPerBlock - 1) / kRowTilesPerBlock;
         hipLaunchKernelGGL(quant_row_kernel<T>, dim3(blocks), dim3(kRowThreads), 0, st, x, cols,
                            ldx, q, ldq, s, lds, total, make_fastdiv((uint32_t)tiles_c));
     } else if (kind == FP8Q_BLOCK_128x128) {
-        dim3 grid((uint32_t)tiles_c, (uint32_t)((rows + kTile - 1) / kTile));
-        hipLaunchKernelGGL(quant_block_kernel<T>, grid, dim3(kBlockThreads), 0, st, x, rows, cols,
-                           ldx, q, ldq, s, lds);
+        const uint32_t total = (uint32_t)(tiles_c * ((rows + kTile - 1) / kTile));
+        // two resident workgroups per CU (about 220 VGPRs per lane)
+        uint32_t blocks = total < (uint32_t)(cus * 2) ? total : (uint32_t)(cus * 2);
+        hipLaunchKernelGGL(quant_block_kernel<T>, dim3(blocks), dim3(kBlockThreads), 0, st, x, rows,
+                           cols, ldx, q, ldq, s, lds, total, make_fastdiv((uint32_t)tiles_c));
     } else {
         uint32_t* cell = reinterpret_cast<uint32_t*>(s);
         int64_t cpr = (cols + 7) / 8;

@@ -22,7 +22,18 @@
 namespace fp8q {
 
 constexpr int kQtThreads = 256;
-constexpr int kStagePitch = 144;   // bytes per staged X^T row (128 + 16: 16-byte aligned, skewed banks)
+constexpr int kStagePitch = 128;   // bytes per staged X^T row
+constexpr int kColPitch = 130;     // floats per row group in the column-maxima array
+
+// LDS layouts (64 banks of 4 bytes), checked with a bank model:
+//  * column maxima: row group g, column c = 8l + j at g * 130 + 8l + (j ^ (l >> 3));
+//    the b32 writes (fixed j) and the per-column reads are conflict-free;
+//  * staged X^T tile: the 8-byte unit of column c, rows 8g..8g+7, at byte
+//    c * 128 + 8 (g ^ sw(c)), sw(c) = 2 ((c ^ (c >> 3)) & 7); even keys keep
+//    units 2t, 2t+1 together, so a 16-byte read of X^T row c at segment t
+//    sits at c * 128 + 16 (t ^ sw(c) / 2).  Writes are 2-way, reads 1-way.
+__device__ __forceinline__ int colmax_idx(int c) { return 8 * (c >> 3) + ((c & 7) ^ ((c >> 6) & 1)); }
+__device__ __forceinline__ int stage_key(int c) { return 2 * ((c ^ (c >> 3)) & 7); }
 
 template <typename T>
 __device__ __forceinline__ void qt_load8(const T* row, int64_t c, int64_t cols, float v[8]);
@@ -73,7 +84,7 @@ __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
     uint8_t* __restrict__ q_row, int64_t ldq_row, float* __restrict__ s_row, int64_t lds_row,
     uint8_t* __restrict__ q_colT, int64_t ldq_colT, float* __restrict__ s_colT, int64_t lds_colT)
 {
-    __shared__ float col_part[16][kTile];        // per row-group column maxima
+    __shared__ float col_part[16 * kColPitch];   // per row-group column maxima
     __shared__ float row_amax[kTile];
     __shared__ float row_s[kTile], row_y[kTile];
     __shared__ int row_mode[kTile];
@@ -112,15 +123,16 @@ __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
         float m = fabsf(v[0][j]);
 #pragma unroll
         for (int u = 1; u < 8; ++u) m = fmaxf(m, fabsf(v[u][j]));
-        col_part[g][8 * l + j] = m;
+        col_part[g * kColPitch + colmax_idx(8 * l + j)] = m;
     }
     __syncthreads();
 
     // one thread per column (tid < 128) and per row (tid >= 128)
     if (tid < kTile) {
-        float m = col_part[0][tid];
+        const int ci = colmax_idx(tid);
+        float m = col_part[ci];
 #pragma unroll
-        for (int k = 1; k < 16; ++k) m = fmaxf(m, col_part[k][tid]);
+        for (int k = 1; k < 16; ++k) m = fmaxf(m, col_part[k * kColPitch + ci]);
         TileScale ts = make_scale(m);
         col_s[tid] = ts.s;
         col_y[tid] = ts.y;
@@ -144,8 +156,8 @@ __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
         for (int u = 0; u < 8; ++u) {
             int i = 8 * g + u;
             TileScale ts{row_s[i], row_y[i], row_mode[i]};
-            uint32_t lo = quant4(v[u][0], v[u][1], v[u][2], v[u][3], ts);
-            uint32_t hi = quant4(v[u][4], v[u][5], v[u][6], v[u][7], ts);
+            uint32_t lo, hi;
+            quant8(v[u], ts, lo, hi);
             int64_t r = r0 + i;
             if (r < rows && c < cols) {
                 uint8_t* dst = q_row + r * ldq_row;
@@ -165,9 +177,10 @@ __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
         for (int j = 0; j < 8; ++j) {
             int cj = 8 * l + j;
             TileScale ts{col_s[cj], col_y[cj], col_mode[cj]};
-            uint32_t lo = quant4(v[0][j], v[1][j], v[2][j], v[3][j], ts);
-            uint32_t hi = quant4(v[4][j], v[5][j], v[6][j], v[7][j], ts);
-            *reinterpret_cast<uint2*>(stage + cj * kStagePitch + 8 * g) = make_uint2(lo, hi);
+            const float cv[8] = {v[0][j], v[1][j], v[2][j], v[3][j], v[4][j], v[5][j], v[6][j], v[7][j]};
+            uint32_t lo, hi;
+            quant8(cv, ts, lo, hi);
+            *reinterpret_cast<uint2*>(stage + cj * kStagePitch + 8 * (g ^ stage_key(cj))) = make_uint2(lo, hi);
         }
         __syncthreads();
         // 8 threads per X^T row (16 bytes each), 32 rows per pass
@@ -178,7 +191,7 @@ __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
             int64_t cglob = c0 + cr;
             int64_t rglob = r0 + seg;
             if (cglob < cols && rglob < rows) {
-                uint4 w = *reinterpret_cast<const uint4*>(stage + cr * kStagePitch + seg);
+                uint4 w = *reinterpret_cast<const uint4*>(stage + cr * kStagePitch + 16 * ((tid & 7) ^ (stage_key(cr) >> 1)));
                 uint8_t* dst = q_colT + cglob * ldq_colT + rglob;
                 if (rglob + 16 <= rows) {
                     *reinterpret_cast<uint4*>(dst) = w;

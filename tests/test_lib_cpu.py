@@ -68,7 +68,8 @@ def test_quant_blockwise_validation():
     assert q_blockwise(q=A16 + 8) == fq.ERR_ALIGN
     assert q_blockwise(ldx=260, cols=256) == fq.ERR_ALIGN             # 520 bytes per row
     assert q_blockwise(ldq=264) == fq.ERR_ALIGN
-    assert q_blockwise(kind=fq.BLOCK_128x128, rows=128 * 65536) == fq.ERR_SHAPE
+    # 128x128 blocks are indexed with 31-bit block ids: ceil(rows/128) * ceil(cols/128) < 2^31
+    assert q_blockwise(kind=fq.BLOCK_128x128, rows=128 * (1 << 30)) == fq.ERR_SHAPE
 
 
 def test_quant_transpose_validation():
