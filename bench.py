@@ -103,6 +103,28 @@ def copy_calibration():
                       "launches": 5}))
 
 
+def copy_ceiling_gbs(dev):
+    """Read+write bandwidth of a plain 1 GiB device-to-device copy (larger
+    than the 256 MB last-level cache): the practical HBM ceiling for a
+    stream that reads and writes, reported next to the nominal 8 TB/s."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(5):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 5
+    del src, dst
+    return round(2 * n / (ms * 1e-3) / 1e9, 1)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -232,6 +254,7 @@ def main():
                     "unit": "GB/s", "frac": round(dwork / dt / 1e9 / PEAK_HBM_GBS, 4),
                     "traffic": traffic, "kernel": dname}
     roofline["traffic_unit"] = "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+    hbm_copy = copy_ceiling_gbs(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -258,6 +281,7 @@ def main():
         "kernels": breakdown,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
+        "hbm_copy_GBps": hbm_copy,
     }
     print(json.dumps(out))
 

@@ -407,6 +407,8 @@ void launch_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K, const u
     g.G = (int)G;
     g.b_group_stride = N * K;
     g.sb_group_stride = ((N + 127) / 128) * (int64_t)g.KB;
+    g.num_cus = device_cu_count();
+    if (launch_grouped_gemm_nk(g, c_dtype == FP8Q_BF16, st)) return;
     dim3 grid((uint32_t)(g.tiles_m * g.tiles_n));
     if (c_dtype == FP8Q_BF16)
         hipLaunchKernelGGL((gemm_kernel<128, SA_ROW, SB_BLOCK, false, true, true>), grid,

@@ -54,5 +54,8 @@ __device__ __forceinline__ uint4 mask_bytes(uint4 v, int valid)
 // per-tensor); returns false if that kernel does not cover the call (the
 // caller then uses the general kernel).
 bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, bool out_bf16, hipStream_t st);
+// Grouped (MoE) launch of the same kernel: A row tiles select their expert
+// through the device group offsets; false if the call is not covered.
+bool launch_grouped_gemm_nk(const GemmArgs& g, bool out_bf16, hipStream_t st);
 
 }  // namespace fp8q

@@ -188,9 +188,14 @@ struct Frags {
     float sbk;       // SB of the wave's 128-column block (block-scaled B)
 };
 
-template <int SA_MODE, int SB_MODE, bool B_KN, bool OUT_BF16>
+// groups whose offsets fit in LDS (grouped launches with more fall back)
+constexpr int kMaxLdsGroups = 1024;
+
+template <int SA_MODE, int SB_MODE, bool B_KN, bool OUT_BF16, bool GROUPED>
 __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
 {
+    // grouped (MoE) launches: the device group offsets, copied once
+    __shared__ int32_t goff[GROUPED ? kMaxLdsGroups + 1 : 1];
     __shared__ __attribute__((aligned(16))) uint8_t As[kStages][kAStage];
     __shared__ __attribute__((aligned(16))) uint8_t Bs[kStages][kBStage];
     __shared__ __attribute__((aligned(16))) float SAs[kStages][TBM];
@@ -225,6 +230,10 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     };
     int ti = local;                // index into this XCD's range
     if (ti >= range_len) return;
+    if (GROUPED) {
+        for (int i = tid; i <= p.G; i += kThreads) goff[i] = p.offsets[i];
+        __syncthreads();
+    }
     int64_t m0, n0;
     tile_origin(ti, m0, n0);
 
@@ -240,7 +249,24 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     const int64_t ext_b = B_KN ? (K - 1) * p.ldb + ((N + 15) & ~(int64_t)15)
                                : (N - 1) * p.ldb + ((K + 15) & ~(int64_t)15);
     const __amdgpu_buffer_rsrc_t ra = rsrc(p.a, ext_a);
-    const __amdgpu_buffer_rsrc_t rb = rsrc(p.b, ext_b);
+    __amdgpu_buffer_rsrc_t rb = rsrc(p.b, ext_b);
+    // grouped: the tile's group e (off[e] <= m0 < off[e+1]) selects expert
+    // e's weight and block scales; tiles at or past off[G] are computed
+    // from group G-1 but not stored
+    int grp_e = 0;
+    bool tile_live = true;
+    auto set_group = [&](int64_t tm0) {
+        if (!GROUPED) return;
+        int lo = 0, hi = p.G - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((int64_t)goff[mid] <= tm0) lo = mid; else hi = mid - 1;
+        }
+        grp_e = lo;
+        tile_live = tm0 < (int64_t)goff[p.G];
+        rb = rsrc(p.b + (int64_t)grp_e * p.b_group_stride, ext_b);
+    };
+    set_group(m0);
     uint32_t offa[2], offb[4];
     // per-lane source offsets of the tile at (tm0, tn0), without the chunk's k0
     auto set_tile_offsets = [&](int64_t tm0, int64_t tn0) {
@@ -281,7 +307,8 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
         if (B_KN)
             rsc = rsrc(p.sb, ((int64_t)(KB - 1) * p.ldsb + nblocks) * 4);
         else
-            rsc = rsrc(p.sb, ((nblocks - 1) * p.ldsb + KB) * 4);
+            rsc = rsrc(p.sb + (GROUPED ? (int64_t)grp_e * p.sb_group_stride : 0),
+                       ((nblocks - 1) * p.ldsb + KB) * 4);
     } else {
         sc_kind = 3;
         rsc = rsrc(p.sa, 4);
@@ -477,13 +504,14 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
         // first so that waiting for the next tile's first chunk (vmcnt) does
         // not also wait for its second chunk.
         const int64_t cm0 = m0, cn0 = n0;
+        const bool store_tile = tile_live;
         ti += nwg;
         const bool more = ti < range_len;
         // epilogue: lane l holds C[m][n .. n+3] of each block
 #pragma unroll
         for (int i = 0; i < NMI; ++i) {
             const int64_t m = cm0 + wm0 + 16 * i + lrow;
-            if (m >= M) continue;
+            if (m >= M || !store_tile) continue;
 #pragma unroll
             for (int j = 0; j < NNI; ++j) {
                 const int64_t n = cn0 + wn0 + 16 * j + 4 * kgrp;
@@ -511,8 +539,11 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
         }
         if (more) {
             tile_origin(ti, m0, n0);
+            set_group(m0);
             set_tile_offsets(m0, n0);
             set_scale_offset(m0, n0);
+            if (GROUPED && sc_kind == 2)
+                rsc = rsrc(p.sb + (int64_t)grp_e * p.sb_group_stride, ((nblocks - 1) * p.ldsb + KB) * 4);
             // every wave is done reading this tile's stages
             __builtin_amdgcn_s_barrier();
             if (KB > 0) issue(0);
@@ -524,7 +555,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     wait_vm<0>();
 }
 
-template <int SA_MODE, int SB_MODE, bool B_KN>
+template <int SA_MODE, int SB_MODE, bool B_KN, bool GROUPED = false>
 static void launch2(const GemmArgs& g, bool bf, hipStream_t st)
 {
     GemmArgs a = g;
@@ -534,9 +565,19 @@ static void launch2(const GemmArgs& g, bool bf, hipStream_t st)
     const int tiles = a.tiles_m * a.tiles_n;
     dim3 grid((uint32_t)(tiles < g.num_cus ? tiles : g.num_cus));
     if (bf)
-        hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, B_KN, true>), grid, dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, B_KN, true, GROUPED>), grid, dim3(kThreads), 0, st, a);
     else
-        hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, B_KN, false>), grid, dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, B_KN, false, GROUPED>), grid, dim3(kThreads), 0, st, a);
+}
+
+bool launch_grouped_gemm_nk(const GemmArgs& g, bool out_bf16, hipStream_t st)
+{
+    const int64_t lim = (int64_t)1 << 31;
+    if (g.G > kMaxLdsGroups || g.M * g.lda >= lim || (g.N + TBK) * g.ldb >= lim ||
+        g.M * g.ldsa * 4 >= lim || g.sb_group_stride * 4 >= lim || (int64_t)g.KB * TBK >= lim)
+        return false;
+    launch2<SA_ROW, SB_BLOCK, false, true>(g, out_bf16, st);
+    return true;
 }
 
 bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, bool out_bf16, hipStream_t st)
