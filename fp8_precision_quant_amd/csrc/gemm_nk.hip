@@ -201,6 +201,9 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     __shared__ __attribute__((aligned(16))) float SAs[kStages][TBM];
     __shared__ __attribute__((aligned(16))) float SBs[kStages][TBN];
     __shared__ __attribute__((aligned(16))) float Sdummy[64];
+    // destination of the loads issued for chunks past the end (kept so that
+    // every chunk issues the same number of loads)
+    __shared__ __attribute__((aligned(16))) uint8_t Ddummy[1024];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -330,24 +333,34 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     };
     set_scale_offset(m0, n0);
 
-    auto issue = [&](int kb) {
+    // Load u (0..6) of chunk kb: A rows (u < 2), B rows (2 <= u < 6), scales
+    // (u = 6).  Chunks at or past KB go to the dummy buffers (their source
+    // offsets lie in or past the operand; the buffer resource bounds them).
+    auto issue_one = [&](int kb, int u) {
         const int st = kb % kStages;
+        const bool real = kb < KB;
         const uint32_t k0 = (uint32_t)kb * TBK;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) dma16(ra, &As[st][(16 * wave + 8 * t) * TBK], offa[t], k0);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        if (u < 2) {
+            dma16(ra, real ? &As[st][(16 * wave + 8 * u) * TBK] : Ddummy, offa[u], k0);
+        } else if (u < 6) {
+            const int t = u - 2;
             if (B_KN)
-                dma16(rb, &Bs[st][(16 * wave + 4 * t) * TBN], offb[t], k0 * (uint32_t)p.ldb);
+                dma16(rb, real ? &Bs[st][(16 * wave + 4 * t) * TBN] : Ddummy, offb[t], k0 * (uint32_t)p.ldb);
             else
-                dma16(rb, &Bs[st][(32 * wave + 8 * t) * TBK], offb[t], k0);
+                dma16(rb, real ? &Bs[st][(32 * wave + 8 * t) * TBK] : Ddummy, offb[t], k0);
+        } else {
+            float* dst = !real ? Sdummy
+                       : sc_kind == 0 ? &SAs[st][64 * wave]
+                       : sc_kind == 1 ? &SBs[st][64 * (wave - 2)]
+                       : sc_kind == 2 ? &SBs[st][0] : Sdummy;
+            const uint32_t sc_soff = (sc_kind == 3 || !real) ? 0u
+                                   : (sc_kind == 2 && B_KN) ? (uint32_t)(kb * p.ldsb * 4) : (uint32_t)kb * 4;
+            dma4(rsc, dst, sc_off, sc_soff);
         }
-        float* dst = sc_kind == 0 ? &SAs[st][64 * wave]
-                   : sc_kind == 1 ? &SBs[st][64 * (wave - 2)]
-                   : sc_kind == 2 ? &SBs[st][0] : Sdummy;
-        const uint32_t sc_soff = sc_kind == 3 ? 0u
-                               : (sc_kind == 2 && B_KN) ? (uint32_t)(kb * p.ldsb * 4) : (uint32_t)kb * 4;
-        dma4(rsc, dst, sc_off, sc_soff);
+    };
+    auto issue = [&](int kb) {
+#pragma unroll
+        for (int u = 0; u < kLoadsPerChunk; ++u) issue_one(kb, u);
     };
 
     v4f acc[NMI][NNI];
@@ -431,31 +444,37 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
 
     // one MFMA per 16x16 block gives the chunk's fp32 partial, one FMA per
     // output scales it into the accumulator
-    auto compute = [&](const Frags& f) {
+    // One MFMA per 16x16 block gives the chunk's fp32 partial and four FMAs
+    // per lane scale it into the accumulator.  The FMAs of block u run
+    // behind the MFMA of block u+1 (software pipelined), and the loads of
+    // chunk kb_load are issued one per MFMA, so that a busy memory pipeline
+    // holds up at most one issue slot at a time.  Scheduling fences keep
+    // each step's instructions together.
+    auto compute = [&](const Frags& f, int kb_load) {
         float rs[NMI];
 #pragma unroll
         for (int i = 0; i < NMI; ++i) {
             const float sa_i = SA_MODE == SA_ROW ? f.sa[i] : sa_t;
             rs[i] = SB_MODE == SB_BLOCK ? sa_i * f.sbk : SB_MODE == SB_TENSOR ? sa_i * sb_t : sa_i;
         }
+        auto scale_into = [&](const v4f& part, int i, int j) {
 #pragma unroll
-        for (int j = 0; j < NNI; ++j) {
-#pragma unroll
-            for (int i = 0; i < NMI; ++i) {
-                v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[j], f.a[i], zero, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float t = SB_MODE == SB_ROW ? rs[i] * f.sbc[j][r] : rs[i];
-                    acc[i][j][r] = __builtin_fmaf(part[r], t, acc[i][j][r]);
-                }
+            for (int r = 0; r < 4; ++r) {
+                const float t = SB_MODE == SB_ROW ? rs[i] * f.sbc[j][r] : rs[i];
+                acc[i][j][r] = __builtin_fmaf(part[r], t, acc[i][j][r]);
             }
-        }
-        // interleave: one MFMA, then the VALU work of earlier partials
+        };
+        v4f prev = zero;
 #pragma unroll
         for (int u = 0; u < NMI * NNI; ++u) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                            // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, SB_MODE == SB_ROW ? 8 : 4, 0);    // VALU
+            const int j = u / NMI, i = u % NMI;
+            const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[j], f.a[i], zero, 0, 0, 0, 0, 0, 0);
+            if (u < kLoadsPerChunk) issue_one(kb_load, u);
+            if (u > 0) scale_into(prev, (u - 1) % NMI, (u - 1) / NMI);
+            __builtin_amdgcn_sched_barrier(0);
+            prev = part;
         }
+        scale_into(prev, NMI - 1, NNI - 1);
         // keep the FMAs here: sunk past the next chunk's branches they would
         // hold every partial live across them
 #pragma unroll
@@ -470,22 +489,23 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     // flight while the MFMAs of chunk kb run from the other register set.
     auto ready = [&](int kb) {
         __builtin_amdgcn_sched_barrier(0);
-        if (kb + 1 < KB)
-            wait_vm<kLoadsPerChunk>();
-        else
-            wait_vm<0>();
+        // the loads of chunk kb+1 (real or dummy) are the only younger ones
+        wait_vm<kLoadsPerChunk>();
         __builtin_amdgcn_s_barrier();
         if (kb == KB - 1 && k_tail < TBK) {
             zero_k_tail<B_KN>(As[kb % kStages], Bs[kb % kStages], k_tail, tid);
             __syncthreads();
         }
-        if (kb + 2 < KB) issue(kb + 2);
         __builtin_amdgcn_sched_barrier(0);
     };
 
     // first tile's first two chunks
-    if (KB > 0) issue(0);
-    if (KB > 1) issue(1);
+    // chunks 0 and 1 (dummy if KB == 1) of the first tile; with K == 0 the
+    // operands may be NULL and nothing is loaded
+    if (KB > 0) {
+        issue(0);
+        issue(1);
+    }
     for (;;) {
 #pragma unroll
         for (int i = 0; i < NMI; ++i)
@@ -497,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
                 ready(kb);
                 read_frags(kb % kStages, f);
                 wait_frags(f);
-                compute(f);
+                compute(f, kb + 2);
             }
         }
         // Store this tile, then start the next tile's loads.  The stores go
@@ -546,8 +566,10 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
                 rsc = rsrc(p.sb + (int64_t)grp_e * p.sb_group_stride, ((nblocks - 1) * p.ldsb + KB) * 4);
             // every wave is done reading this tile's stages
             __builtin_amdgcn_s_barrier();
-            if (KB > 0) issue(0);
-            if (KB > 1) issue(1);
+            if (KB > 0) {
+                issue(0);
+                issue(1);
+            }
         }
         if (!more) break;
     }
