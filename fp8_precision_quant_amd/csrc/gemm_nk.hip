@@ -91,6 +91,20 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, float* lds_words
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds_words, 4, voff, soff, 0, 0);
 }
 
+// waits until at most N LDS (or scalar) reads are pending; x is an operand
+// so that its users stay below the wait
+template <int N>
+__device__ __forceinline__ void lgkm_wait(v8i& x)
+{
+    static_assert(N >= 0 && N < 16, "lgkmcnt immediate");
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "n"(N));
+}
+
+__device__ __forceinline__ void pin4(v8i& a, v8i& b, v8i& c, v8i& d)
+{
+    asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm()
 {
@@ -394,26 +408,10 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     const uint32_t lds_sblk = lds_addr(SBs) + 4 * (wn0 / 128);
 
     // issue the LDS reads of one chunk's operands and scales (no wait)
+    // Issue order: scales, the 4 A fragments, then per B fragment j its
+    // column scales (row-scaled B) and its reads.  LDS reads complete in
+    // order, so compute can start on B fragment 0 while 1..3 are in flight.
     auto read_frags = [&](int st, Frags& f) {
-        const uint32_t a0 = lds_a + st * kAStage + a_off0, a1 = lds_a + st * kAStage + a_off1;
-        f.a[0] = cat(ds128<0 * 16 * TBK>(a0), ds128<0 * 16 * TBK>(a1));
-        f.a[1] = cat(ds128<1 * 16 * TBK>(a0), ds128<1 * 16 * TBK>(a1));
-        f.a[2] = cat(ds128<2 * 16 * TBK>(a0), ds128<2 * 16 * TBK>(a1));
-        f.a[3] = cat(ds128<3 * 16 * TBK>(a0), ds128<3 * 16 * TBK>(a1));
-        if (B_KN) {
-            const uint32_t bs = lds_b + st * kBStage;
-#pragma unroll
-            for (int j = 0; j < NNI; ++j) {
-                const uint32_t ad = bs + kn_off[j];
-                f.b[j] = cat4(ds64tr<0>(ad), ds64tr<8 * TBN>(ad), ds64tr<16 * TBN>(ad), ds64tr<24 * TBN>(ad));
-            }
-        } else {
-            const uint32_t b0 = lds_b + st * kBStage + b_off0, b1 = lds_b + st * kBStage + b_off1;
-            f.b[0] = cat(ds128<0 * 16 * TBK>(b0), ds128<0 * 16 * TBK>(b1));
-            f.b[1] = cat(ds128<1 * 16 * TBK>(b0), ds128<1 * 16 * TBK>(b1));
-            f.b[2] = cat(ds128<2 * 16 * TBK>(b0), ds128<2 * 16 * TBK>(b1));
-            f.b[3] = cat(ds128<3 * 16 * TBK>(b0), ds128<3 * 16 * TBK>(b1));
-        }
         if (SA_MODE == SA_ROW) {
             const uint32_t sa = lds_sa + st * TBM * 4;
             f.sa[0] = ds32<0>(sa);
@@ -421,26 +419,36 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
             f.sa[2] = ds32<128>(sa);
             f.sa[3] = ds32<192>(sa);
         }
-        if (SB_MODE == SB_ROW) {
-            const uint32_t sbp = lds_sb + st * TBN * 4;
-            f.sbc[0] = (v4f)ds128<0>(sbp);
-            f.sbc[1] = (v4f)ds128<64>(sbp);
-            f.sbc[2] = (v4f)ds128<128>(sbp);
-            f.sbc[3] = (v4f)ds128<192>(sbp);
-        }
         if (SB_MODE == SB_BLOCK) f.sbk = ds32<0>(lds_sblk + st * TBN * 4);
+        const uint32_t a0 = lds_a + st * kAStage + a_off0, a1 = lds_a + st * kAStage + a_off1;
+        f.a[0] = cat(ds128<0 * 16 * TBK>(a0), ds128<0 * 16 * TBK>(a1));
+        f.a[1] = cat(ds128<1 * 16 * TBK>(a0), ds128<1 * 16 * TBK>(a1));
+        f.a[2] = cat(ds128<2 * 16 * TBK>(a0), ds128<2 * 16 * TBK>(a1));
+        f.a[3] = cat(ds128<3 * 16 * TBK>(a0), ds128<3 * 16 * TBK>(a1));
+        const uint32_t sbp = lds_sb + st * TBN * 4;
+        const uint32_t bs = lds_b + st * kBStage;
+        const uint32_t b0 = bs + b_off0, b1 = bs + b_off1;
+#pragma unroll
+        for (int j = 0; j < NNI; ++j) {
+            if (SB_MODE == SB_ROW) {
+                if (j == 0) f.sbc[0] = (v4f)ds128<0>(sbp);
+                if (j == 1) f.sbc[1] = (v4f)ds128<64>(sbp);
+                if (j == 2) f.sbc[2] = (v4f)ds128<128>(sbp);
+                if (j == 3) f.sbc[3] = (v4f)ds128<192>(sbp);
+            }
+            if (B_KN) {
+                const uint32_t ad = bs + kn_off[j];
+                f.b[j] = cat4(ds64tr<0>(ad), ds64tr<8 * TBN>(ad), ds64tr<16 * TBN>(ad), ds64tr<24 * TBN>(ad));
+            } else {
+                if (j == 0) f.b[0] = cat(ds128<0 * 16 * TBK>(b0), ds128<0 * 16 * TBK>(b1));
+                if (j == 1) f.b[1] = cat(ds128<1 * 16 * TBK>(b0), ds128<1 * 16 * TBK>(b1));
+                if (j == 2) f.b[2] = cat(ds128<2 * 16 * TBK>(b0), ds128<2 * 16 * TBK>(b1));
+                if (j == 3) f.b[3] = cat(ds128<3 * 16 * TBK>(b0), ds128<3 * 16 * TBK>(b1));
+            }
+        }
     };
-    // wait for them; the registers are operands so that no use moves above
-    // (volatile asm keeps its order, so the scale pins stay behind the wait;
-    // only the scales the mode reads are pinned, the rest stay dead)
-    auto wait_frags = [&](Frags& f) {
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]),
-                       "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3]));
-        if (SA_MODE == SA_ROW) asm volatile("" : "+v"(f.sa[0]), "+v"(f.sa[1]), "+v"(f.sa[2]), "+v"(f.sa[3]));
-        if (SB_MODE == SB_ROW) asm volatile("" : "+v"(f.sbc[0]), "+v"(f.sbc[1]), "+v"(f.sbc[2]), "+v"(f.sbc[3]));
-        if (SB_MODE == SB_BLOCK) asm volatile("" : "+v"(f.sbk));
-    };
+    // LDS reads per B fragment group (its column scales and its reads)
+    constexpr int kPerB = (SB_MODE == SB_ROW ? 1 : 0) + (B_KN ? 4 : 2);
 
     // one MFMA per 16x16 block gives the chunk's fp32 partial, one FMA per
     // output scales it into the accumulator
@@ -450,13 +458,33 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     // chunk kb_load are issued one per MFMA, so that a busy memory pipeline
     // holds up at most one issue slot at a time.  Scheduling fences keep
     // each step's instructions together.
-    auto compute = [&](const Frags& f, int kb_load) {
+    auto compute = [&](Frags& f, int kb_load) {
+        // B fragment j (and, for j = 0, everything issued before it) has
+        // landed once only the reads of fragments j+1.. may be pending; the
+        // registers are asm operands, so no use moves above the wait
+        auto wait_b = [&](int j) {
+            if (j == 0) {
+                lgkm_wait<(NNI - 1) * kPerB>(f.b[0]);
+                pin4(f.a[0], f.a[1], f.a[2], f.a[3]);
+                if (SA_MODE == SA_ROW) asm volatile("" : "+v"(f.sa[0]), "+v"(f.sa[1]), "+v"(f.sa[2]), "+v"(f.sa[3]));
+                if (SB_MODE == SB_BLOCK) asm volatile("" : "+v"(f.sbk));
+            } else if (j == 1) {
+                lgkm_wait<(NNI - 2) * kPerB>(f.b[1]);
+            } else if (j == 2) {
+                lgkm_wait<(NNI - 3) * kPerB>(f.b[2]);
+            } else {
+                lgkm_wait<0>(f.b[3]);
+            }
+            if (SB_MODE == SB_ROW) asm volatile("" : "+v"(f.sbc[j]));
+        };
         float rs[NMI];
+        auto set_rs = [&]() {
 #pragma unroll
-        for (int i = 0; i < NMI; ++i) {
-            const float sa_i = SA_MODE == SA_ROW ? f.sa[i] : sa_t;
-            rs[i] = SB_MODE == SB_BLOCK ? sa_i * f.sbk : SB_MODE == SB_TENSOR ? sa_i * sb_t : sa_i;
-        }
+            for (int i = 0; i < NMI; ++i) {
+                const float sa_i = SA_MODE == SA_ROW ? f.sa[i] : sa_t;
+                rs[i] = SB_MODE == SB_BLOCK ? sa_i * f.sbk : SB_MODE == SB_TENSOR ? sa_i * sb_t : sa_i;
+            }
+        };
         auto scale_into = [&](const v4f& part, int i, int j) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -468,6 +496,8 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
 #pragma unroll
         for (int u = 0; u < NMI * NNI; ++u) {
             const int j = u / NMI, i = u % NMI;
+            if (i == 0) wait_b(j);
+            if (u == 0) set_rs();
             const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[j], f.a[i], zero, 0, 0, 0, 0, 0, 0);
             if (u < kLoadsPerChunk) issue_one(kb_load, u);
             if (u > 0) scale_into(prev, (u - 1) % NMI, (u - 1) / NMI);
@@ -516,7 +546,6 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
             for (int kb = 0; kb < KB; ++kb) {
                 ready(kb);
                 read_frags(kb % kStages, f);
-                wait_frags(f);
                 compute(f, kb + 2);
             }
         }
