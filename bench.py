@@ -60,6 +60,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-moe", action="store_true", help="skip the grouped MoE GEMM timing")
     p.add_argument("--cpu-rows", type=int, default=4096,
                    help="output rows per GEMM in the oracle's timed sample")
     p.add_argument("--copy-calibration", action="store_true",
@@ -123,6 +124,52 @@ def copy_ceiling_gbs(dev):
     ms = a.elapsed_time(b) / 5
     del src, dst
     return round(2 * n / (ms * 1e-3) / 1e9, 1)
+
+
+def moe_grouped(dev, reps=10):
+    """Grouped MoE GEMMs (outside the step): 8192 tokens, hidden 2048, 128
+    experts of intermediate 768, top-8 seeded Zipf(1.1) routing, groups padded
+    to 128 rows; random operands generated on the device.  TFLOP/s count the
+    real (unpadded) rows only."""
+    import torch
+    import fp8_precision_quant_amd as fq
+    import synthetic
+
+    T, H, G, I, topk = 8192, 2048, 128, 768, 8
+    choice = synthetic.zipf_topk_routing(T, G, topk, 1.1, 402)
+    counts = np.bincount(choice.reshape(-1), minlength=G).astype(np.int64)
+    padded = -(-counts // 128) * 128
+    offsets = np.zeros(G + 1, np.int64)
+    offsets[1:] = np.cumsum(padded)
+    M_pad = int(offsets[-1])
+    off = torch.from_numpy(offsets.astype(np.int32)).to(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    out = {"tokens": T, "experts": G, "topk": topk, "real_rows": int(counts.sum()), "M_pad": M_pad}
+    for name, N, K in (("gate_up", 2 * I, H), ("down", H, I)):
+        a = torch.randn((M_pad, K), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        w = (0.02 * torch.randn((G * N, K), generator=gen, device=dev, dtype=torch.float32)).to(torch.bfloat16)
+        qa, sa = fq.fp8_quant_blockwise(a, fq.ROW_1x128)
+        qw, sw = fq.fp8_quant_blockwise(w, fq.BLOCK_128x128)
+        qw = qw.view(G, N, K)
+        sw = sw.view(G, -(-N // 128), -(-K // 128))
+        c = torch.empty((M_pad, N), dtype=torch.bfloat16, device=dev)
+        fq.fp8_grouped_gemm(qa, sa, off, qw, sw, c=c)
+        st = torch.cuda.current_stream(dev)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(reps):
+            fq.fp8_grouped_gemm(qa, sa, off, qw, sw, c=c)
+        e1.record(st)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        flops = 2.0 * counts.sum() * N * K
+        out[name] = {"N": N, "K": K, "us": round(us, 2), "TFLOP/s": round(flops / (us * 1e-6) / 1e12, 1),
+                     "frac_peak": round(flops / (us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+        del a, w, qa, sa, qw, sw, c
+    return out
 
 
 def main():
@@ -255,6 +302,7 @@ def main():
                     "traffic": traffic, "kernel": dname}
     roofline["traffic_unit"] = "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
     hbm_copy = copy_ceiling_gbs(dev)
+    moe = None if args.no_moe else moe_grouped(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -282,6 +330,7 @@ def main():
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
         "hbm_copy_GBps": hbm_copy,
+        "moe_grouped": moe,
     }
     print(json.dumps(out))
 
@@ -307,7 +356,7 @@ def cpu_baseline(x_bits, w_bits, dy_bits, rows_per_gemm):
     _, _, qxT, sxT = oracle.quant_transpose(xf)
     t_t = time.perf_counter() - t_t0
     rows = synthetic.sample_rows(M, rows_per_gemm, 7)
-    rows_w = synthetic.sample_rows(N, rows_per_gemm, 8)
+    rows_w = synthetic.sample_rows(N, 2 * rows_per_gemm, 8)
     t_g0 = time.perf_counter()
     oracle.gemm_blockscaled(qx, sx, "row", qw, sw, "block", "NK", rows=rows)
     oracle.gemm_blockscaled(qdy, sdy, "row", qw, sw, "block", "KN", rows=rows)
@@ -317,9 +366,9 @@ def cpu_baseline(x_bits, w_bits, dy_bits, rows_per_gemm):
     return {"value": round(flops / t_g / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": "quant 1x128 x + 128x128 W (full tensors, %.1f GB/s), quant+transpose of dy and x "
-                      "(full, %.2f s), and fwd/dgrad/wgrad GEMMs on min(M, %d) sampled output rows each "
+                      "(full, %.2f s), and fwd/dgrad GEMMs on all %d rows, wgrad on %d sampled rows "
                       "(%.2f s); value = GEMM FLOPs of the sample / GEMM time"
-                      % (q_bytes / t_q / 1e9, t_t, len(rows_w), t_g),
+                      % (q_bytes / t_q / 1e9, t_t, len(rows), len(rows_w), t_g),
             "total_s": round(time.perf_counter() - t0, 2)}
 
 
