@@ -458,33 +458,36 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     // chunk kb_load are issued one per MFMA, so that a busy memory pipeline
     // holds up at most one issue slot at a time.  Scheduling fences keep
     // each step's instructions together.
-    auto compute = [&](Frags& f, int kb_load) {
-        // B fragment j (and, for j = 0, everything issued before it) has
-        // landed once only the reads of fragments j+1.. may be pending; the
-        // registers are asm operands, so no use moves above the wait
-        auto wait_b = [&](int j) {
-            if (j == 0) {
-                lgkm_wait<(NNI - 1) * kPerB>(f.b[0]);
-                pin4(f.a[0], f.a[1], f.a[2], f.a[3]);
-                if (SA_MODE == SA_ROW) asm volatile("" : "+v"(f.sa[0]), "+v"(f.sa[1]), "+v"(f.sa[2]), "+v"(f.sa[3]));
-                if (SB_MODE == SB_BLOCK) asm volatile("" : "+v"(f.sbk));
-            } else if (j == 1) {
-                lgkm_wait<(NNI - 2) * kPerB>(f.b[1]);
-            } else if (j == 2) {
-                lgkm_wait<(NNI - 3) * kPerB>(f.b[2]);
-            } else {
-                lgkm_wait<0>(f.b[3]);
-            }
-            if (SB_MODE == SB_ROW) asm volatile("" : "+v"(f.sbc[j]));
-        };
-        float rs[NMI];
-        auto set_rs = [&]() {
+    //
+    // B fragment j (and, for j = 0, everything issued before it) has landed
+    // once only the reads of fragments j+1.. may be pending; the registers
+    // are asm operands, so no use moves above the wait.
+    auto wait_b = [&](Frags& f, int j) {
+        if (j == 0) {
+            lgkm_wait<(NNI - 1) * kPerB>(f.b[0]);
+            pin4(f.a[0], f.a[1], f.a[2], f.a[3]);
+            if (SA_MODE == SA_ROW) asm volatile("" : "+v"(f.sa[0]), "+v"(f.sa[1]), "+v"(f.sa[2]), "+v"(f.sa[3]));
+            if (SB_MODE == SB_BLOCK) asm volatile("" : "+v"(f.sbk));
+        } else if (j == 1) {
+            lgkm_wait<(NNI - 2) * kPerB>(f.b[1]);
+        } else if (j == 2) {
+            lgkm_wait<(NNI - 3) * kPerB>(f.b[2]);
+        } else {
+            lgkm_wait<0>(f.b[3]);
+        }
+        if (SB_MODE == SB_ROW) asm volatile("" : "+v"(f.sbc[j]));
+    };
+    float rs[NMI];   // per-row combined scales of the chunk being computed
+    auto set_rs = [&](const Frags& f) {
 #pragma unroll
-            for (int i = 0; i < NMI; ++i) {
-                const float sa_i = SA_MODE == SA_ROW ? f.sa[i] : sa_t;
-                rs[i] = SB_MODE == SB_BLOCK ? sa_i * f.sbk : SB_MODE == SB_TENSOR ? sa_i * sb_t : sa_i;
-            }
-        };
+        for (int i = 0; i < NMI; ++i) {
+            const float sa_i = SA_MODE == SA_ROW ? f.sa[i] : sa_t;
+            rs[i] = SB_MODE == SB_BLOCK ? sa_i * f.sbk : SB_MODE == SB_TENSOR ? sa_i * sb_t : sa_i;
+        }
+    };
+    // the MFMAs of B fragments [jlo, jhi); loads of chunk kb_load (if
+    // with_loads) ride on the first 7 of them
+    auto blocks = [&](Frags& f, int jlo, int jhi, bool staged, bool with_loads, int kb_load) {
         auto scale_into = [&](const v4f& part, int i, int j) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -496,21 +499,31 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
 #pragma unroll
         for (int u = 0; u < NMI * NNI; ++u) {
             const int j = u / NMI, i = u % NMI;
-            if (i == 0) wait_b(j);
-            if (u == 0) set_rs();
+            if (j < jlo || j >= jhi) continue;
+            const int v = u - jlo * NMI;
+            if (staged && i == 0) wait_b(f, j);
+            if (staged && u == 0) set_rs(f);
             const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[j], f.a[i], zero, 0, 0, 0, 0, 0, 0);
-            if (u < kLoadsPerChunk) issue_one(kb_load, u);
-            if (u > 0) scale_into(prev, (u - 1) % NMI, (u - 1) / NMI);
+            if (with_loads && v < kLoadsPerChunk) issue_one(kb_load, v);
+            if (v > 0) scale_into(prev, (u - 1) % NMI, (u - 1) / NMI);
             __builtin_amdgcn_sched_barrier(0);
             prev = part;
         }
-        scale_into(prev, NMI - 1, NNI - 1);
+        scale_into(prev, NMI - 1, jhi - 1);
         // keep the FMAs here: sunk past the next chunk's branches they would
         // hold every partial live across them
 #pragma unroll
         for (int i = 0; i < NMI; ++i)
 #pragma unroll
-            for (int j = 0; j < NNI; ++j) asm volatile("" : "+v"(acc[i][j]));
+            for (int j = 0; j < NNI; ++j)
+                if (j >= jlo && j < jhi) asm volatile("" : "+v"(acc[i][j]));
+    };
+    // every read of the chunk in f has completed (before a barrier that
+    // lets the chunk's stage be reloaded)
+    auto reads_done = [&](Frags& f) {
+        lgkm_wait<0>(f.b[3]);
+        asm volatile("" : "+v"(f.b[2]));
+        if (SB_MODE == SB_ROW) asm volatile("" : "+v"(f.sbc[2]), "+v"(f.sbc[3]));
     };
 
     // Chunk kb+1 is made ready (its loads landed in every wave, the stage of
@@ -542,11 +555,35 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
 #pragma unroll
             for (int j = 0; j < NNI; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
         if (KB > 0) {
+            // The two wave groups (waves 0-3 and 4-7, one of each per SIMD)
+            // are staggered by half a chunk without an extra barrier: after
+            // the barrier of chunk kb, group 0 reads chunk kb and computes
+            // it, while group 1 first computes the second half (B fragments
+            // 2, 3) of chunk kb-1 from its registers, then reads chunk kb and
+            // computes its first half.  So on each SIMD one wave issues MFMAs
+            // while the other waits for LDS.  Both groups pass one barrier
+            // per chunk; each has its own loop so every compute step runs on
+            // every path.
             Frags f;
-            for (int kb = 0; kb < KB; ++kb) {
-                ready(kb);
-                read_frags(kb % kStages, f);
-                compute(f, kb + 2);
+            if (grp == 0) {
+                for (int kb = 0; kb < KB; ++kb) {
+                    ready(kb);
+                    read_frags(kb % kStages, f);
+                    blocks(f, 0, NNI, true, true, kb + 2);
+                }
+            } else {
+                ready(0);
+                read_frags(0, f);
+                blocks(f, 0, NNI / 2, true, true, 2);
+                reads_done(f);
+                for (int kb = 1; kb < KB; ++kb) {
+                    ready(kb);
+                    blocks(f, NNI / 2, NNI, false, true, kb + 2);   // chunk kb-1
+                    read_frags(kb % kStages, f);
+                    blocks(f, 0, NNI / 2, true, false, 0);          // chunk kb
+                    reads_done(f);
+                }
+                blocks(f, NNI / 2, NNI, false, false, 0);           // chunk KB-1
             }
         }
         // Store this tile, then start the next tile's loads.  The stores go
