@@ -510,6 +510,11 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
             prev = part;
         }
         scale_into(prev, NMI - 1, jhi - 1);
+        // a part with fewer MFMAs than loads issues the rest here
+        if (with_loads) {
+#pragma unroll
+            for (int v = (jhi - jlo) * NMI; v < kLoadsPerChunk; ++v) issue_one(kb_load, v);
+        }
         // keep the FMAs here: sunk past the next chunk's branches they would
         // hold every partial live across them
 #pragma unroll
