@@ -27,6 +27,8 @@
 //  * tile order: workgroups are dealt to the 8 XCDs round-robin, so each XCD
 //    gets a contiguous range of tiles, walked in groups of 16 M-tiles so
 //    neighbouring workgroups share A and B panels in that XCD's L2.
+#include <type_traits>
+
 #include "fp8q_device.h"
 #include "fp8q_internal.h"
 #include "gemm_common.h"
@@ -648,6 +650,417 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     wait_vm<0>();
 }
 
+// ---------------------------------------------------------------------------
+// Split-K ping-pong variant for a B operand scaled per 128x128 block or per
+// tensor (forward, dgrad, grouped).  Same workgroup tile and LDS ring as
+// above, but each wave owns all 128 rows of its 64 columns (32 MFMAs per
+// chunk from 8 A and 4 B fragments: 768 LDS bytes per MFMA instead of 1024),
+// and the two wave groups (one wave of each per SIMD) take alternate K
+// chunks.  Phase q (one barrier each): group q % 2 loads chunk q+2 and reads
+// chunk q from LDS into registers while the other group runs the MFMAs of
+// chunk q-1 from registers, so each SIMD has one wave on the matrix core
+// while its partner waits for memory.  A group loads exactly the chunks it
+// reads, two phases ahead, so waiting for a chunk is vmcnt(0) in its waves.
+// At the end of a tile each group holds the sum over its chunks; the halves
+// are added through LDS (the ring is idle by then), each group finishing and
+// storing 64 of the 128 rows.
+constexpr int PMI = TBM / 16;                  // 16-row blocks per wave
+constexpr int kStageBytes = kAStage + kBStage; // A at 0, B at kAStage
+
+struct FragsPP {
+    v8i a[PMI], b[NNI];
+    float s[PMI];    // combined scale of the lane's row in block i for the chunk
+    float sbk;       // SB of the wave's 128-column block (block-scaled B)
+};
+
+template <int OFF>
+__device__ __forceinline__ void ds_write128(uint32_t addr, v4f v)
+{
+    asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF) : "memory");
+}
+
+template <int I>
+__device__ __forceinline__ v8i frag_nk(uint32_t r0, uint32_t r1)
+{
+    return cat(ds128<I * 16 * TBK>(r0), ds128<I * 16 * TBK>(r1));
+}
+
+template <int SA_MODE, int SB_MODE, bool B_KN, bool OUT_BF16, bool GROUPED>
+__global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs p)
+{
+    static_assert(SB_MODE != SB_ROW, "row-scaled B needs per-column scales in registers");
+    __shared__ int32_t goff[GROUPED ? kMaxLdsGroups + 1 : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t Stg[kStages][kStageBytes];
+    __shared__ __attribute__((aligned(16))) float SAs[kStages][TBM];
+    __shared__ __attribute__((aligned(16))) float SBs[kStages][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;   // chunk parity of this wave
+    const int wq = wave & 3;     // wave within its group: columns [64 wq, 64 wq + 64)
+
+    // persistent workgroups over XCD tile ranges (as in gemm_nk_kernel)
+    const int T = p.tiles_m * p.tiles_n;
+    const int xcd = blockIdx.x & 7;
+    const int local = blockIdx.x >> 3;
+    const int G = gridDim.x;
+    const int nwg = (G >> 3) + (xcd < (G & 7) ? 1 : 0);
+    const int range_start = xcd * (T >> 3) + min(xcd, T & 7);
+    const int range_len = (T >> 3) + (xcd < (T & 7) ? 1 : 0);
+    const int span = kGroupM * p.tiles_n;
+    auto tile_origin = [&](int i, int64_t& tm0, int64_t& tn0) {
+        const int pid = range_start + i;
+        const int group = pid / span;
+        const int first_m = group * kGroupM;
+        const int gsz = min(p.tiles_m - first_m, kGroupM);
+        const int idx = pid - group * span;
+        tm0 = (int64_t)(first_m + idx % gsz) * TBM;
+        tn0 = (int64_t)(idx / gsz) * TBN;
+    };
+    int ti = local;
+    if (ti >= range_len) return;
+    if (GROUPED) {
+        for (int i = tid; i <= p.G; i += kThreads) goff[i] = p.offsets[i];
+        __syncthreads();
+    }
+    int64_t m0, n0;
+    tile_origin(ti, m0, n0);
+
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int KB = p.KB;
+    const int k_tail = (int)(K - (int64_t)(KB - 1) * TBK);
+
+    const int64_t ext_a = (M - 1) * p.lda + ((K + 15) & ~(int64_t)15);
+    const int64_t ext_b = B_KN ? (K - 1) * p.ldb + ((N + 15) & ~(int64_t)15)
+                               : (N - 1) * p.ldb + ((K + 15) & ~(int64_t)15);
+    const __amdgpu_buffer_rsrc_t ra = rsrc(p.a, ext_a);
+    __amdgpu_buffer_rsrc_t rb = rsrc(p.b, ext_b);
+    int grp_e = 0;
+    bool tile_live = true;
+    auto set_group = [&](int64_t tm0) {
+        if (!GROUPED) return;
+        int lo = 0, hi = p.G - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((int64_t)goff[mid] <= tm0) lo = mid; else hi = mid - 1;
+        }
+        grp_e = lo;
+        tile_live = tm0 < (int64_t)goff[p.G];
+        rb = rsrc(p.b + (int64_t)grp_e * p.b_group_stride, ext_b);
+    };
+    set_group(m0);
+
+    // scale loads: waves 0-1 of a group the SA of the tile's 128 rows
+    // (row-scaled A), wave 2 the block scales of its two 128-column blocks
+    const int64_t nblocks = (N + 127) / 128;
+    const int sc_kind = (wq < 2 && SA_MODE == SA_ROW) ? 0 : (wq == 2 && SB_MODE == SB_BLOCK) ? 2 : 3;
+    auto scale_rsrc = [&]() {
+        if (sc_kind == 0) return rsrc(p.sa, ((M - 1) * p.ldsa + KB) * 4);
+        if (sc_kind == 2) {
+            if (B_KN) return rsrc(p.sb, ((int64_t)(KB - 1) * p.ldsb + nblocks) * 4);
+            return rsrc(p.sb + (GROUPED ? (int64_t)grp_e * p.sb_group_stride : 0), ((nblocks - 1) * p.ldsb + KB) * 4);
+        }
+        return rsrc(p.sa, 4);
+    };
+    __amdgpu_buffer_rsrc_t rsc = scale_rsrc();
+
+    // Loads of chunk kb by this wave: A rows [32 wq, 32 wq + 32) (4 DMAs of
+    // 8 rows), B rows [64 wq, 64 wq + 64) of [N][K] B (8 DMAs of 8 rows) or K
+    // rows [32 wq, 32 wq + 32) of [K][N] B (8 DMAs of 4 rows), and its scale
+    // words.  DMA t of an operand differs from DMA 0 by t row steps (a scalar
+    // offset) and, for odd t, by the row's swizzle key (bit 0 of the 8-row
+    // group index, resp. bit 2 of the [K][N] key): two per-lane offsets per
+    // operand.  Rows past M or N are not clamped: lda and ldb are multiples
+    // of 16 and at least K, so such rows start past the buffer resource's
+    // bound and read as zero (they feed only outputs that are not stored);
+    // scale rows past M and a missing second column block read as zero too.
+    // (rebuilt from the lane id for each chunk, so that they do not occupy
+    // registers through the compute phase)
+    struct DmaOffs { uint32_t va[2], vb[2], vsc; };
+    auto dma_offsets = [&]() {
+        DmaOffs o;
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        const int ra_row = 32 * wq + (l >> 3);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            o.va[h] = (uint32_t)((m0 + ra_row) * p.lda) + 16u * (uint32_t)((l & 7) ^ (l >> 3) ^ h);
+            if (B_KN) {
+                const int r = 32 * wq + (l >> 4);
+                const int key = (4 * h + (l >> 4)) ^ (8 * (wq & 1));
+                o.vb[h] = (uint32_t)(r * p.ldb + n0) + 16u * (uint32_t)((l & 15) ^ key);
+            } else {
+                o.vb[h] = (uint32_t)((n0 + 64 * wq + (l >> 3)) * p.ldb) + 16u * (uint32_t)((l & 7) ^ (l >> 3) ^ h);
+            }
+        }
+        o.vsc = sc_kind == 0 ? (uint32_t)((m0 + 64 * wq + l) * p.ldsa * 4)
+              : sc_kind == 2 ? (uint32_t)((n0 / 128 + (l < 1 ? l : 1)) * (B_KN ? 4 : p.ldsb * 4)) : 0u;
+        return o;
+    };
+    auto issue = [&](int kb) {
+        const DmaOffs o = dma_offsets();
+        const int st = kb % kStages;
+        const uint32_t k0 = (uint32_t)kb * TBK;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            dma16(ra, &Stg[st][(32 * wq + 8 * t) * TBK], o.va[t & 1], k0 + (uint32_t)(8 * t * p.lda));
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            if (B_KN)
+                dma16(rb, &Stg[st][kAStage + (32 * wq + 4 * t) * TBN], o.vb[t & 1], (k0 + 4u * t) * (uint32_t)p.ldb);
+            else
+                dma16(rb, &Stg[st][kAStage + (64 * wq + 8 * t) * TBK], o.vb[t & 1], k0 + (uint32_t)(8 * t * p.ldb));
+        }
+        if (sc_kind == 0)
+            dma4(rsc, &SAs[st][64 * wq], o.vsc, (uint32_t)kb * 4);
+        else if (sc_kind == 2)
+            dma4(rsc, &SBs[st][0], o.vsc, B_KN ? (uint32_t)(kb * p.ldsb * 4) : (uint32_t)kb * 4);
+    };
+
+    v4f acc[PMI][NNI];
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    const float sa_t = (SA_MODE == SA_TENSOR && KB > 0) ? p.sa[0] : 0.0f;
+    const float sb_t = (SB_MODE == SB_TENSOR && KB > 0) ? p.sb[0] : 0.0f;
+
+    // the LDS reads of one chunk (addresses rebuilt from the lane id)
+    auto read_frags = [&](int st, FragsPP& f) {
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        const int lrow = l & 15, kgrp = l >> 4;
+        const uint32_t so = lds_addr(Stg) + (uint32_t)st * kStageBytes;
+        if (SA_MODE == SA_ROW) {
+            const uint32_t sa = lds_addr(SAs) + (uint32_t)(st * TBM + lrow) * 4;
+            f.s[0] = ds32<0>(sa);
+            f.s[1] = ds32<64>(sa);
+            f.s[2] = ds32<128>(sa);
+            f.s[3] = ds32<192>(sa);
+            f.s[4] = ds32<256>(sa);
+            f.s[5] = ds32<320>(sa);
+            f.s[6] = ds32<384>(sa);
+            f.s[7] = ds32<448>(sa);
+        }
+        if (SB_MODE == SB_BLOCK) f.sbk = ds32<0>(lds_addr(SBs) + (uint32_t)(st * 64 + (wq >> 1)) * 4);
+        const uint32_t a0 = so + sw(lrow, 2 * kgrp), a1 = so + sw(lrow, 2 * kgrp + 1);
+        f.a[0] = frag_nk<0>(a0, a1);
+        f.a[1] = frag_nk<1>(a0, a1);
+        f.a[2] = frag_nk<2>(a0, a1);
+        f.a[3] = frag_nk<3>(a0, a1);
+        f.a[4] = frag_nk<4>(a0, a1);
+        f.a[5] = frag_nk<5>(a0, a1);
+        f.a[6] = frag_nk<6>(a0, a1);
+        f.a[7] = frag_nk<7>(a0, a1);
+        if (B_KN) {
+            // lane (kgrp, lrow) addresses K row 32 kgrp + lrow / 2 at column
+            // 64 wq + 16 j + 8 (lrow & 1); fragment j is fragment 0 with the
+            // 16-byte slot index xor j
+            const int r = 32 * kgrp + (lrow >> 1);
+            const uint32_t rel = (uint32_t)(r * TBN + (((4 * wq) ^ kn_key(r)) << 4) + 8 * (lrow & 1));
+#pragma unroll
+            for (int j = 0; j < NNI; ++j) {
+                const uint32_t ad = so + kAStage + (rel ^ (uint32_t)(j << 4));
+                f.b[j] = cat4(ds64tr<0>(ad), ds64tr<8 * TBN>(ad), ds64tr<16 * TBN>(ad), ds64tr<24 * TBN>(ad));
+            }
+        } else {
+            const uint32_t b0 = so + kAStage + sw(64 * wq + lrow, 2 * kgrp);
+            const uint32_t b1 = so + kAStage + sw(64 * wq + lrow, 2 * kgrp + 1);
+            f.b[0] = frag_nk<0>(b0, b1);
+            f.b[1] = frag_nk<1>(b0, b1);
+            f.b[2] = frag_nk<2>(b0, b1);
+            f.b[3] = frag_nk<3>(b0, b1);
+        }
+    };
+    // all reads of f have landed; fold the chunk's B scale into the row scales
+    auto reads_wait = [&](FragsPP& f) {
+        lgkm_wait<0>(f.b[3]);
+        pin4(f.a[0], f.a[1], f.a[2], f.a[3]);
+        pin4(f.a[4], f.a[5], f.a[6], f.a[7]);
+        asm volatile("" : "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]));
+        if (SA_MODE == SA_ROW)
+            asm volatile("" : "+v"(f.s[0]), "+v"(f.s[1]), "+v"(f.s[2]), "+v"(f.s[3]),
+                              "+v"(f.s[4]), "+v"(f.s[5]), "+v"(f.s[6]), "+v"(f.s[7]));
+        if (SB_MODE == SB_BLOCK) asm volatile("" : "+v"(f.sbk));
+        const float sbv = SB_MODE == SB_BLOCK ? f.sbk : sb_t;
+#pragma unroll
+        for (int i = 0; i < PMI; ++i) f.s[i] = (SA_MODE == SA_ROW ? f.s[i] : sa_t) * sbv;
+    };
+    // Partial last chunk: every fragment of a lane (A, B as [N][K] or, through
+    // the transposing reads, as [K][N]) holds the chunk's K bytes
+    // [32 kgrp, 32 kgrp + 32) in order, so one mask per dword clears the bytes
+    // at or past K in both operands (a code past K may be anything, NaN too).
+    auto mask_k_tail = [&](FragsPP& f) {
+        const int kgrp = lane >> 4;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+            const int keep = k_tail - (32 * kgrp + 4 * d);
+            const int mk = keep >= 4 ? -1 : (keep <= 0 ? 0 : (int)((1u << (8 * keep)) - 1u));
+#pragma unroll
+            for (int i = 0; i < PMI; ++i) f.a[i][d] &= mk;
+#pragma unroll
+            for (int j = 0; j < NNI; ++j) f.b[j][d] &= mk;
+        }
+    };
+    // the 32 MFMAs of the chunk in f; the FMAs of block u run behind the
+    // MFMA of block u+1
+    auto compute = [&](FragsPP& f) {
+        v4f prev = zero;
+#pragma unroll
+        for (int u = 0; u < PMI * NNI; ++u) {
+            const int j = u / PMI, i = u % PMI;
+            const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[j], f.a[i], zero, 0, 0, 0, 0, 0, 0);
+            if (u > 0) {
+                const int pi = (u - 1) % PMI, pj = (u - 1) / PMI;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[pi][pj][r] = __builtin_fmaf(prev[r], f.s[pi], acc[pi][pj][r]);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            prev = part;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[PMI - 1][NNI - 1][r] = __builtin_fmaf(prev[r], f.s[PMI - 1], acc[PMI - 1][NNI - 1][r]);
+#pragma unroll
+        for (int i = 0; i < PMI; ++i)
+#pragma unroll
+            for (int j = 0; j < NNI; ++j) asm volatile("" : "+v"(acc[i][j]));
+    };
+    auto bar = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // group g loads chunk g of the first tile
+    if (grp < KB) issue(grp);
+    for (;;) {
+#pragma unroll
+        for (int i = 0; i < PMI; ++i)
+#pragma unroll
+            for (int j = 0; j < NNI; ++j) acc[i][j] = zero;
+        if (KB > 0) {
+            // KB + 1 phases, each a barrier in every wave.  Phase c: chunk c's
+            // loads (issued by this group two phases ago) landed, and chunk
+            // c-1's stage, read in phase c-1, takes chunk c+2.
+            FragsPP f;
+            int q = 0;
+            if (grp == 1) {
+                bar();
+                q = 1;
+            }
+            for (int c = grp; c < KB; c += 2) {
+                wait_vm<0>();
+                bar();
+                if (c + 2 < KB) issue(c + 2);
+                read_frags(c % kStages, f);
+                reads_wait(f);
+                if (c == KB - 1 && k_tail < TBK) mask_k_tail(f);
+                bar();
+                compute(f);
+                q = c + 2;
+            }
+            if (q == KB) bar();
+        }
+        // Add the two groups' halves: group 0 finishes rows [0, 64), group 1
+        // rows [64, 128).  Each wave sends the other half to its partner (the
+        // wave of the other group with the same columns) through a 16 KB slot
+        // of the LDS ring, which no wave reads or loads into any more.
+        const int64_t cm0 = m0, cn0 = n0;
+        const bool store_tile = tile_live;
+        ti += nwg;
+        const bool more = ti < range_len;
+        const uint32_t slot_out = lds_addr(Stg) + (uint32_t)(wave * 16384 + lane * 16);
+        const uint32_t slot_in = lds_addr(Stg) + (uint32_t)(((wave + 4) & 7) * 16384 + lane * 16);
+        auto finish = [&](auto half) {
+            constexpr int h = decltype(half)::value;   // rows kept: [64h, 64h+64)
+            constexpr int o = (1 - h) * 4;            // first block sent
+#pragma unroll
+            for (int q2 = 0; q2 < 16; ++q2) {
+                const v4f v = acc[o + q2 / 4][q2 % 4];
+                switch (q2) {
+#define FP8Q_W(Q) case Q: ds_write128<Q * 1024>(slot_out, v); break;
+                    FP8Q_W(0) FP8Q_W(1) FP8Q_W(2) FP8Q_W(3) FP8Q_W(4) FP8Q_W(5) FP8Q_W(6) FP8Q_W(7)
+                    FP8Q_W(8) FP8Q_W(9) FP8Q_W(10) FP8Q_W(11) FP8Q_W(12) FP8Q_W(13) FP8Q_W(14) FP8Q_W(15)
+#undef FP8Q_W
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            v4f in[16];
+#pragma unroll
+            for (int q2 = 0; q2 < 16; ++q2) {
+                switch (q2) {
+#define FP8Q_R(Q) case Q: in[Q] = (v4f)ds128<Q * 1024>(slot_in); break;
+                    FP8Q_R(0) FP8Q_R(1) FP8Q_R(2) FP8Q_R(3) FP8Q_R(4) FP8Q_R(5) FP8Q_R(6) FP8Q_R(7)
+                    FP8Q_R(8) FP8Q_R(9) FP8Q_R(10) FP8Q_R(11) FP8Q_R(12) FP8Q_R(13) FP8Q_R(14) FP8Q_R(15)
+#undef FP8Q_R
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            const int lrow = lane & 15, kgrp = lane >> 4;
+#pragma unroll
+            for (int q2 = 0; q2 < 16; ++q2) {
+                asm volatile("" : "+v"(in[q2]));
+                acc[h * 4 + q2 / 4][q2 % 4] += in[q2];
+            }
+            // lane l holds C[m][n .. n+3] of each kept block
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t m = cm0 + 64 * h + 16 * i + lrow;
+                if (m >= M || !store_tile) continue;
+#pragma unroll
+                for (int j = 0; j < NNI; ++j) {
+                    const int64_t n = cn0 + 64 * wq + 16 * j + 4 * kgrp;
+                    const v4f v = acc[h * 4 + i][j];
+                    if (n + 3 < N) {
+                        if (OUT_BF16) {
+                            const uint32_t lo = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+                            const uint32_t hi = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+                            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.c) + m * p.ldc + n) = make_uint2(lo, hi);
+                        } else {
+                            *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.c) + m * p.ldc + n) = v;
+                        }
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            if (n + r < N) {
+                                if (OUT_BF16)
+                                    reinterpret_cast<uint16_t*>(p.c)[m * p.ldc + n + r] = (uint16_t)bf16_rne(v[r]);
+                                else
+                                    reinterpret_cast<float*>(p.c)[m * p.ldc + n + r] = v[r];
+                            }
+                        }
+                    }
+                }
+            }
+        };
+        if (grp == 0) finish(std::integral_constant<int, 0>{});
+        else finish(std::integral_constant<int, 1>{});
+        if (!more) break;
+        tile_origin(ti, m0, n0);
+        set_group(m0);
+        rsc = scale_rsrc();
+        // every wave is done with the exchange slots before they are loaded into
+        __builtin_amdgcn_s_barrier();
+        if (grp < KB) issue(grp);
+    }
+    wait_vm<0>();
+}
+
+template <int SA_MODE, int SB_MODE, bool B_KN, bool GROUPED = false>
+static void launch_pp(const GemmArgs& g, bool bf, hipStream_t st)
+{
+    GemmArgs a = g;
+    a.tiles_m = (int)((g.M + TBM - 1) / TBM);
+    a.tiles_n = (int)((g.N + TBN - 1) / TBN);
+    const int tiles = a.tiles_m * a.tiles_n;
+    dim3 grid((uint32_t)(tiles < g.num_cus ? tiles : g.num_cus));
+    if (bf)
+        hipLaunchKernelGGL((gemm_pp_kernel<SA_MODE, SB_MODE, B_KN, true, GROUPED>), grid, dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((gemm_pp_kernel<SA_MODE, SB_MODE, B_KN, false, GROUPED>), grid, dim3(kThreads), 0, st, a);
+}
+
 template <int SA_MODE, int SB_MODE, bool B_KN, bool GROUPED = false>
 static void launch2(const GemmArgs& g, bool bf, hipStream_t st)
 {
@@ -669,7 +1082,7 @@ bool launch_grouped_gemm_nk(const GemmArgs& g, bool out_bf16, hipStream_t st)
     if (g.G > kMaxLdsGroups || g.M * g.lda >= lim || (g.N + TBK) * g.ldb >= lim ||
         g.M * g.ldsa * 4 >= lim || g.sb_group_stride * 4 >= lim || (int64_t)g.KB * TBK >= lim)
         return false;
-    launch2<SA_ROW, SB_BLOCK, false, true>(g, out_bf16, st);
+    launch_pp<SA_ROW, SB_BLOCK, false, true>(g, out_bf16, st);
     return true;
 }
 
@@ -684,22 +1097,22 @@ bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, bool
     if (b_kn) {
         if (sb_mode == SB_ROW) return false;
         if (sa_mode == SA_ROW) {
-            if (sb_mode == SB_BLOCK) launch2<SA_ROW, SB_BLOCK, true>(g, out_bf16, st);
-            else launch2<SA_ROW, SB_TENSOR, true>(g, out_bf16, st);
+            if (sb_mode == SB_BLOCK) launch_pp<SA_ROW, SB_BLOCK, true>(g, out_bf16, st);
+            else launch_pp<SA_ROW, SB_TENSOR, true>(g, out_bf16, st);
         } else {
-            if (sb_mode == SB_BLOCK) launch2<SA_TENSOR, SB_BLOCK, true>(g, out_bf16, st);
-            else launch2<SA_TENSOR, SB_TENSOR, true>(g, out_bf16, st);
+            if (sb_mode == SB_BLOCK) launch_pp<SA_TENSOR, SB_BLOCK, true>(g, out_bf16, st);
+            else launch_pp<SA_TENSOR, SB_TENSOR, true>(g, out_bf16, st);
         }
         return true;
     }
     if (sa_mode == SA_ROW) {
-        if (sb_mode == SB_BLOCK) launch2<SA_ROW, SB_BLOCK, false>(g, out_bf16, st);
+        if (sb_mode == SB_BLOCK) launch_pp<SA_ROW, SB_BLOCK, false>(g, out_bf16, st);
         else if (sb_mode == SB_ROW) launch2<SA_ROW, SB_ROW, false>(g, out_bf16, st);
-        else launch2<SA_ROW, SB_TENSOR, false>(g, out_bf16, st);
+        else launch_pp<SA_ROW, SB_TENSOR, false>(g, out_bf16, st);
     } else {
-        if (sb_mode == SB_BLOCK) launch2<SA_TENSOR, SB_BLOCK, false>(g, out_bf16, st);
+        if (sb_mode == SB_BLOCK) launch_pp<SA_TENSOR, SB_BLOCK, false>(g, out_bf16, st);
         else if (sb_mode == SB_ROW) launch2<SA_TENSOR, SB_ROW, false>(g, out_bf16, st);
-        else launch2<SA_TENSOR, SB_TENSOR, false>(g, out_bf16, st);
+        else launch_pp<SA_TENSOR, SB_TENSOR, false>(g, out_bf16, st);
     }
     return true;
 }
