@@ -93,6 +93,12 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, float* lds_words
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)lds_words, 4, voff, soff, 0, 0);
 }
 
+// the same with the LDS destination given as a (wave-uniform) LDS address
+__device__ __forceinline__ void dma16_at(__amdgpu_buffer_rsrc_t rs, uint32_t lds, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(uintptr_t)lds, 16, voff, soff, 0, 0);
+}
+
 // waits until at most N LDS (or scalar) reads are pending; x is an operand
 // so that its users stay below the wait
 template <int N>
@@ -661,6 +667,9 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
 // chunk q-1 from registers, so each SIMD has one wave on the matrix core
 // while its partner waits for memory.  A group loads exactly the chunks it
 // reads, two phases ahead, so waiting for a chunk is vmcnt(0) in its waves.
+// With [N][K] B each wave loads the B rows of its own columns, so it reads
+// those right after its compute phase and only the shared A rows after the
+// barrier.
 // At the end of a tile each group holds the sum over its chunks; the halves
 // are added through LDS (the ring is idle by then), each group finishing and
 // storing 64 of the 128 rows.
@@ -685,14 +694,29 @@ __device__ __forceinline__ v8i frag_nk(uint32_t r0, uint32_t r1)
     return cat(ds128<I * 16 * TBK>(r0), ds128<I * 16 * TBK>(r1));
 }
 
+// the 4 column scales of a lane in 16-column block j (row-scaled B)
+__device__ __forceinline__ v4f col_scales(uint32_t a, int j)
+{
+    switch (j) {
+    case 0: return (v4f)ds128<0>(a);
+    case 1: return (v4f)ds128<64>(a);
+    case 2: return (v4f)ds128<128>(a);
+    default: return (v4f)ds128<192>(a);
+    }
+}
+
 template <int SA_MODE, int SB_MODE, bool B_KN, bool OUT_BF16, bool GROUPED>
 __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs p)
 {
-    static_assert(SB_MODE != SB_ROW, "row-scaled B needs per-column scales in registers");
+    constexpr int kSbStages = SB_MODE == SB_ROW ? 4 : kStages;
+    static_assert(!(B_KN && SB_MODE == SB_ROW), "row-scaled B is [N][K] only");
     __shared__ int32_t goff[GROUPED ? kMaxLdsGroups + 1 : 1];
     __shared__ __attribute__((aligned(16))) uint8_t Stg[kStages][kStageBytes];
     __shared__ __attribute__((aligned(16))) float SAs[kStages][TBM];
-    __shared__ __attribute__((aligned(16))) float SBs[kStages][64];
+    // B scales of a chunk: its two 128-column blocks (block-scaled B), or its
+    // 256 column scales (row-scaled B), which the computing group reads one
+    // phase after the chunk's operands, hence a ring one deeper
+    __shared__ __attribute__((aligned(16))) float SBs[kSbStages][SB_MODE == SB_ROW ? TBN : 64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -752,18 +776,22 @@ __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs p)
     set_group(m0);
 
     // scale loads: waves 0-1 of a group the SA of the tile's 128 rows
-    // (row-scaled A), wave 2 the block scales of its two 128-column blocks
+    // (row-scaled A); wave 2 the block scales of the tile's two 128-column
+    // blocks (block-scaled B), or every wave the scales of its 64 columns
+    // (row-scaled B)
     const int64_t nblocks = (N + 127) / 128;
-    const int sc_kind = (wq < 2 && SA_MODE == SA_ROW) ? 0 : (wq == 2 && SB_MODE == SB_BLOCK) ? 2 : 3;
-    auto scale_rsrc = [&]() {
-        if (sc_kind == 0) return rsrc(p.sa, ((M - 1) * p.ldsa + KB) * 4);
-        if (sc_kind == 2) {
+    const bool load_sa = SA_MODE == SA_ROW && wq < 2;
+    const bool load_sb = SB_MODE == SB_ROW || (SB_MODE == SB_BLOCK && wq == 2);
+    const __amdgpu_buffer_rsrc_t rsa = rsrc(p.sa, SA_MODE == SA_ROW ? ((M - 1) * p.ldsa + KB) * 4 : 4);
+    auto sb_rsrc = [&]() {
+        if (SB_MODE == SB_ROW) return rsrc(p.sb, ((N - 1) * p.ldsb + KB) * 4);
+        if (SB_MODE == SB_BLOCK) {
             if (B_KN) return rsrc(p.sb, ((int64_t)(KB - 1) * p.ldsb + nblocks) * 4);
             return rsrc(p.sb + (GROUPED ? (int64_t)grp_e * p.sb_group_stride : 0), ((nblocks - 1) * p.ldsb + KB) * 4);
         }
-        return rsrc(p.sa, 4);
+        return rsrc(p.sb, 4);
     };
-    __amdgpu_buffer_rsrc_t rsc = scale_rsrc();
+    __amdgpu_buffer_rsrc_t rsb = sb_rsrc();
 
     // Loads of chunk kb by this wave: A rows [32 wq, 32 wq + 32) (4 DMAs of
     // 8 rows), B rows [64 wq, 64 wq + 64) of [N][K] B (8 DMAs of 8 rows) or K
@@ -777,7 +805,7 @@ __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs p)
     // scale rows past M and a missing second column block read as zero too.
     // (rebuilt from the lane id for each chunk, so that they do not occupy
     // registers through the compute phase)
-    struct DmaOffs { uint32_t va[2], vb[2], vsc; };
+    struct DmaOffs { uint32_t va[2], vb[2], vsa, vsb; };
     auto dma_offsets = [&]() {
         DmaOffs o;
         int l = lane;
@@ -794,28 +822,32 @@ __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs p)
                 o.vb[h] = (uint32_t)((n0 + 64 * wq + (l >> 3)) * p.ldb) + 16u * (uint32_t)((l & 7) ^ (l >> 3) ^ h);
             }
         }
-        o.vsc = sc_kind == 0 ? (uint32_t)((m0 + 64 * wq + l) * p.ldsa * 4)
-              : sc_kind == 2 ? (uint32_t)((n0 / 128 + (l < 1 ? l : 1)) * (B_KN ? 4 : p.ldsb * 4)) : 0u;
+        o.vsa = (uint32_t)((m0 + 64 * wq + l) * p.ldsa * 4);
+        o.vsb = SB_MODE == SB_ROW ? (uint32_t)((n0 + 64 * wq + l) * p.ldsb * 4)
+                                  : (uint32_t)((n0 / 128 + (l < 1 ? l : 1)) * (B_KN ? 4 : p.ldsb * 4));
         return o;
     };
     auto issue = [&](int kb) {
         const DmaOffs o = dma_offsets();
         const int st = kb % kStages;
-        const uint32_t k0 = (uint32_t)kb * TBK;
+        // per-chunk scalars, opaque so that the per-DMA sums below are formed
+        // here rather than hoisted out of the loop into spilled registers
+        uint32_t a_lds = lds_addr(&Stg[st][0]) + (uint32_t)(32 * wq * TBK);
+        uint32_t b_lds = lds_addr(&Stg[st][kAStage]) + (uint32_t)(B_KN ? 32 * wq * TBN : 64 * wq * TBK);
+        uint32_t a_soff = (uint32_t)kb * TBK, a_step = 8u * (uint32_t)p.lda;
+        uint32_t b_soff = B_KN ? (uint32_t)kb * TBK * (uint32_t)p.ldb : (uint32_t)kb * TBK;
+        uint32_t b_step = (B_KN ? 4u : 8u) * (uint32_t)p.ldb;
+        asm volatile("" : "+s"(a_lds), "+s"(b_lds), "+s"(a_soff), "+s"(a_step), "+s"(b_soff), "+s"(b_step));
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            dma16(ra, &Stg[st][(32 * wq + 8 * t) * TBK], o.va[t & 1], k0 + (uint32_t)(8 * t * p.lda));
+        for (int t = 0; t < 4; ++t) dma16_at(ra, a_lds + (uint32_t)(8 * t * TBK), o.va[t & 1], a_soff + t * a_step);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            if (B_KN)
-                dma16(rb, &Stg[st][kAStage + (32 * wq + 4 * t) * TBN], o.vb[t & 1], (k0 + 4u * t) * (uint32_t)p.ldb);
-            else
-                dma16(rb, &Stg[st][kAStage + (64 * wq + 8 * t) * TBK], o.vb[t & 1], k0 + (uint32_t)(8 * t * p.ldb));
-        }
-        if (sc_kind == 0)
-            dma4(rsc, &SAs[st][64 * wq], o.vsc, (uint32_t)kb * 4);
-        else if (sc_kind == 2)
-            dma4(rsc, &SBs[st][0], o.vsc, B_KN ? (uint32_t)(kb * p.ldsb * 4) : (uint32_t)kb * 4);
+        for (int t = 0; t < 8; ++t)
+            dma16_at(rb, b_lds + (uint32_t)(B_KN ? 4 * t * TBN : 8 * t * TBK), o.vb[t & 1], b_soff + t * b_step);
+        if (load_sa) dma4(rsa, &SAs[st][64 * wq], o.vsa, (uint32_t)kb * 4);
+        if (SB_MODE == SB_ROW)
+            dma4(rsb, &SBs[kb % kSbStages][64 * wq], o.vsb, (uint32_t)kb * 4);
+        else if (load_sb)
+            dma4(rsb, &SBs[st][0], o.vsb, B_KN ? (uint32_t)(kb * p.ldsb * 4) : (uint32_t)kb * 4);
     };
 
     v4f acc[PMI][NNI];
@@ -824,7 +856,40 @@ __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs p)
     const float sb_t = (SB_MODE == SB_TENSOR && KB > 0) ? p.sb[0] : 0.0f;
 
     // the LDS reads of one chunk (addresses rebuilt from the lane id)
-    auto read_frags = [&](int st, FragsPP& f) {
+    // B fragments of the chunk in stage st: the wave's own 64 columns.  For
+    // [N][K] B those are exactly the B rows this wave loaded, so they may be
+    // read as soon as its own loads have landed; [K][N] B rows are loaded
+    // across all columns by every wave of the group, so those are read after
+    // the phase barrier like A.
+    constexpr bool kEarlyB = !B_KN;
+    auto read_b = [&](int st, FragsPP& f) {
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        const int lrow = l & 15, kgrp = l >> 4;
+        const uint32_t so = lds_addr(Stg) + (uint32_t)st * kStageBytes;
+        if (B_KN) {
+            // lane (kgrp, lrow) addresses K row 32 kgrp + lrow / 2 at column
+            // 64 wq + 16 j + 8 (lrow & 1); fragment j is fragment 0 with the
+            // 16-byte slot index xor j
+            const int r = 32 * kgrp + (lrow >> 1);
+            const uint32_t rel = (uint32_t)(r * TBN + (((4 * wq) ^ kn_key(r)) << 4) + 8 * (lrow & 1));
+#pragma unroll
+            for (int j = 0; j < NNI; ++j) {
+                const uint32_t ad = so + kAStage + (rel ^ (uint32_t)(j << 4));
+                f.b[j] = cat4(ds64tr<0>(ad), ds64tr<8 * TBN>(ad), ds64tr<16 * TBN>(ad), ds64tr<24 * TBN>(ad));
+            }
+        } else {
+            const uint32_t b0 = so + kAStage + sw(64 * wq + lrow, 2 * kgrp);
+            const uint32_t b1 = so + kAStage + sw(64 * wq + lrow, 2 * kgrp + 1);
+            f.b[0] = frag_nk<0>(b0, b1);
+            f.b[1] = frag_nk<1>(b0, b1);
+            f.b[2] = frag_nk<2>(b0, b1);
+            f.b[3] = frag_nk<3>(b0, b1);
+        }
+    };
+    // A fragments and scales of the chunk in stage st (A rows are loaded by
+    // all four waves of the group: read after the phase barrier)
+    auto read_a = [&](int st, FragsPP& f) {
         int l = lane;
         asm volatile("" : "+v"(l));
         const int lrow = l & 15, kgrp = l >> 4;
@@ -850,39 +915,21 @@ __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs p)
         f.a[5] = frag_nk<5>(a0, a1);
         f.a[6] = frag_nk<6>(a0, a1);
         f.a[7] = frag_nk<7>(a0, a1);
-        if (B_KN) {
-            // lane (kgrp, lrow) addresses K row 32 kgrp + lrow / 2 at column
-            // 64 wq + 16 j + 8 (lrow & 1); fragment j is fragment 0 with the
-            // 16-byte slot index xor j
-            const int r = 32 * kgrp + (lrow >> 1);
-            const uint32_t rel = (uint32_t)(r * TBN + (((4 * wq) ^ kn_key(r)) << 4) + 8 * (lrow & 1));
-#pragma unroll
-            for (int j = 0; j < NNI; ++j) {
-                const uint32_t ad = so + kAStage + (rel ^ (uint32_t)(j << 4));
-                f.b[j] = cat4(ds64tr<0>(ad), ds64tr<8 * TBN>(ad), ds64tr<16 * TBN>(ad), ds64tr<24 * TBN>(ad));
-            }
-        } else {
-            const uint32_t b0 = so + kAStage + sw(64 * wq + lrow, 2 * kgrp);
-            const uint32_t b1 = so + kAStage + sw(64 * wq + lrow, 2 * kgrp + 1);
-            f.b[0] = frag_nk<0>(b0, b1);
-            f.b[1] = frag_nk<1>(b0, b1);
-            f.b[2] = frag_nk<2>(b0, b1);
-            f.b[3] = frag_nk<3>(b0, b1);
-        }
     };
     // all reads of f have landed; fold the chunk's B scale into the row scales
     auto reads_wait = [&](FragsPP& f) {
-        lgkm_wait<0>(f.b[3]);
+        lgkm_wait<0>(f.a[7]);
         pin4(f.a[0], f.a[1], f.a[2], f.a[3]);
-        pin4(f.a[4], f.a[5], f.a[6], f.a[7]);
-        asm volatile("" : "+v"(f.b[0]), "+v"(f.b[1]), "+v"(f.b[2]));
+        asm volatile("" : "+v"(f.a[4]), "+v"(f.a[5]), "+v"(f.a[6]));
+        pin4(f.b[0], f.b[1], f.b[2], f.b[3]);
         if (SA_MODE == SA_ROW)
             asm volatile("" : "+v"(f.s[0]), "+v"(f.s[1]), "+v"(f.s[2]), "+v"(f.s[3]),
                               "+v"(f.s[4]), "+v"(f.s[5]), "+v"(f.s[6]), "+v"(f.s[7]));
         if (SB_MODE == SB_BLOCK) asm volatile("" : "+v"(f.sbk));
-        const float sbv = SB_MODE == SB_BLOCK ? f.sbk : sb_t;
+        const float sbv = SB_MODE == SB_BLOCK ? f.sbk : SB_MODE == SB_TENSOR ? sb_t : 1.0f;
 #pragma unroll
-        for (int i = 0; i < PMI; ++i) f.s[i] = (SA_MODE == SA_ROW ? f.s[i] : sa_t) * sbv;
+        for (int i = 0; i < PMI; ++i)
+            f.s[i] = SB_MODE == SB_ROW ? (SA_MODE == SA_ROW ? f.s[i] : sa_t) : (SA_MODE == SA_ROW ? f.s[i] : sa_t) * sbv;
     };
     // Partial last chunk: every fragment of a lane (A, B as [N][K] or, through
     // the transposing reads, as [K][N]) holds the chunk's K bytes
@@ -900,26 +947,42 @@ __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs p)
             for (int j = 0; j < NNI; ++j) f.b[j][d] &= mk;
         }
     };
-    // the 32 MFMAs of the chunk in f; the FMAs of block u run behind the
-    // MFMA of block u+1
-    auto compute = [&](FragsPP& f) {
+    // the 32 MFMAs of chunk c in f; the FMAs of block u run behind the MFMA
+    // of block u+1.  Row-scaled B: the lane's 4 column scales of block j are
+    // read from LDS while the MFMAs of block j-1 run, and each FMA takes
+    // the product of its row and column scale.
+    auto compute = [&](FragsPP& f, int c) {
+        uint32_t sbp = 0;
+        v4f sc[NNI];
+        if (SB_MODE == SB_ROW) {
+            int l = lane;
+            asm volatile("" : "+v"(l));
+            sbp = lds_addr(SBs) + (uint32_t)((c % kSbStages) * TBN + 64 * wq + 4 * (l >> 4)) * 4;
+            sc[0] = col_scales(sbp, 0);
+        }
+        auto scale_fma = [&](const v4f& pv, int pi, int pj) {
+            if (SB_MODE == SB_ROW) {
+                if (pi == 0) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(sc[pj]));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[pi][pj][r] = __builtin_fmaf(pv[r], f.s[pi] * sc[pj][r], acc[pi][pj][r]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[pi][pj][r] = __builtin_fmaf(pv[r], f.s[pi], acc[pi][pj][r]);
+            }
+        };
         v4f prev = zero;
 #pragma unroll
         for (int u = 0; u < PMI * NNI; ++u) {
             const int j = u / PMI, i = u % PMI;
             const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[j], f.a[i], zero, 0, 0, 0, 0, 0, 0);
-            if (u > 0) {
-                const int pi = (u - 1) % PMI, pj = (u - 1) / PMI;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[pi][pj][r] = __builtin_fmaf(prev[r], f.s[pi], acc[pi][pj][r]);
-            }
+            if (SB_MODE == SB_ROW && i == 1 && j + 1 < NNI) sc[j + 1] = col_scales(sbp, j + 1);
+            if (u > 0) scale_fma(prev, (u - 1) % PMI, (u - 1) / PMI);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, SB_MODE == SB_ROW ? 8 : 4, 0);
             __builtin_amdgcn_sched_barrier(0);
             prev = part;
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[PMI - 1][NNI - 1][r] = __builtin_fmaf(prev[r], f.s[PMI - 1], acc[PMI - 1][NNI - 1][r]);
+        scale_fma(prev, PMI - 1, NNI - 1);
 #pragma unroll
         for (int i = 0; i < PMI; ++i)
 #pragma unroll
@@ -942,21 +1005,33 @@ __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs p)
             // KB + 1 phases, each a barrier in every wave.  Phase c: chunk c's
             // loads (issued by this group two phases ago) landed, and chunk
             // c-1's stage, read in phase c-1, takes chunk c+2.
+            // A group reads the B fragments of its next chunk right after its
+            // compute phase (its own loads, two phases old by then), so its
+            // read phase holds only the A fragments and scales.
             FragsPP f;
             int q = 0;
             if (grp == 1) {
                 bar();
                 q = 1;
             }
-            for (int c = grp; c < KB; c += 2) {
+            if (kEarlyB && grp < KB) {
                 wait_vm<0>();
+                read_b(grp % kStages, f);
+            }
+            for (int c = grp; c < KB; c += 2) {
+                if (!kEarlyB) wait_vm<0>();
                 bar();
                 if (c + 2 < KB) issue(c + 2);
-                read_frags(c % kStages, f);
+                if (!kEarlyB) read_b(c % kStages, f);
+                read_a(c % kStages, f);
                 reads_wait(f);
                 if (c == KB - 1 && k_tail < TBK) mask_k_tail(f);
                 bar();
-                compute(f);
+                compute(f, c);
+                if (kEarlyB && c + 2 < KB) {
+                    wait_vm<0>();
+                    read_b((c + 2) % kStages, f);
+                }
                 q = c + 2;
             }
             if (q == KB) bar();
@@ -1039,7 +1114,7 @@ __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs p)
         if (!more) break;
         tile_origin(ti, m0, n0);
         set_group(m0);
-        rsc = scale_rsrc();
+        rsb = sb_rsrc();
         // every wave is done with the exchange slots before they are loaded into
         __builtin_amdgcn_s_barrier();
         if (grp < KB) issue(grp);
@@ -1107,11 +1182,11 @@ bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, bool
     }
     if (sa_mode == SA_ROW) {
         if (sb_mode == SB_BLOCK) launch_pp<SA_ROW, SB_BLOCK, false>(g, out_bf16, st);
-        else if (sb_mode == SB_ROW) launch2<SA_ROW, SB_ROW, false>(g, out_bf16, st);
+        else if (sb_mode == SB_ROW) launch_pp<SA_ROW, SB_ROW, false>(g, out_bf16, st);
         else launch_pp<SA_ROW, SB_TENSOR, false>(g, out_bf16, st);
     } else {
         if (sb_mode == SB_BLOCK) launch_pp<SA_TENSOR, SB_BLOCK, false>(g, out_bf16, st);
-        else if (sb_mode == SB_ROW) launch2<SA_TENSOR, SB_ROW, false>(g, out_bf16, st);
+        else if (sb_mode == SB_ROW) launch_pp<SA_TENSOR, SB_ROW, false>(g, out_bf16, st);
         else launch_pp<SA_TENSOR, SB_TENSOR, false>(g, out_bf16, st);
     }
     return true;
