@@ -1,7 +1,8 @@
 // Block-scaled FP8 GEMM on gfx950: the forward y = x W^T (B = W stored
 // [N][K]), dgrad dx = dy W (B = W read as stored, [K][N], no transposed copy:
 // Ling 2.0 FP8 blog, "FP8 on-demand transpose weight"), the weight gradient
-// dW = dy^T x on transposed re-quantized operands, and per-tensor scaling.
+// dW = dy^T x on transposed re-quantized operands (row-scaled B), per-tensor
+// scaling, and the grouped (MoE) forward.
 //
 //   C[m][n] = sum_kb SA(m,kb) * SB(n,kb) * sum_{k in chunk kb} dec(A[m][k]) * dec(B[n][k])
 //
@@ -10,16 +11,19 @@
 // "fine-grained quantization"; 128x128 weight blocks: "FP8-RL" article, 一.)
 //
 // gfx950 mapping:
-//  * workgroup tile 128 (M) x 256 (N), K chunk 128 = one scale chunk; 8 waves
-//    of 64 x 64; one v_mfma_f32_16x16x128_f8f6f4 per 16x16 block per chunk
-//    gives that chunk's fp32 partial, which one VALU FMA scales into the fp32
-//    accumulator; MFMAs and FMAs are interleaved so the matrix core keeps
-//    working while earlier partials are scaled;
+//  * persistent workgroups (one per CU) with a tile of 128 (M) x 256 (N);
+//    K chunk 128 = one scale chunk = one v_mfma_f32_16x16x128_f8f6f4 per
+//    16x16 block, which gives the chunk's fp32 partial; VALU FMAs scale it
+//    into the fp32 accumulator, each behind the next block's MFMA;
+//  * 8 waves, each owning all 128 rows of 64 columns (8 A and 4 B fragments,
+//    32 MFMAs per chunk); the two groups of four waves (one wave of each per
+//    SIMD) take alternate K chunks in ping-pong phases, so one wave of every
+//    SIMD runs MFMAs from registers while its partner loads and reads the
+//    next chunk; the two partial tiles are added through LDS at the end;
 //  * operands and per-chunk scales go global -> LDS with buffer loads that
 //    write LDS directly (no VGPR staging), through a ring of 3 LDS stages of
-//    48 KB: chunk kb+2 is in flight while chunk kb computes.  Every wave
-//    issues the same number of loads per chunk, so waiting for a chunk is an
-//    exact vmcnt.  Buffer resources bound every load to its operand;
+//    48 KB, two chunks ahead.  Buffer resources bound every load to its
+//    operand;
 //  * 16-byte LDS slots are XOR-swizzled per row so fragment reads are free
 //    of bank conflicts; a [K][N] operand is staged as stored (K rows of 256
 //    bytes) and read with ds_read_b64_tr_b8, which returns each lane 8
@@ -41,17 +45,14 @@ constexpr int TBM = 128;
 constexpr int TBN = 256;
 constexpr int TBK = 128;
 constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
-constexpr int WTM = 64;              // wave tile
-constexpr int WTN = 64;
-constexpr int NMI = WTM / 16;        // 16x16 blocks per wave
-constexpr int NNI = WTN / 16;
+constexpr int WTN = 64;              // columns per wave (all TBM rows)
+constexpr int PMI = TBM / 16;        // 16-row blocks per wave
+constexpr int NNI = WTN / 16;        // 16-column blocks per wave
 constexpr int kStages = 3;
 constexpr int kGroupM = 16;
 constexpr int kAStage = TBM * TBK;   // bytes
 constexpr int kBStage = TBN * TBK;
-// tile DMAs per wave per chunk (1 KB each) plus one scale DMA
-constexpr int kLoadsPerChunk = (TBM + TBN) * TBK / 1024 / kWaves + 1;
+constexpr int kStageBytes = kAStage + kBStage; // A at 0, B at kAStage
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -177,506 +178,27 @@ __device__ __forceinline__ v8i cat(v4i lo, v4i hi)
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Zero the bytes at or beyond `valid` (1..127) of every row of an A and a B
-// stage (the last, partial K chunk).  A [K][N] B stage has K rows instead:
-// rows at or beyond `valid` are cleared whole.
-template <bool B_KN>
-__device__ __forceinline__ void zero_k_tail(uint8_t* As, uint8_t* Bs, int valid, int tid)
-{
-    if (B_KN) {
-        for (int i = valid * (TBN / 16) + tid; i < TBK * (TBN / 16); i += kThreads)
-            reinterpret_cast<uint4*>(Bs)[i] = make_uint4(0, 0, 0, 0);
-    }
-    for (int row = tid; row < (B_KN ? TBM : TBM + TBN); row += kThreads) {
-        uint8_t* t = row < TBM ? As : Bs;
-        const int r = row < TBM ? row : row - TBM;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int v = valid - 16 * c;
-            if (v >= 16) continue;
-            uint4* p = reinterpret_cast<uint4*>(t + sw(r, c));
-            *p = v <= 0 ? make_uint4(0, 0, 0, 0) : mask_bytes(*p, v);
-        }
-    }
-}
-
 }  // namespace
-
-// one chunk's operand fragments and scales in registers
-struct Frags {
-    v8i a[NMI], b[NNI];
-    float sa[NMI];   // SA of the lane's row in block i (row-scaled A)
-    v4f sbc[NNI];    // SB of the lane's 4 columns in block j (row-scaled B)
-    float sbk;       // SB of the wave's 128-column block (block-scaled B)
-};
 
 // groups whose offsets fit in LDS (grouped launches with more fall back)
 constexpr int kMaxLdsGroups = 1024;
 
-template <int SA_MODE, int SB_MODE, bool B_KN, bool OUT_BF16, bool GROUPED>
-__global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
-{
-    // grouped (MoE) launches: the device group offsets, copied once
-    __shared__ int32_t goff[GROUPED ? kMaxLdsGroups + 1 : 1];
-    __shared__ __attribute__((aligned(16))) uint8_t As[kStages][kAStage];
-    __shared__ __attribute__((aligned(16))) uint8_t Bs[kStages][kBStage];
-    __shared__ __attribute__((aligned(16))) float SAs[kStages][TBM];
-    __shared__ __attribute__((aligned(16))) float SBs[kStages][TBN];
-    __shared__ __attribute__((aligned(16))) float Sdummy[64];
-    // destination of the loads issued for chunks past the end (kept so that
-    // every chunk issues the same number of loads)
-    __shared__ __attribute__((aligned(16))) uint8_t Ddummy[1024];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-    // Persistent workgroups.  Workgroups are dealt to the 8 XCDs
-    // round-robin; XCD x owns a contiguous range of tile ids, walked by its
-    // workgroups in lockstep (tile id = start + local + i * count), in
-    // groups of kGroupM M-tiles so that concurrently running tiles share A
-    // and B panels in that XCD's L2.
-    const int T = p.tiles_m * p.tiles_n;
-    const int xcd = blockIdx.x & 7;
-    const int local = blockIdx.x >> 3;
-    const int G = gridDim.x;
-    const int nwg = (G >> 3) + (xcd < (G & 7) ? 1 : 0);     // workgroups on this XCD
-    const int range_start = xcd * (T >> 3) + min(xcd, T & 7);
-    const int range_len = (T >> 3) + (xcd < (T & 7) ? 1 : 0);
-    const int span = kGroupM * p.tiles_n;
-    auto tile_origin = [&](int i, int64_t& tm0, int64_t& tn0) {
-        const int pid = range_start + i;
-        const int group = pid / span;
-        const int first_m = group * kGroupM;
-        const int gsz = min(p.tiles_m - first_m, kGroupM);
-        const int idx = pid - group * span;
-        tm0 = (int64_t)(first_m + idx % gsz) * TBM;
-        tn0 = (int64_t)(idx / gsz) * TBN;
-    };
-    int ti = local;                // index into this XCD's range
-    if (ti >= range_len) return;
-    if (GROUPED) {
-        for (int i = tid; i <= p.G; i += kThreads) goff[i] = p.offsets[i];
-        __syncthreads();
-    }
-    int64_t m0, n0;
-    tile_origin(ti, m0, n0);
-
-    const int64_t M = p.M, N = p.N, K = p.K;
-    const int KB = p.KB;
-    const int k_tail = (int)(K - (int64_t)(KB - 1) * TBK);   // bytes in the last chunk (1..128)
-
-    // ---- load plan: wave w fills A rows [16w, 16w+16) (2 DMAs) and B rows
-    // [32w, 32w+32) (4 DMAs) of each stage, plus one 64-lane scale DMA:
-    // waves 0-1 the A-row scales, waves 2-5 the B-column scales (row-scaled
-    // B), the rest a dummy copy so every wave issues the same count.
-    const int64_t ext_a = (M - 1) * p.lda + ((K + 15) & ~(int64_t)15);
-    const int64_t ext_b = B_KN ? (K - 1) * p.ldb + ((N + 15) & ~(int64_t)15)
-                               : (N - 1) * p.ldb + ((K + 15) & ~(int64_t)15);
-    const __amdgpu_buffer_rsrc_t ra = rsrc(p.a, ext_a);
-    __amdgpu_buffer_rsrc_t rb = rsrc(p.b, ext_b);
-    // grouped: the tile's group e (off[e] <= m0 < off[e+1]) selects expert
-    // e's weight and block scales; tiles at or past off[G] are computed
-    // from group G-1 but not stored
-    int grp_e = 0;
-    bool tile_live = true;
-    auto set_group = [&](int64_t tm0) {
-        if (!GROUPED) return;
-        int lo = 0, hi = p.G - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if ((int64_t)goff[mid] <= tm0) lo = mid; else hi = mid - 1;
-        }
-        grp_e = lo;
-        tile_live = tm0 < (int64_t)goff[p.G];
-        rb = rsrc(p.b + (int64_t)grp_e * p.b_group_stride, ext_b);
-    };
-    set_group(m0);
-    uint32_t offa[2], offb[4];
-    // per-lane source offsets of the tile at (tm0, tn0), without the chunk's k0
-    auto set_tile_offsets = [&](int64_t tm0, int64_t tn0) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) offa[t] = dma_src_off(16 * wave + 8 * t, lane, tm0, M, p.lda);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            if (B_KN) {
-                // K rows 16w + 4t + l/16 of the chunk, 16-byte slot l % 16;
-                // rows past K lie outside the buffer resource and read as zero
-                const int r = 16 * wave + 4 * t + (lane >> 4);
-                const int c = (lane & 15) ^ kn_key(r);
-                offb[t] = (uint32_t)(r * p.ldb + tn0 + 16 * c);
-            } else {
-                offb[t] = dma_src_off(32 * wave + 8 * t, lane, tn0, N, p.ldb);
-            }
-        }
-    };
-    set_tile_offsets(m0, n0);
-
-    // scale DMA: source words sc[row * ld + kb].  Waves 0-1: SA of the
-    // tile's 128 rows (row-scaled A).  Wave 2-5: SB of the tile's 256
-    // columns (row-scaled B); with 128x128-block B scales wave 2 instead
-    // loads the scales of the tile's two 128-column blocks into SBs[0..1].
-    // Everything else (and lanes past the scale grid) re-reads a valid word.
-    __amdgpu_buffer_rsrc_t rsc;
-    uint32_t sc_off = 0;
-    int sc_kind;   // 0: A rows, 1: B columns, 2: B blocks, 3: dummy
-    const int64_t nblocks = (N + 127) / 128;
-    if (wave < 2 && SA_MODE == SA_ROW) {
-        sc_kind = 0;
-        rsc = rsrc(p.sa, ((M - 1) * p.ldsa + KB) * 4);
-    } else if (wave >= 2 && wave < 6 && SB_MODE == SB_ROW) {
-        sc_kind = 1;
-        rsc = rsrc(p.sb, ((N - 1) * p.ldsb + KB) * 4);
-    } else if (wave == 2 && SB_MODE == SB_BLOCK) {
-        sc_kind = 2;
-        if (B_KN)
-            rsc = rsrc(p.sb, ((int64_t)(KB - 1) * p.ldsb + nblocks) * 4);
-        else
-            rsc = rsrc(p.sb + (GROUPED ? (int64_t)grp_e * p.sb_group_stride : 0),
-                       ((nblocks - 1) * p.ldsb + KB) * 4);
-    } else {
-        sc_kind = 3;
-        rsc = rsrc(p.sa, 4);
-    }
-    auto set_scale_offset = [&](int64_t tm0, int64_t tn0) {
-        if (sc_kind == 0) {
-            int64_t row = tm0 + 64 * wave + lane;
-            row = row < M ? row : M - 1;
-            sc_off = (uint32_t)(row * p.ldsa * 4);
-        } else if (sc_kind == 1) {
-            int64_t row = tn0 + 64 * (wave - 2) + lane;
-            row = row < N ? row : N - 1;
-            sc_off = (uint32_t)(row * p.ldsb * 4);
-        } else if (sc_kind == 2) {
-            int64_t blk = tn0 / 128 + (lane < 2 ? lane : 1);
-            blk = blk < nblocks ? blk : nblocks - 1;
-            sc_off = B_KN ? (uint32_t)(blk * 4) : (uint32_t)(blk * p.ldsb * 4);
-        }
-    };
-    set_scale_offset(m0, n0);
-
-    // Load u (0..6) of chunk kb: A rows (u < 2), B rows (2 <= u < 6), scales
-    // (u = 6).  Chunks at or past KB go to the dummy buffers (their source
-    // offsets lie in or past the operand; the buffer resource bounds them).
-    auto issue_one = [&](int kb, int u) {
-        const int st = kb % kStages;
-        const bool real = kb < KB;
-        const uint32_t k0 = (uint32_t)kb * TBK;
-        if (u < 2) {
-            dma16(ra, real ? &As[st][(16 * wave + 8 * u) * TBK] : Ddummy, offa[u], k0);
-        } else if (u < 6) {
-            const int t = u - 2;
-            if (B_KN)
-                dma16(rb, real ? &Bs[st][(16 * wave + 4 * t) * TBN] : Ddummy, offb[t], k0 * (uint32_t)p.ldb);
-            else
-                dma16(rb, real ? &Bs[st][(32 * wave + 8 * t) * TBK] : Ddummy, offb[t], k0);
-        } else {
-            float* dst = !real ? Sdummy
-                       : sc_kind == 0 ? &SAs[st][64 * wave]
-                       : sc_kind == 1 ? &SBs[st][64 * (wave - 2)]
-                       : sc_kind == 2 ? &SBs[st][0] : Sdummy;
-            const uint32_t sc_soff = (sc_kind == 3 || !real) ? 0u
-                                   : (sc_kind == 2 && B_KN) ? (uint32_t)(kb * p.ldsb * 4) : (uint32_t)kb * 4;
-            dma4(rsc, dst, sc_off, sc_soff);
-        }
-    };
-    auto issue = [&](int kb) {
-#pragma unroll
-        for (int u = 0; u < kLoadsPerChunk; ++u) issue_one(kb, u);
-    };
-
-    v4f acc[NMI][NNI];
-
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
-    const int lrow = lane & 15;
-    const int kgrp = lane >> 4;
-    const int grp = wave >> 2;                    // ping-pong group
-    const int wm0 = grp * WTM;                    // group g: rows [64g, 64g+64)
-    const int wn0 = (wave & 3) * WTN;             // 4 waves along N
-    const float sa_t = (SA_MODE == SA_TENSOR && KB > 0) ? p.sa[0] : 0.0f;
-    const float sb_t = (SB_MODE == SB_TENSOR && KB > 0) ? p.sb[0] : 0.0f;
-    const int a_off0 = sw(wm0 + lrow, 2 * kgrp), a_off1 = sw(wm0 + lrow, 2 * kgrp + 1);
-    const int b_off0 = sw(wn0 + lrow, 2 * kgrp), b_off1 = sw(wn0 + lrow, 2 * kgrp + 1);
-    // [K][N] B: lane (group g = kgrp, i = lrow) addresses K row 32g + i/2 at
-    // column wn0 + 16j + 8 (i & 1); reads t = 0..3 step 8 K rows (2048 bytes)
-    int kn_off[NNI];
-#pragma unroll
-    for (int j = 0; j < NNI; ++j) {
-        const int r = 32 * kgrp + (lrow >> 1);
-        const int c = (wn0 >> 4) + j;
-        kn_off[j] = r * TBN + ((c ^ kn_key(r)) << 4) + 8 * (lrow & 1);
-    }
-
-    const uint32_t lds_a = lds_addr(As), lds_b = lds_addr(Bs);
-    // the MFMA takes the B fragment as its first operand, so lane l's outputs
-    // are C[m = .. + l % 16][n = .. + 4 (l / 16) + r]: four adjacent columns
-    const uint32_t lds_sa = lds_addr(SAs) + 4 * (wm0 + lrow);
-    const uint32_t lds_sb = lds_addr(SBs) + 4 * (wn0 + 4 * kgrp);
-    // the wave's 64 columns lie in one 128-column block of B's scale grid
-    const uint32_t lds_sblk = lds_addr(SBs) + 4 * (wn0 / 128);
-
-    // issue the LDS reads of one chunk's operands and scales (no wait)
-    // Issue order: scales, the 4 A fragments, then per B fragment j its
-    // column scales (row-scaled B) and its reads.  LDS reads complete in
-    // order, so compute can start on B fragment 0 while 1..3 are in flight.
-    auto read_frags = [&](int st, Frags& f) {
-        if (SA_MODE == SA_ROW) {
-            const uint32_t sa = lds_sa + st * TBM * 4;
-            f.sa[0] = ds32<0>(sa);
-            f.sa[1] = ds32<64>(sa);
-            f.sa[2] = ds32<128>(sa);
-            f.sa[3] = ds32<192>(sa);
-        }
-        if (SB_MODE == SB_BLOCK) f.sbk = ds32<0>(lds_sblk + st * TBN * 4);
-        const uint32_t a0 = lds_a + st * kAStage + a_off0, a1 = lds_a + st * kAStage + a_off1;
-        f.a[0] = cat(ds128<0 * 16 * TBK>(a0), ds128<0 * 16 * TBK>(a1));
-        f.a[1] = cat(ds128<1 * 16 * TBK>(a0), ds128<1 * 16 * TBK>(a1));
-        f.a[2] = cat(ds128<2 * 16 * TBK>(a0), ds128<2 * 16 * TBK>(a1));
-        f.a[3] = cat(ds128<3 * 16 * TBK>(a0), ds128<3 * 16 * TBK>(a1));
-        const uint32_t sbp = lds_sb + st * TBN * 4;
-        const uint32_t bs = lds_b + st * kBStage;
-        const uint32_t b0 = bs + b_off0, b1 = bs + b_off1;
-#pragma unroll
-        for (int j = 0; j < NNI; ++j) {
-            if (SB_MODE == SB_ROW) {
-                if (j == 0) f.sbc[0] = (v4f)ds128<0>(sbp);
-                if (j == 1) f.sbc[1] = (v4f)ds128<64>(sbp);
-                if (j == 2) f.sbc[2] = (v4f)ds128<128>(sbp);
-                if (j == 3) f.sbc[3] = (v4f)ds128<192>(sbp);
-            }
-            if (B_KN) {
-                const uint32_t ad = bs + kn_off[j];
-                f.b[j] = cat4(ds64tr<0>(ad), ds64tr<8 * TBN>(ad), ds64tr<16 * TBN>(ad), ds64tr<24 * TBN>(ad));
-            } else {
-                if (j == 0) f.b[0] = cat(ds128<0 * 16 * TBK>(b0), ds128<0 * 16 * TBK>(b1));
-                if (j == 1) f.b[1] = cat(ds128<1 * 16 * TBK>(b0), ds128<1 * 16 * TBK>(b1));
-                if (j == 2) f.b[2] = cat(ds128<2 * 16 * TBK>(b0), ds128<2 * 16 * TBK>(b1));
-                if (j == 3) f.b[3] = cat(ds128<3 * 16 * TBK>(b0), ds128<3 * 16 * TBK>(b1));
-            }
-        }
-    };
-    // LDS reads per B fragment group (its column scales and its reads)
-    constexpr int kPerB = (SB_MODE == SB_ROW ? 1 : 0) + (B_KN ? 4 : 2);
-
-    // one MFMA per 16x16 block gives the chunk's fp32 partial, one FMA per
-    // output scales it into the accumulator
-    // One MFMA per 16x16 block gives the chunk's fp32 partial and four FMAs
-    // per lane scale it into the accumulator.  The FMAs of block u run
-    // behind the MFMA of block u+1 (software pipelined), and the loads of
-    // chunk kb_load are issued one per MFMA, so that a busy memory pipeline
-    // holds up at most one issue slot at a time.  Scheduling fences keep
-    // each step's instructions together.
-    //
-    // B fragment j (and, for j = 0, everything issued before it) has landed
-    // once only the reads of fragments j+1.. may be pending; the registers
-    // are asm operands, so no use moves above the wait.
-    auto wait_b = [&](Frags& f, int j) {
-        if (j == 0) {
-            lgkm_wait<(NNI - 1) * kPerB>(f.b[0]);
-            pin4(f.a[0], f.a[1], f.a[2], f.a[3]);
-            if (SA_MODE == SA_ROW) asm volatile("" : "+v"(f.sa[0]), "+v"(f.sa[1]), "+v"(f.sa[2]), "+v"(f.sa[3]));
-            if (SB_MODE == SB_BLOCK) asm volatile("" : "+v"(f.sbk));
-        } else if (j == 1) {
-            lgkm_wait<(NNI - 2) * kPerB>(f.b[1]);
-        } else if (j == 2) {
-            lgkm_wait<(NNI - 3) * kPerB>(f.b[2]);
-        } else {
-            lgkm_wait<0>(f.b[3]);
-        }
-        if (SB_MODE == SB_ROW) asm volatile("" : "+v"(f.sbc[j]));
-    };
-    float rs[NMI];   // per-row combined scales of the chunk being computed
-    auto set_rs = [&](const Frags& f) {
-#pragma unroll
-        for (int i = 0; i < NMI; ++i) {
-            const float sa_i = SA_MODE == SA_ROW ? f.sa[i] : sa_t;
-            rs[i] = SB_MODE == SB_BLOCK ? sa_i * f.sbk : SB_MODE == SB_TENSOR ? sa_i * sb_t : sa_i;
-        }
-    };
-    // the MFMAs of B fragments [jlo, jhi); loads of chunk kb_load (if
-    // with_loads) ride on the first 7 of them
-    auto blocks = [&](Frags& f, int jlo, int jhi, bool staged, bool with_loads, int kb_load) {
-        auto scale_into = [&](const v4f& part, int i, int j) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float t = SB_MODE == SB_ROW ? rs[i] * f.sbc[j][r] : rs[i];
-                acc[i][j][r] = __builtin_fmaf(part[r], t, acc[i][j][r]);
-            }
-        };
-        v4f prev = zero;
-#pragma unroll
-        for (int u = 0; u < NMI * NNI; ++u) {
-            const int j = u / NMI, i = u % NMI;
-            if (j < jlo || j >= jhi) continue;
-            const int v = u - jlo * NMI;
-            if (staged && i == 0) wait_b(f, j);
-            if (staged && u == 0) set_rs(f);
-            const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b[j], f.a[i], zero, 0, 0, 0, 0, 0, 0);
-            if (with_loads && v < kLoadsPerChunk) issue_one(kb_load, v);
-            if (v > 0) scale_into(prev, (u - 1) % NMI, (u - 1) / NMI);
-            __builtin_amdgcn_sched_barrier(0);
-            prev = part;
-        }
-        scale_into(prev, NMI - 1, jhi - 1);
-        // a part with fewer MFMAs than loads issues the rest here
-        if (with_loads) {
-#pragma unroll
-            for (int v = (jhi - jlo) * NMI; v < kLoadsPerChunk; ++v) issue_one(kb_load, v);
-        }
-        // keep the FMAs here: sunk past the next chunk's branches they would
-        // hold every partial live across them
-#pragma unroll
-        for (int i = 0; i < NMI; ++i)
-#pragma unroll
-            for (int j = 0; j < NNI; ++j)
-                if (j >= jlo && j < jhi) asm volatile("" : "+v"(acc[i][j]));
-    };
-    // every read of the chunk in f has completed (before a barrier that
-    // lets the chunk's stage be reloaded)
-    auto reads_done = [&](Frags& f) {
-        lgkm_wait<0>(f.b[3]);
-        asm volatile("" : "+v"(f.b[2]));
-        if (SB_MODE == SB_ROW) asm volatile("" : "+v"(f.sbc[2]), "+v"(f.sbc[3]));
-    };
-
-    // Chunk kb+1 is made ready (its loads landed in every wave, the stage of
-    // chunk kb is free because every wave has its fragments in registers,
-    // chunk kb+3 is issued into that stage) and its fragment reads are in
-    // flight while the MFMAs of chunk kb run from the other register set.
-    auto ready = [&](int kb) {
-        __builtin_amdgcn_sched_barrier(0);
-        // the loads of chunk kb+1 (real or dummy) are the only younger ones
-        wait_vm<kLoadsPerChunk>();
-        __builtin_amdgcn_s_barrier();
-        if (kb == KB - 1 && k_tail < TBK) {
-            zero_k_tail<B_KN>(As[kb % kStages], Bs[kb % kStages], k_tail, tid);
-            __syncthreads();
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // first tile's first two chunks
-    // chunks 0 and 1 (dummy if KB == 1) of the first tile; with K == 0 the
-    // operands may be NULL and nothing is loaded
-    if (KB > 0) {
-        issue(0);
-        issue(1);
-    }
-    for (;;) {
-#pragma unroll
-        for (int i = 0; i < NMI; ++i)
-#pragma unroll
-            for (int j = 0; j < NNI; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-        if (KB > 0) {
-            // The two wave groups (waves 0-3 and 4-7, one of each per SIMD)
-            // are staggered by half a chunk without an extra barrier: after
-            // the barrier of chunk kb, group 0 reads chunk kb and computes
-            // it, while group 1 first computes the second half (B fragments
-            // 2, 3) of chunk kb-1 from its registers, then reads chunk kb and
-            // computes its first half.  So on each SIMD one wave issues MFMAs
-            // while the other waits for LDS.  Both groups pass one barrier
-            // per chunk; each has its own loop so every compute step runs on
-            // every path.
-            Frags f;
-            if (grp == 0) {
-                for (int kb = 0; kb < KB; ++kb) {
-                    ready(kb);
-                    read_frags(kb % kStages, f);
-                    blocks(f, 0, NNI, true, true, kb + 2);
-                }
-            } else {
-                ready(0);
-                read_frags(0, f);
-                blocks(f, 0, NNI / 2, true, true, 2);
-                reads_done(f);
-                for (int kb = 1; kb < KB; ++kb) {
-                    ready(kb);
-                    blocks(f, NNI / 2, NNI, false, true, kb + 2);   // chunk kb-1
-                    read_frags(kb % kStages, f);
-                    blocks(f, 0, NNI / 2, true, false, 0);          // chunk kb
-                    reads_done(f);
-                }
-                blocks(f, NNI / 2, NNI, false, false, 0);           // chunk KB-1
-            }
-        }
-        // Store this tile, then start the next tile's loads.  The stores go
-        // first so that waiting for the next tile's first chunk (vmcnt) does
-        // not also wait for its second chunk.
-        const int64_t cm0 = m0, cn0 = n0;
-        const bool store_tile = tile_live;
-        ti += nwg;
-        const bool more = ti < range_len;
-        // epilogue: lane l holds C[m][n .. n+3] of each block
-#pragma unroll
-        for (int i = 0; i < NMI; ++i) {
-            const int64_t m = cm0 + wm0 + 16 * i + lrow;
-            if (m >= M || !store_tile) continue;
-#pragma unroll
-            for (int j = 0; j < NNI; ++j) {
-                const int64_t n = cn0 + wn0 + 16 * j + 4 * kgrp;
-                const v4f v = acc[i][j];
-                if (n + 3 < N) {
-                    if (OUT_BF16) {
-                        const uint32_t lo = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-                        const uint32_t hi = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-                        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.c) + m * p.ldc + n) = make_uint2(lo, hi);
-                    } else {
-                        *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.c) + m * p.ldc + n) = v;
-                    }
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        if (n + r < N) {
-                            if (OUT_BF16)
-                                reinterpret_cast<uint16_t*>(p.c)[m * p.ldc + n + r] = (uint16_t)bf16_rne(v[r]);
-                            else
-                                reinterpret_cast<float*>(p.c)[m * p.ldc + n + r] = v[r];
-                        }
-                    }
-                }
-            }
-        }
-        if (more) {
-            tile_origin(ti, m0, n0);
-            set_group(m0);
-            set_tile_offsets(m0, n0);
-            set_scale_offset(m0, n0);
-            if (GROUPED && sc_kind == 2)
-                rsc = rsrc(p.sb + (int64_t)grp_e * p.sb_group_stride, ((nblocks - 1) * p.ldsb + KB) * 4);
-            // every wave is done reading this tile's stages
-            __builtin_amdgcn_s_barrier();
-            if (KB > 0) {
-                issue(0);
-                issue(1);
-            }
-        }
-        if (!more) break;
-    }
-    // drain the stores before the wave ends
-    wait_vm<0>();
-}
-
 // ---------------------------------------------------------------------------
-// Split-K ping-pong variant for a B operand scaled per 128x128 block or per
-// tensor (forward, dgrad, grouped).  Same workgroup tile and LDS ring as
-// above, but each wave owns all 128 rows of its 64 columns (32 MFMAs per
-// chunk from 8 A and 4 B fragments: 768 LDS bytes per MFMA instead of 1024),
-// and the two wave groups (one wave of each per SIMD) take alternate K
-// chunks.  Phase q (one barrier each): group q % 2 loads chunk q+2 and reads
-// chunk q from LDS into registers while the other group runs the MFMAs of
-// chunk q-1 from registers, so each SIMD has one wave on the matrix core
-// while its partner waits for memory.  A group loads exactly the chunks it
-// reads, two phases ahead, so waiting for a chunk is vmcnt(0) in its waves.
-// With [N][K] B each wave loads the B rows of its own columns, so it reads
-// those right after its compute phase and only the shared A rows after the
-// barrier.
+// The kernel.  Each wave owns all 128 rows of its 64 columns (32 MFMAs per
+// chunk from 8 A and 4 B fragments: 768 LDS bytes per MFMA, against 1024
+// for a 64 x 64 wave tile), and the two wave groups (one wave of each per
+// SIMD) take alternate K chunks.  Phase q (one barrier each): group q % 2
+// loads chunk q+2 and reads chunk q from LDS into registers while the other
+// group runs the MFMAs of chunk q-1 from registers, so each SIMD has one
+// wave on the matrix core while its partner waits for memory.  A group
+// loads exactly the chunks it reads, two phases ahead, so waiting for a
+// chunk is vmcnt(0) in its waves.  With [N][K] B each wave loads the B rows
+// of its own columns, so it reads those right after its compute phase and
+// only the shared A rows after the barrier.
 // At the end of a tile each group holds the sum over its chunks; the halves
 // are added through LDS (the ring is idle by then), each group finishing and
 // storing 64 of the 128 rows.
-constexpr int PMI = TBM / 16;                  // 16-row blocks per wave
-constexpr int kStageBytes = kAStage + kBStage; // A at 0, B at kAStage
-
-struct FragsPP {
+struct Frags {
     v8i a[PMI], b[NNI];
     float s[PMI];    // combined scale of the lane's row in block i for the chunk
     float sbk;       // SB of the wave's 128-column block (block-scaled B)
@@ -706,7 +228,7 @@ __device__ __forceinline__ v4f col_scales(uint32_t a, int j)
 }
 
 template <int SA_MODE, int SB_MODE, bool B_KN, bool OUT_BF16, bool GROUPED>
-__global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs p)
+__global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
 {
     constexpr int kSbStages = SB_MODE == SB_ROW ? 4 : kStages;
     static_assert(!(B_KN && SB_MODE == SB_ROW), "row-scaled B is [N][K] only");
@@ -724,7 +246,11 @@ __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs p)
     const int grp = wave >> 2;   // chunk parity of this wave
     const int wq = wave & 3;     // wave within its group: columns [64 wq, 64 wq + 64)
 
-    // persistent workgroups over XCD tile ranges (as in gemm_nk_kernel)
+    // Persistent workgroups.  Workgroups are dealt to the 8 XCDs
+    // round-robin; XCD x owns a contiguous range of tile ids, walked by its
+    // workgroups in lockstep (tile id = start + local + i * count), in
+    // groups of kGroupM M-tiles so that concurrently running tiles share A
+    // and B panels in that XCD's L2.
     const int T = p.tiles_m * p.tiles_n;
     const int xcd = blockIdx.x & 7;
     const int local = blockIdx.x >> 3;
@@ -862,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs p)
     // across all columns by every wave of the group, so those are read after
     // the phase barrier like A.
     constexpr bool kEarlyB = !B_KN;
-    auto read_b = [&](int st, FragsPP& f) {
+    auto read_b = [&](int st, Frags& f) {
         int l = lane;
         asm volatile("" : "+v"(l));
         const int lrow = l & 15, kgrp = l >> 4;
@@ -889,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs p)
     };
     // A fragments and scales of the chunk in stage st (A rows are loaded by
     // all four waves of the group: read after the phase barrier)
-    auto read_a = [&](int st, FragsPP& f) {
+    auto read_a = [&](int st, Frags& f) {
         int l = lane;
         asm volatile("" : "+v"(l));
         const int lrow = l & 15, kgrp = l >> 4;
@@ -917,7 +443,7 @@ __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs p)
         f.a[7] = frag_nk<7>(a0, a1);
     };
     // all reads of f have landed; fold the chunk's B scale into the row scales
-    auto reads_wait = [&](FragsPP& f) {
+    auto reads_wait = [&](Frags& f) {
         lgkm_wait<0>(f.a[7]);
         pin4(f.a[0], f.a[1], f.a[2], f.a[3]);
         asm volatile("" : "+v"(f.a[4]), "+v"(f.a[5]), "+v"(f.a[6]));
@@ -935,7 +461,7 @@ __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs p)
     // the transposing reads, as [K][N]) holds the chunk's K bytes
     // [32 kgrp, 32 kgrp + 32) in order, so one mask per dword clears the bytes
     // at or past K in both operands (a code past K may be anything, NaN too).
-    auto mask_k_tail = [&](FragsPP& f) {
+    auto mask_k_tail = [&](Frags& f) {
         const int kgrp = lane >> 4;
 #pragma unroll
         for (int d = 0; d < 8; ++d) {
@@ -951,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs p)
     // of block u+1.  Row-scaled B: the lane's 4 column scales of block j are
     // read from LDS while the MFMAs of block j-1 run, and each FMA takes
     // the product of its row and column scale.
-    auto compute = [&](FragsPP& f, int c) {
+    auto compute = [&](Frags& f, int c) {
         uint32_t sbp = 0;
         v4f sc[NNI];
         if (SB_MODE == SB_ROW) {
@@ -1008,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs p)
             // A group reads the B fragments of its next chunk right after its
             // compute phase (its own loads, two phases old by then), so its
             // read phase holds only the A fragments and scales.
-            FragsPP f;
+            Frags f;
             int q = 0;
             if (grp == 1) {
                 bar();
@@ -1123,26 +649,11 @@ __global__ __launch_bounds__(kThreads) void gemm_pp_kernel(GemmArgs p)
 }
 
 template <int SA_MODE, int SB_MODE, bool B_KN, bool GROUPED = false>
-static void launch_pp(const GemmArgs& g, bool bf, hipStream_t st)
+static void launch_tiles(const GemmArgs& g, bool bf, hipStream_t st)
 {
     GemmArgs a = g;
     a.tiles_m = (int)((g.M + TBM - 1) / TBM);
     a.tiles_n = (int)((g.N + TBN - 1) / TBN);
-    const int tiles = a.tiles_m * a.tiles_n;
-    dim3 grid((uint32_t)(tiles < g.num_cus ? tiles : g.num_cus));
-    if (bf)
-        hipLaunchKernelGGL((gemm_pp_kernel<SA_MODE, SB_MODE, B_KN, true, GROUPED>), grid, dim3(kThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL((gemm_pp_kernel<SA_MODE, SB_MODE, B_KN, false, GROUPED>), grid, dim3(kThreads), 0, st, a);
-}
-
-template <int SA_MODE, int SB_MODE, bool B_KN, bool GROUPED = false>
-static void launch2(const GemmArgs& g, bool bf, hipStream_t st)
-{
-    GemmArgs a = g;
-    a.tiles_m = (int)((g.M + TBM - 1) / TBM);
-    a.tiles_n = (int)((g.N + TBN - 1) / TBN);
-    // one persistent workgroup per CU (the LDS ring allows one per CU)
     const int tiles = a.tiles_m * a.tiles_n;
     dim3 grid((uint32_t)(tiles < g.num_cus ? tiles : g.num_cus));
     if (bf)
@@ -1157,7 +668,7 @@ bool launch_grouped_gemm_nk(const GemmArgs& g, bool out_bf16, hipStream_t st)
     if (g.G > kMaxLdsGroups || g.M * g.lda >= lim || (g.N + TBK) * g.ldb >= lim ||
         g.M * g.ldsa * 4 >= lim || g.sb_group_stride * 4 >= lim || (int64_t)g.KB * TBK >= lim)
         return false;
-    launch_pp<SA_ROW, SB_BLOCK, false, true>(g, out_bf16, st);
+    launch_tiles<SA_ROW, SB_BLOCK, false, true>(g, out_bf16, st);
     return true;
 }
 
@@ -1172,22 +683,22 @@ bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, bool
     if (b_kn) {
         if (sb_mode == SB_ROW) return false;
         if (sa_mode == SA_ROW) {
-            if (sb_mode == SB_BLOCK) launch_pp<SA_ROW, SB_BLOCK, true>(g, out_bf16, st);
-            else launch_pp<SA_ROW, SB_TENSOR, true>(g, out_bf16, st);
+            if (sb_mode == SB_BLOCK) launch_tiles<SA_ROW, SB_BLOCK, true>(g, out_bf16, st);
+            else launch_tiles<SA_ROW, SB_TENSOR, true>(g, out_bf16, st);
         } else {
-            if (sb_mode == SB_BLOCK) launch_pp<SA_TENSOR, SB_BLOCK, true>(g, out_bf16, st);
-            else launch_pp<SA_TENSOR, SB_TENSOR, true>(g, out_bf16, st);
+            if (sb_mode == SB_BLOCK) launch_tiles<SA_TENSOR, SB_BLOCK, true>(g, out_bf16, st);
+            else launch_tiles<SA_TENSOR, SB_TENSOR, true>(g, out_bf16, st);
         }
         return true;
     }
     if (sa_mode == SA_ROW) {
-        if (sb_mode == SB_BLOCK) launch_pp<SA_ROW, SB_BLOCK, false>(g, out_bf16, st);
-        else if (sb_mode == SB_ROW) launch_pp<SA_ROW, SB_ROW, false>(g, out_bf16, st);
-        else launch_pp<SA_ROW, SB_TENSOR, false>(g, out_bf16, st);
+        if (sb_mode == SB_BLOCK) launch_tiles<SA_ROW, SB_BLOCK, false>(g, out_bf16, st);
+        else if (sb_mode == SB_ROW) launch_tiles<SA_ROW, SB_ROW, false>(g, out_bf16, st);
+        else launch_tiles<SA_ROW, SB_TENSOR, false>(g, out_bf16, st);
     } else {
-        if (sb_mode == SB_BLOCK) launch_pp<SA_TENSOR, SB_BLOCK, false>(g, out_bf16, st);
-        else if (sb_mode == SB_ROW) launch_pp<SA_TENSOR, SB_ROW, false>(g, out_bf16, st);
-        else launch_pp<SA_TENSOR, SB_TENSOR, false>(g, out_bf16, st);
+        if (sb_mode == SB_BLOCK) launch_tiles<SA_TENSOR, SB_BLOCK, false>(g, out_bf16, st);
+        else if (sb_mode == SB_ROW) launch_tiles<SA_TENSOR, SB_ROW, false>(g, out_bf16, st);
+        else launch_tiles<SA_TENSOR, SB_TENSOR, false>(g, out_bf16, st);
     }
     return true;
 }
