@@ -31,7 +31,7 @@ TILE = 128
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         "libfp8q.so is not built (expected at %s); run "
-        "`python -m fp8_precision_quant_amd.build`" % LIB_PATH)
+        "`python fp8_precision_quant_amd/build.py`" % LIB_PATH)
 
 _lib = ctypes.CDLL(LIB_PATH)
 _i64, _int, _p = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
@@ -42,14 +42,19 @@ _lib.fp8_gemm_blockscaled.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _int
                                       _p, _i64, _int, _p, _i64, _int, _p, _i64, _int, _p]
 _lib.fp8_grouped_gemm.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _p,
                                   _p, _p, _p, _i64, _int, _p]
+_lib.fp8_grouped_gemm_dgrad.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _p,
+                                        _p, _p, _p, _i64, _int, _p]
+_lib.fp8_grouped_gemm_wgrad.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _p, _i64,
+                                        _p, _i64, _p, _i64, _p, _p, _i64, _p]
 for _f in ("fp8_quant_blockwise", "fp8_quant_transpose", "fp8_gemm_blockscaled",
-           "fp8_grouped_gemm"):
+           "fp8_grouped_gemm", "fp8_grouped_gemm_dgrad", "fp8_grouped_gemm_wgrad"):
     getattr(_lib, _f).restype = _int
 _lib.fp8q_status_string.argtypes = [_int]
 _lib.fp8q_status_string.restype = ctypes.c_char_p
 
 SYMBOLS = ("fp8_quant_blockwise", "fp8_quant_transpose", "fp8_gemm_blockscaled",
-           "fp8_grouped_gemm", "fp8q_status_string")
+           "fp8_grouped_gemm", "fp8_grouped_gemm_dgrad", "fp8_grouped_gemm_wgrad",
+           "fp8q_status_string")
 
 
 class Fp8qError(RuntimeError):
@@ -193,4 +198,54 @@ def fp8_grouped_gemm(a: torch.Tensor, sa: torch.Tensor, group_offsets: torch.Ten
                                _ptr(group_offsets), _ptr(b), _ptr(sb), _ptr(c), _ld(c), cd,
                                _stream(a.device, stream))
     _check(st, "fp8_grouped_gemm")
+    return c
+
+
+def fp8_grouped_gemm_dgrad(a: torch.Tensor, sa: torch.Tensor, group_offsets: torch.Tensor,
+                           w: torch.Tensor, sw: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                           c: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Per group e: rows [off[e], off[e+1]) of ``a[M_pad, N]`` (dY codes,
+    1x128 scales along N) times expert weight ``w[e]`` read as stored
+    (``w[G, N, K]`` codes, ``sw[G, ceil(N/128), ceil(K/128)]`` block scales):
+    dX[M_pad, K]."""
+    M_pad, N = a.shape
+    G, Nw, K = w.shape
+    if Nw != N:
+        raise ValueError("contraction sizes differ")
+    if group_offsets.dtype != torch.int32 or group_offsets.numel() != G + 1:
+        raise ValueError("group_offsets must be int32 with G+1 entries")
+    if not (w.is_contiguous() and sw.is_contiguous() and group_offsets.is_contiguous()):
+        raise ValueError("w, sw and group_offsets must be contiguous")
+    if c is None:
+        c = _empty_aligned(M_pad, K, out_dtype, a.device, 16 // (4 if out_dtype == torch.float32 else 2))
+    cd = F32 if c.dtype == torch.float32 else BF16
+    st = _lib.fp8_grouped_gemm_dgrad(G, M_pad, N, K, _ptr(a), _ld(a), _ptr(sa), _ld(sa),
+                                     _ptr(group_offsets), _ptr(w), _ptr(sw), _ptr(c), _ld(c), cd,
+                                     _stream(a.device, stream))
+    _check(st, "fp8_grouped_gemm_dgrad")
+    return c
+
+
+def fp8_grouped_gemm_wgrad(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
+                           group_offsets: torch.Tensor, c: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """Per group e: dW[e] = sum over the group's tokens of ``a[N, M_pad]``
+    (dY^T codes) times ``b[K, M_pad]`` (X^T codes), both with 1x128 scales
+    along tokens (fp8_quant_transpose's column outputs): fp32 dW[G, N, K]."""
+    N, M_pad = a.shape
+    K, Mb = b.shape
+    if Mb != M_pad:
+        raise ValueError("token counts differ")
+    G = group_offsets.numel() - 1
+    if group_offsets.dtype != torch.int32 or G < 1 or not group_offsets.is_contiguous():
+        raise ValueError("group_offsets must be a contiguous int32 tensor with G+1 entries")
+    if c is None:
+        c = torch.empty((G, N, K), dtype=torch.float32, device=a.device)
+    if c.dtype != torch.float32 or c.dim() != 3 or c.shape != (G, N, K) or c.stride(0) != N * c.stride(1) \
+            or c.stride(2) != 1:
+        raise ValueError("c must be float32 [G, N, K] with group stride N * row stride")
+    st = _lib.fp8_grouped_gemm_wgrad(G, M_pad, N, K, _ptr(a), _ld(a), _ptr(sa), _ld(sa),
+                                     _ptr(b), _ld(b), _ptr(sb), _ld(sb), _ptr(group_offsets),
+                                     _ptr(c), c.stride(1), _stream(a.device, stream))
+    _check(st, "fp8_grouped_gemm_wgrad")
     return c

@@ -1,6 +1,7 @@
 """Build libfp8q.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-Usage: ``python -m fp8_precision_quant_amd.build`` (or ``build()`` from Python).
+Usage: ``python fp8_precision_quant_amd/build.py`` (run as a file: importing
+the package would first load the existing library), or ``__graft_entry__.build()``.
 Every source is compiled on each call; objects are compiled in parallel and
 linked in-tree next to this file, so the library travels with the source tree.
 """

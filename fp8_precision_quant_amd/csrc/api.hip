@@ -183,4 +183,52 @@ int fp8_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K,
     return launch_status();
 }
 
+int fp8_grouped_gemm_dgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K,
+                           const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                           const int32_t* group_offsets,
+                           const uint8_t* w, const float* sw,
+                           void* c, int64_t ldc, int c_dtype, void* stream)
+{
+    if (!dtype_ok(c_dtype)) return FP8Q_ERR_UNSUPPORTED;
+    if (G < 1 || M_pad < 0 || N < 0 || K < 0 || M_pad % kTile) return FP8Q_ERR_SHAPE;
+    if (M_pad == 0 || K == 0) return FP8Q_OK;
+    if (!group_offsets || !c) return FP8Q_ERR_NULL;
+    if (N > 0 && (!a || !sa || !w || !sw)) return FP8Q_ERR_NULL;
+    if (lda < N || ldc < K || ldsa < cdiv(N, kTile)) return FP8Q_ERR_SHAPE;
+    if (G >= kMaxIndex || (M_pad / kTile) * cdiv(K, 128) >= kMaxIndex) return FP8Q_ERR_SHAPE;
+    if (!aligned16(c) || K % 16 || (ldc * elem_size(c_dtype)) % 16) return FP8Q_ERR_ALIGN;
+    if (N > 0 && (!aligned16(a) || !aligned16(w) || lda % 16)) return FP8Q_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(group_offsets) & 3u) return FP8Q_ERR_ALIGN;
+    int st = check_device();
+    if (st != FP8Q_OK) return st;
+    if (!fp8q::launch_grouped_gemm_dgrad(G, M_pad, N, K, a, lda, sa, ldsa, group_offsets, w, sw, c, ldc,
+                                         c_dtype, static_cast<hipStream_t>(stream)))
+        return FP8Q_ERR_UNSUPPORTED;
+    return launch_status();
+}
+
+int fp8_grouped_gemm_wgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K,
+                           const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                           const uint8_t* b, int64_t ldb, const float* sb, int64_t ldsb,
+                           const int32_t* group_offsets,
+                           float* c, int64_t ldc, void* stream)
+{
+    if (G < 1 || M_pad < 0 || N < 0 || K < 0 || M_pad % kTile) return FP8Q_ERR_SHAPE;
+    if (N == 0 || K == 0) return FP8Q_OK;
+    if (!group_offsets || !c) return FP8Q_ERR_NULL;
+    if (M_pad > 0 && (!a || !sa || !b || !sb)) return FP8Q_ERR_NULL;
+    if (lda < M_pad || ldb < M_pad || ldc < K || ldsa < M_pad / kTile || ldsb < M_pad / kTile)
+        return FP8Q_ERR_SHAPE;
+    if (G >= kMaxIndex || G * cdiv(N, 128) * cdiv(K, 256) >= kMaxIndex) return FP8Q_ERR_SHAPE;
+    if (!aligned16(c) || (ldc * 4) % 16) return FP8Q_ERR_ALIGN;
+    if (M_pad > 0 && (!aligned16(a) || !aligned16(b) || lda % 16 || ldb % 16)) return FP8Q_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(group_offsets) & 3u) return FP8Q_ERR_ALIGN;
+    int st = check_device();
+    if (st != FP8Q_OK) return st;
+    if (!fp8q::launch_grouped_gemm_wgrad(G, M_pad, N, K, a, lda, sa, ldsa, b, ldb, sb, ldsb, group_offsets,
+                                         c, ldc, static_cast<hipStream_t>(stream)))
+        return FP8Q_ERR_UNSUPPORTED;
+    return launch_status();
+}
+
 }  // extern "C"

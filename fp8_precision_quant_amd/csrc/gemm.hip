@@ -408,7 +408,7 @@ void launch_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K, const u
     g.b_group_stride = N * K;
     g.sb_group_stride = ((N + 127) / 128) * (int64_t)g.KB;
     g.num_cus = device_cu_count();
-    if (launch_grouped_gemm_nk(g, c_dtype == FP8Q_BF16, st)) return;
+    if (launch_grouped_gemm_nk(g, c_dtype == FP8Q_BF16, false, st)) return;
     dim3 grid((uint32_t)(g.tiles_m * g.tiles_n));
     if (c_dtype == FP8Q_BF16)
         hipLaunchKernelGGL((gemm_kernel<128, SA_ROW, SB_BLOCK, false, true, true>), grid,
@@ -416,6 +416,48 @@ void launch_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K, const u
     else
         hipLaunchKernelGGL((gemm_kernel<128, SA_ROW, SB_BLOCK, false, false, true>), grid,
                            dim3(kGemmThreads), 0, st, g);
+}
+
+bool launch_grouped_gemm_dgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K, const uint8_t* a,
+                               int64_t lda, const float* sa, int64_t ldsa, const int32_t* offsets,
+                               const uint8_t* w, const float* sw, void* c, int64_t ldc, int c_dtype,
+                               hipStream_t st)
+{
+    // dX[m][k] = sum_n dY[m][n] W_e[n][k]: contraction over W's rows, so in
+    // GEMM terms M = M_pad, N = K, K = N and B is W_e read as stored ([K][N])
+    GemmArgs g{};
+    g.M = M_pad; g.N = K; g.K = N;
+    g.a = a; g.lda = lda; g.sa = sa; g.ldsa = ldsa;
+    g.b = w; g.ldb = K; g.sb = sw;
+    g.KB = (int)((N + BK - 1) / BK);
+    g.ldsb = (K + 127) / 128;
+    g.c = c; g.ldc = ldc;
+    g.offsets = offsets;
+    g.G = (int)G;
+    g.b_group_stride = N * K;
+    g.sb_group_stride = (int64_t)g.KB * g.ldsb;
+    g.num_cus = device_cu_count();
+    return launch_grouped_gemm_nk(g, c_dtype == FP8Q_BF16, true, st);
+}
+
+bool launch_grouped_gemm_wgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K, const uint8_t* a,
+                               int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b,
+                               int64_t ldb, const float* sb, int64_t ldsb, const int32_t* offsets,
+                               float* c, int64_t ldc, hipStream_t st)
+{
+    // dW_e[n][k] = sum over the group's tokens t of dYT[n][t] XT[k][t]: rows
+    // of A and B are N and K, the contraction runs over the group's tokens
+    GemmArgs g{};
+    g.M = N; g.N = K; g.K = M_pad;
+    g.a = a; g.lda = lda; g.sa = sa; g.ldsa = ldsa;
+    g.b = b; g.ldb = ldb; g.sb = sb; g.ldsb = ldsb;
+    g.KB = (int)(M_pad / BK);
+    g.c = c; g.ldc = ldc;
+    g.offsets = offsets;
+    g.G = (int)G;
+    g.c_group_stride = N * ldc;
+    g.num_cus = device_cu_count();
+    return launch_grouped_wgrad_nk(g, st);
 }
 
 }  // namespace fp8q

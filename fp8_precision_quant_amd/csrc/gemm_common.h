@@ -27,6 +27,7 @@ struct GemmArgs {
     const int32_t* offsets;
     int G;
     int64_t b_group_stride, sb_group_stride;
+    int64_t c_group_stride;  // groups of K: elements between groups' output blocks
 };
 
 __device__ __forceinline__ uint32_t bf16_rne(float f)
@@ -55,7 +56,11 @@ __device__ __forceinline__ uint4 mask_bytes(uint4 v, int valid)
 // caller then uses the general kernel).
 bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, bool out_bf16, hipStream_t st);
 // Grouped (MoE) launch of the same kernel: A row tiles select their expert
-// through the device group offsets; false if the call is not covered.
-bool launch_grouped_gemm_nk(const GemmArgs& g, bool out_bf16, hipStream_t st);
+// through the device group offsets (B per expert as [N][K] for the forward,
+// read as [K][N] for dgrad); false if the call is not covered.
+bool launch_grouped_gemm_nk(const GemmArgs& g, bool out_bf16, bool b_kn, hipStream_t st);
+// Grouped weight gradient: for each group, the product over the group's
+// token chunks only, into the group's own fp32 output block.
+bool launch_grouped_wgrad_nk(const GemmArgs& g, hipStream_t st);
 
 }  // namespace fp8q

@@ -227,12 +227,16 @@ __device__ __forceinline__ v4f col_scales(uint32_t a, int j)
     }
 }
 
-template <int SA_MODE, int SB_MODE, bool B_KN, bool OUT_BF16, bool GROUPED>
+// GMODE: 0 dense; 1 groups of A rows (MoE forward and dgrad: the row tile's
+// group selects the expert's B and B scales); 2 groups of K (MoE weight
+// gradient: tile rows index the virtual matrix [G][M], the group's token
+// chunks are the K loop and each group has its own output block).
+template <int SA_MODE, int SB_MODE, bool B_KN, bool OUT_BF16, int GMODE>
 __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
 {
     constexpr int kSbStages = SB_MODE == SB_ROW ? 4 : kStages;
     static_assert(!(B_KN && SB_MODE == SB_ROW), "row-scaled B is [N][K] only");
-    __shared__ int32_t goff[GROUPED ? kMaxLdsGroups + 1 : 1];
+    __shared__ int32_t goff[GMODE != 0 ? kMaxLdsGroups + 1 : 1];
     __shared__ __attribute__((aligned(16))) uint8_t Stg[kStages][kStageBytes];
     __shared__ __attribute__((aligned(16))) float SAs[kStages][TBM];
     // B scales of a chunk: its two 128-column blocks (block-scaled B), or its
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     };
     int ti = local;
     if (ti >= range_len) return;
-    if (GROUPED) {
+    if (GMODE != 0) {
         for (int i = tid; i <= p.G; i += kThreads) goff[i] = p.offsets[i];
         __syncthreads();
     }
@@ -278,8 +282,11 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     tile_origin(ti, m0, n0);
 
     const int64_t M = p.M, N = p.N, K = p.K;
-    const int KB = p.KB;
-    const int k_tail = (int)(K - (int64_t)(KB - 1) * TBK);
+    const int KBg = p.KB;                 // chunks of the whole K extent
+    const int k_tail = (int)(K - (int64_t)(KBg - 1) * TBK);
+    int KB = KBg;                         // chunks of this tile's K loop
+    int kb_base = 0;                      // its first chunk
+    int64_t c_off = 0;                    // its output block (elements)
 
     const int64_t ext_a = (M - 1) * p.lda + ((K + 15) & ~(int64_t)15);
     const int64_t ext_b = B_KN ? (K - 1) * p.ldb + ((N + 15) & ~(int64_t)15)
@@ -288,16 +295,32 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     __amdgpu_buffer_rsrc_t rb = rsrc(p.b, ext_b);
     int grp_e = 0;
     bool tile_live = true;
-    auto set_group = [&](int64_t tm0) {
-        if (!GROUPED) return;
-        int lo = 0, hi = p.G - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if ((int64_t)goff[mid] <= tm0) lo = mid; else hi = mid - 1;
+    // groups of rows: the tile's group e (off[e] <= m0 < off[e+1]) selects
+    // expert e's B and block scales; tiles at or past off[G] are computed
+    // from group G-1 but not stored.  Groups of K: virtual row tile
+    // e * ceil(M/128) + t is row tile t of group e, whose K loop runs over
+    // the chunks [off[e], off[e+1]) / 128 (none for an empty group).
+    // (values read from LDS are made wave-uniform explicitly, so that the
+    // loop bounds and addresses derived from them stay scalar)
+    const int tiles_g = (int)((M + TBM - 1) / TBM);
+    auto set_group = [&](int64_t& tm0) {
+        if (GMODE == 1) {
+            int lo = 0, hi = p.G - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if ((int64_t)goff[mid] <= tm0) lo = mid; else hi = mid - 1;
+            }
+            grp_e = __builtin_amdgcn_readfirstlane(lo);
+            tile_live = tm0 < (int64_t)__builtin_amdgcn_readfirstlane(goff[p.G]);
+            rb = rsrc(p.b + (int64_t)grp_e * p.b_group_stride, ext_b);
+        } else if (GMODE == 2) {
+            const int vt = (int)(tm0 / TBM);
+            grp_e = __builtin_amdgcn_readfirstlane(vt / tiles_g);
+            tm0 = (int64_t)(vt - grp_e * tiles_g) * TBM;
+            kb_base = __builtin_amdgcn_readfirstlane(goff[grp_e]) / TBK;
+            KB = __builtin_amdgcn_readfirstlane(goff[grp_e + 1]) / TBK - kb_base;
+            c_off = (int64_t)grp_e * p.c_group_stride;
         }
-        grp_e = lo;
-        tile_live = tm0 < (int64_t)goff[p.G];
-        rb = rsrc(p.b + (int64_t)grp_e * p.b_group_stride, ext_b);
     };
     set_group(m0);
 
@@ -308,12 +331,13 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     const int64_t nblocks = (N + 127) / 128;
     const bool load_sa = SA_MODE == SA_ROW && wq < 2;
     const bool load_sb = SB_MODE == SB_ROW || (SB_MODE == SB_BLOCK && wq == 2);
-    const __amdgpu_buffer_rsrc_t rsa = rsrc(p.sa, SA_MODE == SA_ROW ? ((M - 1) * p.ldsa + KB) * 4 : 4);
+    const __amdgpu_buffer_rsrc_t rsa = rsrc(p.sa, SA_MODE == SA_ROW ? ((M - 1) * p.ldsa + KBg) * 4 : 4);
     auto sb_rsrc = [&]() {
-        if (SB_MODE == SB_ROW) return rsrc(p.sb, ((N - 1) * p.ldsb + KB) * 4);
+        if (SB_MODE == SB_ROW) return rsrc(p.sb, ((N - 1) * p.ldsb + KBg) * 4);
         if (SB_MODE == SB_BLOCK) {
-            if (B_KN) return rsrc(p.sb, ((int64_t)(KB - 1) * p.ldsb + nblocks) * 4);
-            return rsrc(p.sb + (GROUPED ? (int64_t)grp_e * p.sb_group_stride : 0), ((nblocks - 1) * p.ldsb + KB) * 4);
+            const float* sbg = p.sb + (GMODE == 1 ? (int64_t)grp_e * p.sb_group_stride : 0);
+            if (B_KN) return rsrc(sbg, ((int64_t)(KBg - 1) * p.ldsb + nblocks) * 4);
+            return rsrc(sbg, ((nblocks - 1) * p.ldsb + KBg) * 4);
         }
         return rsrc(p.sb, 4);
     };
@@ -360,8 +384,9 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
         // here rather than hoisted out of the loop into spilled registers
         uint32_t a_lds = lds_addr(&Stg[st][0]) + (uint32_t)(32 * wq * TBK);
         uint32_t b_lds = lds_addr(&Stg[st][kAStage]) + (uint32_t)(B_KN ? 32 * wq * TBN : 64 * wq * TBK);
-        uint32_t a_soff = (uint32_t)kb * TBK, a_step = 8u * (uint32_t)p.lda;
-        uint32_t b_soff = B_KN ? (uint32_t)kb * TBK * (uint32_t)p.ldb : (uint32_t)kb * TBK;
+        const uint32_t kg = (uint32_t)(kb_base + kb);   // chunk within the whole K extent
+        uint32_t a_soff = kg * TBK, a_step = 8u * (uint32_t)p.lda;
+        uint32_t b_soff = B_KN ? kg * TBK * (uint32_t)p.ldb : kg * TBK;
         uint32_t b_step = (B_KN ? 4u : 8u) * (uint32_t)p.ldb;
         asm volatile("" : "+s"(a_lds), "+s"(b_lds), "+s"(a_soff), "+s"(a_step), "+s"(b_soff), "+s"(b_step));
 #pragma unroll
@@ -369,11 +394,11 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
 #pragma unroll
         for (int t = 0; t < 8; ++t)
             dma16_at(rb, b_lds + (uint32_t)(B_KN ? 4 * t * TBN : 8 * t * TBK), o.vb[t & 1], b_soff + t * b_step);
-        if (load_sa) dma4(rsa, &SAs[st][64 * wq], o.vsa, (uint32_t)kb * 4);
+        if (load_sa) dma4(rsa, &SAs[st][64 * wq], o.vsa, kg * 4);
         if (SB_MODE == SB_ROW)
-            dma4(rsb, &SBs[kb % kSbStages][64 * wq], o.vsb, (uint32_t)kb * 4);
+            dma4(rsb, &SBs[kb % kSbStages][64 * wq], o.vsb, kg * 4);
         else if (load_sb)
-            dma4(rsb, &SBs[st][0], o.vsb, B_KN ? (uint32_t)(kb * p.ldsb * 4) : (uint32_t)kb * 4);
+            dma4(rsb, &SBs[st][0], o.vsb, B_KN ? kg * (uint32_t)p.ldsb * 4 : kg * 4);
     };
 
     v4f acc[PMI][NNI];
@@ -551,7 +576,8 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
                 if (!kEarlyB) read_b(c % kStages, f);
                 read_a(c % kStages, f);
                 reads_wait(f);
-                if (c == KB - 1 && k_tail < TBK) mask_k_tail(f);
+                // (groups of K are whole 128-token chunks: no partial chunk)
+                if (GMODE != 2 && c == KB - 1 && k_tail < TBK) mask_k_tail(f);
                 bar();
                 compute(f, c);
                 if (kEarlyB && c + 2 < KB) {
@@ -617,18 +643,18 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
                         if (OUT_BF16) {
                             const uint32_t lo = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
                             const uint32_t hi = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-                            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.c) + m * p.ldc + n) = make_uint2(lo, hi);
+                            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.c) + c_off + m * p.ldc + n) = make_uint2(lo, hi);
                         } else {
-                            *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.c) + m * p.ldc + n) = v;
+                            *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.c) + c_off + m * p.ldc + n) = v;
                         }
                     } else {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             if (n + r < N) {
                                 if (OUT_BF16)
-                                    reinterpret_cast<uint16_t*>(p.c)[m * p.ldc + n + r] = (uint16_t)bf16_rne(v[r]);
+                                    reinterpret_cast<uint16_t*>(p.c)[c_off + m * p.ldc + n + r] = (uint16_t)bf16_rne(v[r]);
                                 else
-                                    reinterpret_cast<float*>(p.c)[m * p.ldc + n + r] = v[r];
+                                    reinterpret_cast<float*>(p.c)[c_off + m * p.ldc + n + r] = v[r];
                             }
                         }
                     }
@@ -648,27 +674,40 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     wait_vm<0>();
 }
 
-template <int SA_MODE, int SB_MODE, bool B_KN, bool GROUPED = false>
+template <int SA_MODE, int SB_MODE, bool B_KN, int GMODE = 0>
 static void launch_tiles(const GemmArgs& g, bool bf, hipStream_t st)
 {
     GemmArgs a = g;
-    a.tiles_m = (int)((g.M + TBM - 1) / TBM);
+    a.tiles_m = (int)((g.M + TBM - 1) / TBM) * (GMODE == 2 ? g.G : 1);
     a.tiles_n = (int)((g.N + TBN - 1) / TBN);
-    const int tiles = a.tiles_m * a.tiles_n;
+    const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
     dim3 grid((uint32_t)(tiles < g.num_cus ? tiles : g.num_cus));
     if (bf)
-        hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, B_KN, true, GROUPED>), grid, dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, B_KN, true, GMODE>), grid, dim3(kThreads), 0, st, a);
     else
-        hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, B_KN, false, GROUPED>), grid, dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, B_KN, false, GMODE>), grid, dim3(kThreads), 0, st, a);
 }
 
-bool launch_grouped_gemm_nk(const GemmArgs& g, bool out_bf16, hipStream_t st)
+bool launch_grouped_gemm_nk(const GemmArgs& g, bool out_bf16, bool b_kn, hipStream_t st)
+{
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t b_rows = b_kn ? g.K : g.N;
+    if (g.G > kMaxLdsGroups || g.M * g.lda >= lim || (b_rows + TBK) * g.ldb >= lim ||
+        g.M * g.ldsa * 4 >= lim || g.sb_group_stride * 4 >= lim || (int64_t)g.KB * TBK >= lim)
+        return false;
+    if (b_kn) launch_tiles<SA_ROW, SB_BLOCK, true, 1>(g, out_bf16, st);
+    else launch_tiles<SA_ROW, SB_BLOCK, false, 1>(g, out_bf16, st);
+    return true;
+}
+
+bool launch_grouped_wgrad_nk(const GemmArgs& g, hipStream_t st)
 {
     const int64_t lim = (int64_t)1 << 31;
     if (g.G > kMaxLdsGroups || g.M * g.lda >= lim || (g.N + TBK) * g.ldb >= lim ||
-        g.M * g.ldsa * 4 >= lim || g.sb_group_stride * 4 >= lim || (int64_t)g.KB * TBK >= lim)
+        g.M * g.ldsa * 4 >= lim || g.N * g.ldsb * 4 >= lim || (int64_t)g.KB * TBK >= lim ||
+        (int64_t)g.G * ((g.M + TBM - 1) / TBM) >= lim)
         return false;
-    launch_tiles<SA_ROW, SB_BLOCK, false, true>(g, out_bf16, st);
+    launch_tiles<SA_ROW, SB_ROW, false, 2>(g, false, st);
     return true;
 }
 

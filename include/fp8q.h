@@ -32,9 +32,11 @@
  *    dequantization multiplier (x ~= dec(code) * s).
  *  - GEMM: C[m][n] = sum over K-chunks kb of 128 (the last may be shorter) of
  *    SA(m,kb) * SB(n,kb) * sum_{k in kb} dec(A[m][k]) * dec(B^[n][k]),
- *    products exact, fp32 partial sums, fp32 accumulator; summation order
- *    inside a chunk is the hardware's.  BF16 output is the fp32 result
- *    rounded to nearest even.
+ *    products exact, fp32 partial sums, fp32 accumulator; the summation
+ *    order inside a chunk is the hardware's, and the order in which the
+ *    chunk terms are added is unspecified (the library adds the even and the
+ *    odd chunks separately, then the two sums).  BF16 output is the fp32
+ *    result rounded to nearest even.
  *  - Inputs must be finite; NaN/Inf inputs give unspecified codes.
  *
  * Conventions for every entry point:
@@ -174,6 +176,59 @@ int fp8_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K,
                      const int32_t* group_offsets,
                      const uint8_t* b, const float* sb,
                      void* c, int64_t ldc, int c_dtype, void* stream);
+
+/*
+ * fp8_grouped_gemm_dgrad -- MoE expert dgrad over padded groups (Ling 2.0
+ * FP8 blog, "FP8 padding routing map" and "FP8 on-demand transpose weight").
+ *
+ * For each group e, rows [off[e], off[e+1]) of dY times expert weight W[e]
+ * read as stored (no transposed copy):
+ *   dX[m][k] = sum over chunks nb of 128 along n of
+ *              SA(m,nb) * SW_e(nb, k/128) * sum_{n in nb} dec(dY[m][n]) * dec(W[e][n][k])
+ * with the Numerics above (W[e]'s 128x128 block grid used transposed).
+ *  a, lda, sa, ldsa : dY codes [M_pad][N] (contiguous groups, lda >= N), 1x128
+ *                     scales along N: SA(m,nb) = sa[m*ldsa + nb], ldsa >= ceil(N/128).
+ *  group_offsets    : DEVICE int32[G+1] as for fp8_grouped_gemm.
+ *  w                : W codes [G][N][K], the forward weights as stored (row
+ *                     stride K, K % 16 == 0).
+ *  sw               : W block scales [G][ceil(N/128)][ceil(K/128)], contiguous.
+ *  c, ldc, c_dtype  : dX [M_pad][K], ldc >= K.
+ * M_pad must be a multiple of 128.  Rows outside [0, off[G]) are not written.
+ * Returns FP8Q_ERR_UNSUPPORTED (nothing enqueued) if G > 1024 or an operand
+ * spans 2 GiB or more.
+ */
+int fp8_grouped_gemm_dgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K,
+                           const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                           const int32_t* group_offsets,
+                           const uint8_t* w, const float* sw,
+                           void* c, int64_t ldc, int c_dtype, void* stream);
+
+/*
+ * fp8_grouped_gemm_wgrad -- MoE expert weight gradient over padded groups
+ * (Ling 2.0 FP8 blog, "FP8 padding routing map" and the transposed
+ * re-quantization of "grad (transpose)").
+ *
+ * For each group e, the sum over its tokens t in [off[e], off[e+1]) only:
+ *   dW[e][n][k] = sum over chunks tb of 128 tokens of
+ *                 SA(n,tb) * SB(k,tb) * sum_{t in tb} dec(dYT[n][t]) * dec(XT[k][t])
+ * with the Numerics above; a group with no rows gets dW[e] = 0.  The operands
+ * are the column outputs of fp8_quant_transpose on the padded dY and X, whose
+ * 1x128 tiles along tokens never straddle two groups because every off[e] is
+ * a multiple of 128.
+ *  a, lda, sa, ldsa : dYT codes [N][M_pad] (lda >= M_pad), SA(n,tb) = sa[n*ldsa + tb],
+ *                     ldsa >= M_pad/128.
+ *  b, ldb, sb, ldsb : XT codes [K][M_pad] (ldb >= M_pad), SB(k,tb) = sb[k*ldsb + tb],
+ *                     ldsb >= M_pad/128.
+ *  group_offsets    : DEVICE int32[G+1] as for fp8_grouped_gemm.
+ *  c, ldc           : fp32 dW [G][N][ldc] (group stride N*ldc elements), ldc >= K.
+ * M_pad must be a multiple of 128.  Returns FP8Q_ERR_UNSUPPORTED (nothing
+ * enqueued) if G > 1024 or an operand spans 2 GiB or more.
+ */
+int fp8_grouped_gemm_wgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K,
+                           const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                           const uint8_t* b, int64_t ldb, const float* sb, int64_t ldsb,
+                           const int32_t* group_offsets,
+                           float* c, int64_t ldc, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* fp8q_status_string(int status);

@@ -299,6 +299,74 @@ def grouped_gemm(a, sa, offsets, b, sb, rows=None, f64=False):
     return (out, R) if f64 else out
 
 
+def grouped_gemm_dgrad(a, sa, offsets, w, sw, rows=None, f64=False):
+    """MoE dgrad per group: rows [off[e], off[e+1]) of dY times expert weight
+    W[e] read as stored (Ling 2.0 FP8 blog, "FP8 on-demand transpose weight";
+    groups padded per "FP8 padding routing map").
+
+    ``a`` dY codes [M_pad][N] with 1x128 scales ``sa`` along N; ``w`` [G][N][K]
+    codes with 128x128 block scales ``sw`` [G][ceil(N/128)][ceil(K/128)].  The
+    contraction runs over W's rows, i.e. W[e] is the [K][N] ("KN") operand of
+    the definition with its block grid as stored.  Rows outside every group
+    produce zeros.
+    """
+    a = np.asarray(a, np.uint8)
+    off = np.asarray(offsets, np.int64)
+    G = off.size - 1
+    M = a.shape[0]
+    K = w.shape[2]
+    want = np.arange(M) if rows is None else np.asarray(rows, np.int64)
+    out = np.zeros((want.size, K), np.float64 if f64 else np.float32)
+    R = np.zeros((want.size, K), np.float64) if f64 else None
+    for e in range(G):
+        lo, hi = int(off[e]), int(off[e + 1])
+        sel = np.nonzero((want >= lo) & (want < hi))[0]
+        if sel.size == 0:
+            continue
+        res = gemm_blockscaled(a[lo:hi], np.asarray(sa)[lo:hi], "row", w[e], sw[e],
+                               "block", "KN", rows=want[sel] - lo, f64=f64)
+        if f64:
+            out[sel], R[sel] = res
+        else:
+            out[sel] = res
+    return (out, R) if f64 else out
+
+
+def grouped_gemm_wgrad(at, sat, bt, sbt, offsets, rows=None, f64=False):
+    """MoE weight gradient per group: dW[e] = sum over the group's tokens only
+    of dY^T times X (the transposed re-quantization of Ling 2.0 FP8 blog,
+    "grad (transpose)"; groups per "FP8 padding routing map").
+
+    ``at`` dY^T codes [N][M_pad] and ``bt`` X^T codes [K][M_pad], both with
+    1x128 scales along tokens (``sat`` [N][M_pad/128], ``sbt`` [K][M_pad/128]);
+    every offset is a multiple of 128, so group e's chunks are the token
+    chunks [off[e], off[e+1]) / 128.  Returns [G][len(rows) or N][K]; a group
+    with no tokens gives zeros.
+    """
+    at = np.asarray(at, np.uint8)
+    bt = np.asarray(bt, np.uint8)
+    off = np.asarray(offsets, np.int64)
+    G = off.size - 1
+    N, K = at.shape[0], bt.shape[0]
+    nr = N if rows is None else len(rows)
+    out = np.zeros((G, nr, K), np.float64 if f64 else np.float32)
+    R = np.zeros((G, nr, K), np.float64) if f64 else None
+    for e in range(G):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        assert lo % TILE == 0 and hi % TILE == 0
+        cl, ch = lo // TILE, hi // TILE
+        res = gemm_blockscaled(at[:, lo:hi], np.asarray(sat)[:, cl:ch], "row",
+                               bt[:, lo:hi], np.asarray(sbt)[:, cl:ch], "row", "NK",
+                               rows=rows, f64=f64)
+        if f64:
+            out[e], R[e] = res
+        else:
+            out[e] = res
+    return (out, R) if f64 else out
+
+
 # ---------------------------------------------------------------------------
 # output rounding and statistics
 # ---------------------------------------------------------------------------

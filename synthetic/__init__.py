@@ -158,6 +158,20 @@ def moe(T=8192, H=2048, G=128, I=768, topk=8, zipf_s=1.1, with_weights=True):
     return MoEInputs(x, counts, offsets.astype(np.int32), token_index, a, w_gu, a2, w_d)
 
 
+def moe_backward_dy(m: MoEInputs, seed: int = 406):
+    """Output gradients of the two expert GEMMs, gathered like their inputs
+    (zero pad rows): dy_gate_up [M_pad, 2I] and dy_down [M_pad, H] bf16 bits,
+    1e-3 N(0,1) with 0.1% entries x 10^U(1,3) (the backward recipe)."""
+    real = m.token_index >= 0
+    M_pad = real.size
+    n_gu, n_d = m.w_gate_up.shape[1], m.w_down.shape[1]
+    dgu = heavy_tail_f32(normal_f32((M_pad, n_gu), seed, 1e-3), 0.001, seed + 3000)
+    dd = heavy_tail_f32(normal_f32((M_pad, n_d), seed + 1, 1e-3), 0.001, seed + 3001)
+    dgu[~real] = 0
+    dd[~real] = 0
+    return bf16_from_f32(dgu), bf16_from_f32(dd)
+
+
 def long_k(M=16384, N=8192, K=8192):
     """x [M x K] bf16 exp(2u_m) z (seed 501), W [N x K] bf16 ~N(0,0.02) (seed 502)."""
     return bf16_from_f32(lognormal_rows_f32((M, K), 501)), normal_bf16((N, K), 502, 0.02)

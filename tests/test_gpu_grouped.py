@@ -1,10 +1,14 @@
-"""GPU parity of the grouped (MoE expert) GEMM, fp8_grouped_gemm.
+"""GPU parity of the grouped (MoE expert) GEMMs: fp8_grouped_gemm (forward),
+fp8_grouped_gemm_dgrad and fp8_grouped_gemm_wgrad (backward).
 
 Groups are padded with zero rows to multiples of 128 (Ling 2.0 FP8 blog,
 "FP8 padding routing map": padded rows do not change the result).  Bar as in
 the dense GEMM (1e-3 * R per element, exact zeros where R == 0), plus: every
 group equals the dense GEMM with that expert's weights, pad rows are exactly
 zero, empty groups are skipped, and rows past the last group are untouched.
+The backward: dgrad reads each expert's weight as stored and must equal the
+oracle's per-group dgrad; wgrad sums each expert's tokens only (empty groups
+give exactly 0) from the transposed re-quantization of dY and X.
 Workload: 8192 tokens, hidden 2048, 128 experts of intermediate 768, top-8
 Zipf(1.1) routing, gate/up (N=1536, K=2048) and down (N=2048, K=768).
 """
@@ -110,3 +114,127 @@ def test_moe_full_size_sampled_rows(moe_inputs, which):
     bf16_parity(cb[rows], c32[rows], co, R, oracle.f32_to_bf16_bits(c32[rows]))
     pad = m.token_index < 0
     assert np.all(c32[pad] == 0)
+
+
+def _groups(counts):
+    return np.concatenate([[0], np.cumsum([-(-c // 128) * 128 for c in counts])]).astype(np.int64)
+
+
+def _run_dgrad(a, sa, off, w, sw, out=torch.float32, c=None):
+    c = fq.fp8_grouped_gemm_dgrad(to_dev(a), to_dev(sa), to_dev(off.astype(np.int32)), to_dev(w),
+                                  to_dev(sw), out_dtype=out, c=c)
+    torch.cuda.synchronize()
+    return c
+
+
+def _run_wgrad(at, sat, bt, sbt, off, c=None):
+    c = fq.fp8_grouped_gemm_wgrad(to_dev(at), to_dev(sat), to_dev(bt), to_dev(sbt),
+                                  to_dev(off.astype(np.int32)), c=c)
+    torch.cuda.synchronize()
+    return c
+
+
+def test_dgrad_small_groups_with_empty_and_ragged():
+    counts = [100, 0, 260, 1, 0, 128]
+    G, N, K = len(counts), 300, 400          # contraction N = 300: a partial last chunk
+    off = _groups(counts)
+    M = int(off[-1])
+    A = np.zeros((M, N), np.uint8)
+    sa = np.zeros((M, 3), np.float32)
+    for e, cnt in enumerate(counts):
+        A[off[e]:off[e] + cnt] = _codes((cnt, N), 110 + e)
+        sa[off[e]:off[e] + cnt] = _scales((cnt, 3), 120 + e)
+    W = _codes((G, N, K), 130)
+    sw = _scales((G, 3, 4), 131)
+    c = host(_run_dgrad(A, sa, off, W, sw))
+    co = oracle.grouped_gemm_dgrad(A, sa, off, W, sw)
+    _, R = oracle.grouped_gemm_dgrad(A, sa, off, W, sw, f64=True)
+    gemm_parity(c, co, R)
+    cb = host(_run_dgrad(A, sa, off, W, sw, out=torch.bfloat16))
+    bf16_parity(cb, c, co, R, oracle.f32_to_bf16_bits(c))
+    for e, cnt in enumerate(counts):
+        assert np.all(c[off[e] + cnt:off[e + 1]] == 0)
+
+
+def test_dgrad_rows_past_last_group_untouched():
+    G, N, K = 2, 256, 320
+    off = np.array([0, 128, 256])
+    M_pad = 384                              # the last 128 rows belong to no group
+    A = _codes((M_pad, N), 140)
+    sa = _scales((M_pad, 2), 141)
+    W = _codes((G, N, K), 142)
+    sw = _scales((G, 2, 3), 143)
+    c = torch.full((M_pad, K), -9.0, dtype=torch.float32, device=DEV)
+    _run_dgrad(A, sa, off, W, sw, c=c)
+    ch = host(c)
+    assert np.all(ch[256:] == -9.0)
+    co = oracle.grouped_gemm_dgrad(A[:256], sa[:256], off, W, sw)
+    _, R = oracle.grouped_gemm_dgrad(A[:256], sa[:256], off, W, sw, f64=True)
+    gemm_parity(ch[:256], co, R)
+
+
+def test_wgrad_small_groups_with_empty_and_ragged():
+    counts = [200, 0, 128, 60, 1, 0]
+    G, N, K = len(counts), 150, 260
+    off = _groups(counts)
+    M = int(off[-1])
+    g = np.random.Generator(np.random.PCG64(150))
+    dy = g.standard_normal((M, N)).astype(np.float32)
+    x = g.standard_normal((M, K)).astype(np.float32) * 3
+    for e, cnt in enumerate(counts):
+        dy[off[e] + cnt:off[e + 1]] = 0
+        x[off[e] + cnt:off[e + 1]] = 0
+    at, sat = oracle.quant_1x128(np.ascontiguousarray(dy.T))
+    bt, sbt = oracle.quant_1x128(np.ascontiguousarray(x.T))
+    # output in a wider buffer: columns past K must stay untouched
+    buf = torch.full((G, N, 272), -7.0, dtype=torch.float32, device=DEV)
+    _run_wgrad(at, sat, bt, sbt, off, c=buf[:, :, :K])
+    hb = host(buf)
+    assert np.all(hb[:, :, K:] == -7.0)
+    co = oracle.grouped_gemm_wgrad(at, sat, bt, sbt, off)
+    _, R = oracle.grouped_gemm_wgrad(at, sat, bt, sbt, off, f64=True)
+    for e in range(G):
+        gemm_parity(hb[e, :, :K], co[e], R[e])
+        if counts[e] == 0:
+            assert np.all(hb[e, :, :K] == 0)
+
+
+@pytest.fixture(scope="module")
+def moe_backward(moe_inputs):
+    m, gu, dn = moe_inputs
+    dgu, dd = synthetic.moe_backward_dy(m)
+    dgu32, dd32 = synthetic.bf16_to_f32(dgu), synthetic.bf16_to_f32(dd)
+    return m, gu, dn, dgu32, dd32
+
+
+@pytest.mark.parametrize("which", ["gate_up", "down"])
+def test_moe_dgrad_full_size_sampled_rows(moe_backward, which):
+    m, gu, dn, dgu, dd = moe_backward
+    _, _, qw, sw = gu if which == "gate_up" else dn
+    qdy, sdy = oracle.quant_1x128(dgu if which == "gate_up" else dd)
+    off = m.offsets.astype(np.int64)
+    c32 = host(_run_dgrad(qdy, sdy, off, qw, sw))
+    big, small = int(np.argmax(m.counts)), int(np.argmin(m.counts))
+    rows = np.unique(np.concatenate([np.arange(off[big], off[big] + 6), np.arange(off[small], off[small] + 4),
+                                     synthetic.sample_rows(qdy.shape[0], 10, 407)]))
+    co = oracle.grouped_gemm_dgrad(qdy, sdy, off, qw, sw, rows=rows)
+    _, R = oracle.grouped_gemm_dgrad(qdy, sdy, off, qw, sw, rows=rows, f64=True)
+    gemm_parity(c32[rows], co, R)
+    assert np.all(c32[m.token_index < 0] == 0)
+
+
+@pytest.mark.parametrize("which", ["gate_up", "down"])
+def test_moe_wgrad_full_size_sampled_rows(moe_backward, which):
+    # dW_e = dY_e^T X_e over each expert's tokens; X is the expert GEMM's input
+    m, gu, dn, dgu, dd = moe_backward
+    dy = dgu if which == "gate_up" else dd
+    xin = synthetic.bf16_to_f32(m.a_gate_up if which == "gate_up" else m.a_down)
+    at, sat = oracle.quant_1x128(np.ascontiguousarray(dy.T))
+    bt, sbt = oracle.quant_1x128(np.ascontiguousarray(xin.T))
+    off = m.offsets.astype(np.int64)
+    c = host(_run_wgrad(at, sat, bt, sbt, off))
+    rows = synthetic.sample_rows(at.shape[0], 6, 408)
+    co = oracle.grouped_gemm_wgrad(at, sat, bt, sbt, off, rows=rows)
+    _, R = oracle.grouped_gemm_wgrad(at, sat, bt, sbt, off, rows=rows, f64=True)
+    for e in range(c.shape[0]):
+        gemm_parity(c[e][rows], co[e], R[e])

@@ -23,7 +23,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert names == sorted(["fp8_quant_blockwise", "fp8_quant_transpose", "fp8_gemm_blockscaled",
-                            "fp8_grouped_gemm", "fp8q_status_string"])
+                            "fp8_grouped_gemm", "fp8_grouped_gemm_dgrad", "fp8_grouped_gemm_wgrad",
+                            "fp8q_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -138,6 +139,50 @@ def test_grouped_validation():
     assert call(a7=1) == fq.ERR_SHAPE
     assert call(a3=200, a5=256, a7=2) == fq.ERR_ALIGN      # K % 16 != 0
     assert call(a8=A16 + 2) == fq.ERR_ALIGN
+
+
+def test_grouped_dgrad_validation():
+    f = L.fp8_grouped_gemm_dgrad
+    # G, M_pad, N, K, a, lda, sa, ldsa, off, w, sw, c, ldc, cdt, stream
+    base = [4, 512, 256, 256, A16, 256, A16, 2, A16, A16, A16, A16, 256, fq.BF16, None]
+    def call(**ch):
+        a = list(base)
+        for i, v in ch.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a13=4) == fq.ERR_UNSUPPORTED
+    assert call(a0=0) == fq.ERR_SHAPE
+    assert call(a1=500) == fq.ERR_SHAPE                    # M_pad not a multiple of 128
+    assert call(a1=0, a4=None) == fq.OK                    # empty output
+    assert call(a3=0, a11=None) == fq.OK
+    assert call(a8=None) == fq.ERR_NULL
+    assert call(a9=None) == fq.ERR_NULL
+    assert call(a5=200) == fq.ERR_SHAPE                    # lda < N
+    assert call(a7=1) == fq.ERR_SHAPE                      # ldsa < ceil(N/128)
+    assert call(a12=200) == fq.ERR_SHAPE                   # ldc < K
+    assert call(a3=200, a12=256) == fq.ERR_ALIGN           # K % 16 != 0 (weight row stride)
+    assert call(a8=A16 + 2) == fq.ERR_ALIGN
+
+
+def test_grouped_wgrad_validation():
+    f = L.fp8_grouped_gemm_wgrad
+    # G, M_pad, N, K, a, lda, sa, ldsa, b, ldb, sb, ldsb, off, c, ldc, stream
+    base = [4, 512, 256, 256, A16, 512, A16, 4, A16, 512, A16, 4, A16, A16, 256, None]
+    def call(**ch):
+        a = list(base)
+        for i, v in ch.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a0=0) == fq.ERR_SHAPE
+    assert call(a1=500) == fq.ERR_SHAPE                    # M_pad not a multiple of 128
+    assert call(a2=0, a13=None) == fq.OK                   # empty output
+    assert call(a12=None) == fq.ERR_NULL
+    assert call(a8=None) == fq.ERR_NULL
+    assert call(a5=400) == fq.ERR_SHAPE                    # lda < M_pad
+    assert call(a11=3) == fq.ERR_SHAPE                     # ldsb < M_pad/128
+    assert call(a14=200) == fq.ERR_SHAPE                   # ldc < K
+    assert call(a9=520) == fq.ERR_ALIGN                    # ldb % 16 != 0
+    assert call(a13=A16 + 4) == fq.ERR_ALIGN
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is present: valid fake pointers would launch")

@@ -15,7 +15,12 @@ come from": BF16 Linear -> quantize -> FP8 GEMM) with an FP32 accumulator
 * a numpy fp64 ``matmul`` per chunk (library primitive) at medium size;
 * the grouped GEMM equals the per-group dense GEMM, and zero pad rows give 0
   (Ling 2.0 FP8 blog, "FP8 padding routing map": padded rows leave the
-  result mathematically unchanged).
+  result mathematically unchanged);
+* the grouped backward (dgrad with each expert's weight read as stored, and
+  wgrad over each group's tokens only) against fp64 ``matmul`` of the
+  dequantized operands group by group, and the linearity of wgrad over
+  groups (the per-group weight gradients of a split sum to the gradient over
+  all tokens).
 """
 from fractions import Fraction
 
@@ -195,3 +200,79 @@ def test_bf16_output_rounding_matches_torch():
     x = np.concatenate([x, ties[np.isfinite(ties)]])
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(oracle.f32_to_bf16_bits(x), ref)
+
+
+def _dequant_rows(codes, scales):
+    """fp64 values of 1x128-tiled codes (exact)."""
+    d = oracle.e4m3_decode(codes).astype(np.float64)
+    return d * np.repeat(scales.astype(np.float64), 128, axis=1)[:, :d.shape[1]]
+
+
+def _dequant_blocks(codes, scales):
+    d = oracle.e4m3_decode(codes).astype(np.float64)
+    s = np.repeat(np.repeat(scales.astype(np.float64), 128, axis=0), 128, axis=1)
+    return d * s[:d.shape[0], :d.shape[1]]
+
+
+def _groups(counts):
+    padded = [-(-c // 128) * 128 for c in counts]
+    return np.concatenate([[0], np.cumsum(padded)]).astype(np.int32)
+
+
+def test_grouped_dgrad_against_dequantized_matmul():
+    # dX[rows of e] = dY[rows of e] @ W_e with W_e's blocks as stored: a
+    # transposed block grid or a swapped operand shows up as a large error
+    G, N, K = 3, 384, 200
+    counts = [130, 0, 100]
+    off = _groups(counts)
+    M = int(off[-1])
+    A = np.zeros((M, N), np.uint8)
+    SA = np.zeros((M, 3), np.float32)
+    for e in range(G):
+        A[off[e]:off[e] + counts[e]] = _codes((counts[e], N), 60 + e)
+        SA[off[e]:off[e] + counts[e]] = _scales((counts[e], 3), 70 + e)
+    W = np.stack([_codes((N, K), 80 + e) for e in range(G)])
+    SW = np.stack([_scales((3, 2), 90 + e) for e in range(G)])
+    C32 = oracle.grouped_gemm_dgrad(A, SA, off, W, SW)
+    C64, R = oracle.grouped_gemm_dgrad(A, SA, off, W, SW, f64=True)
+    for e in range(G):
+        rows = slice(int(off[e]), int(off[e + 1]))
+        if counts[e] == 0:
+            continue
+        ref = _dequant_rows(A[rows], SA[rows]) @ _dequant_blocks(W[e], SW[e])
+        assert np.allclose(C64[rows], ref, rtol=0, atol=1e-12 * max(R[rows].max(), 1e-30))
+        assert np.all(np.abs(C32[rows] - ref) <= (127 + 2 + 3) * U * R[rows] * 1.01)
+    assert np.all(C32[off[0] + counts[0]:off[1]] == 0)
+
+
+def test_grouped_wgrad_per_group_and_linearity():
+    # dW_e = dY^T[:, tokens of e] @ X[tokens of e]; an empty group is 0; the
+    # per-group gradients add up to the gradient over all tokens
+    G, N, K = 4, 150, 260
+    counts = [200, 0, 128, 60]
+    off = _groups(counts)
+    M = int(off[-1])
+    g = np.random.Generator(np.random.PCG64(7))
+    dy = g.standard_normal((M, N)).astype(np.float32)
+    x = g.standard_normal((M, K)).astype(np.float32)
+    for e in range(G):                       # pad rows are zero
+        dy[off[e] + counts[e]:off[e + 1]] = 0
+        x[off[e] + counts[e]:off[e + 1]] = 0
+    at, sat = oracle.quant_1x128(np.ascontiguousarray(dy.T))
+    bt, sbt = oracle.quant_1x128(np.ascontiguousarray(x.T))
+    C32 = oracle.grouped_gemm_wgrad(at, sat, bt, sbt, off)
+    C64, R = oracle.grouped_gemm_wgrad(at, sat, bt, sbt, off, f64=True)
+    da, db = _dequant_rows(at, sat), _dequant_rows(bt, sbt)
+    for e in range(G):
+        tok = slice(int(off[e]), int(off[e + 1]))
+        ref = da[:, tok] @ db[:, tok].T
+        if counts[e] == 0:
+            assert np.all(C32[e] == 0) and np.all(C64[e] == 0)
+            continue
+        assert np.allclose(C64[e], ref, rtol=0, atol=1e-12 * R[e].max())
+        kb = (int(off[e + 1]) - int(off[e])) // 128
+        assert np.all(np.abs(C32[e] - ref) <= (127 + 2 + kb) * U * R[e] * 1.01)
+    whole = da @ db.T
+    assert np.allclose(C64.sum(axis=0), whole, rtol=0, atol=1e-12 * R.sum(axis=0).max())
+    rows = np.array([3, 0, 149])
+    assert np.array_equal(oracle.grouped_gemm_wgrad(at, sat, bt, sbt, off, rows=rows), C32[:, rows])
