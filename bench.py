@@ -129,8 +129,10 @@ def copy_ceiling_gbs(dev):
 def moe_grouped(dev, reps=10):
     """Grouped MoE GEMMs (outside the step): 8192 tokens, hidden 2048, 128
     experts of intermediate 768, top-8 seeded Zipf(1.1) routing, groups padded
-    to 128 rows; random operands generated on the device.  TFLOP/s count the
-    real (unpadded) rows only."""
+    to 128 rows; random operands generated on the device.  For each expert
+    layer: the forward, and the backward's dgrad (expert weight read as
+    stored) and wgrad (per-expert token ranges, transposed re-quantized
+    operands, fp32 out).  TFLOP/s count the real (unpadded) rows only."""
     import torch
     import fp8_precision_quant_amd as fq
     import synthetic
@@ -145,30 +147,44 @@ def moe_grouped(dev, reps=10):
     off = torch.from_numpy(offsets.astype(np.int32)).to(dev)
     gen = torch.Generator(device=dev)
     gen.manual_seed(7)
-    out = {"tokens": T, "experts": G, "topk": topk, "real_rows": int(counts.sum()), "M_pad": M_pad}
-    for name, N, K in (("gate_up", 2 * I, H), ("down", H, I)):
-        a = torch.randn((M_pad, K), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
-        w = (0.02 * torch.randn((G * N, K), generator=gen, device=dev, dtype=torch.float32)).to(torch.bfloat16)
-        qa, sa = fq.fp8_quant_blockwise(a, fq.ROW_1x128)
-        qw, sw = fq.fp8_quant_blockwise(w, fq.BLOCK_128x128)
-        qw = qw.view(G, N, K)
-        sw = sw.view(G, -(-N // 128), -(-K // 128))
-        c = torch.empty((M_pad, N), dtype=torch.bfloat16, device=dev)
-        fq.fp8_grouped_gemm(qa, sa, off, qw, sw, c=c)
-        st = torch.cuda.current_stream(dev)
+    st = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        fn()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(st)
         for _ in range(reps):
-            fq.fp8_grouped_gemm(qa, sa, off, qw, sw, c=c)
+            fn()
         e1.record(st)
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    out = {"tokens": T, "experts": G, "topk": topk, "real_rows": int(counts.sum()), "M_pad": M_pad}
+    for name, N, K in (("gate_up", 2 * I, H), ("down", H, I)):
+        a = torch.randn((M_pad, K), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        dy = (1e-3 * torch.randn((M_pad, N), generator=gen, device=dev, dtype=torch.float32)).to(torch.bfloat16)
+        w = (0.02 * torch.randn((G * N, K), generator=gen, device=dev, dtype=torch.float32)).to(torch.bfloat16)
+        qa, sa = fq.fp8_quant_blockwise(a, fq.ROW_1x128)
+        qw, sw = fq.fp8_quant_blockwise(w, fq.BLOCK_128x128)
+        qw = qw.view(G, N, K)
+        sw = sw.view(G, -(-N // 128), -(-K // 128))
+        qdy, sdy, qdyT, sdyT = fq.fp8_quant_transpose(dy)
+        _, _, qaT, saT = fq.fp8_quant_transpose(a, rows_out=False)
+        c = torch.empty((M_pad, N), dtype=torch.bfloat16, device=dev)
+        dx = torch.empty((M_pad, K), dtype=torch.bfloat16, device=dev)
+        dw = torch.empty((G, N, K), dtype=torch.float32, device=dev)
         flops = 2.0 * counts.sum() * N * K
-        out[name] = {"N": N, "K": K, "us": round(us, 2), "TFLOP/s": round(flops / (us * 1e-6) / 1e12, 1),
-                     "frac_peak": round(flops / (us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4)}
-        del a, w, qa, sa, qw, sw, c
+        res = {"N": N, "K": K}
+        for part, fn in (("fwd", lambda: fq.fp8_grouped_gemm(qa, sa, off, qw, sw, c=c)),
+                         ("dgrad", lambda: fq.fp8_grouped_gemm_dgrad(qdy, sdy, off, qw, sw, c=dx)),
+                         ("wgrad", lambda: fq.fp8_grouped_gemm_wgrad(qdyT, sdyT, qaT, saT, off, c=dw))):
+            us = timed(fn)
+            res[part] = {"us": round(us, 2), "TFLOP/s": round(flops / (us * 1e-6) / 1e12, 1),
+                         "frac_peak": round(flops / (us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+        out[name] = res
+        del a, dy, w, qa, sa, qw, sw, qdy, sdy, qdyT, sdyT, qaT, saT, c, dx, dw
     return out
 
 

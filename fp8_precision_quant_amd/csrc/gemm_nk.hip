@@ -237,6 +237,8 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     constexpr int kSbStages = SB_MODE == SB_ROW ? 4 : kStages;
     static_assert(!(B_KN && SB_MODE == SB_ROW), "row-scaled B is [N][K] only");
     __shared__ int32_t goff[GMODE != 0 ? kMaxLdsGroups + 1 : 1];
+    // groups of K: this XCD's groups, largest first
+    __shared__ int32_t xlist[GMODE == 2 ? kMaxLdsGroups / 8 + 1 : 1];
     __shared__ __attribute__((aligned(16))) uint8_t Stg[kStages][kStageBytes];
     __shared__ __attribute__((aligned(16))) float SAs[kStages][TBM];
     // B scales of a chunk: its two 128-column blocks (block-scaled B), or its
@@ -263,7 +265,23 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     const int range_start = xcd * (T >> 3) + min(xcd, T & 7);
     const int range_len = (T >> 3) + (xcd < (T & 7) ? 1 : 0);
     const int span = kGroupM * p.tiles_n;
+    // Groups of K have very uneven K loops (the tokens routed to each
+    // expert), so there the groups are ranked by size and dealt to the XCDs
+    // in snake order (ranks 0..7 to XCDs 0..7, ranks 8..15 to XCDs 7..0,
+    // ...); each XCD's workgroups walk its groups' tiles largest group first.
+    // A group's tiles stay on one XCD, so its operands share one L2.
+    const int tiles_g = (int)((p.M + TBM - 1) / TBM);    // row tiles per group
+    const int tpg = tiles_g * p.tiles_n;                  // tiles per group
+    const int nx = GMODE == 2 ? (p.G >> 3) + (((p.G >> 3) & 1) ? (7 - xcd < (p.G & 7)) : (xcd < (p.G & 7))) : 0;
+    const int tiles_here = GMODE == 2 ? nx * tpg : range_len;
     auto tile_origin = [&](int i, int64_t& tm0, int64_t& tn0) {
+        if (GMODE == 2) {
+            const int e = xlist[i / tpg];
+            const int rem = i % tpg;
+            tm0 = (int64_t)(e * tiles_g + rem % tiles_g) * TBM;
+            tn0 = (int64_t)(rem / tiles_g) * TBN;
+            return;
+        }
         const int pid = range_start + i;
         const int group = pid / span;
         const int first_m = group * kGroupM;
@@ -273,9 +291,22 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
         tn0 = (int64_t)(idx / gsz) * TBN;
     };
     int ti = local;
-    if (ti >= range_len) return;
+    if (ti >= tiles_here) return;
     if (GMODE != 0) {
         for (int i = tid; i <= p.G; i += kThreads) goff[i] = p.offsets[i];
+        __syncthreads();
+    }
+    if (GMODE == 2) {
+        for (int e = tid; e < p.G; e += kThreads) {
+            const int size = goff[e + 1] - goff[e];
+            int rank = 0;
+            for (int f = 0; f < p.G; ++f) {
+                const int sf = goff[f + 1] - goff[f];
+                rank += (sf > size || (sf == size && f < e)) ? 1 : 0;
+            }
+            const int x = ((rank >> 3) & 1) ? 7 - (rank & 7) : (rank & 7);
+            if (x == xcd) xlist[rank >> 3] = e;
+        }
         __syncthreads();
     }
     int64_t m0, n0;
@@ -302,7 +333,6 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     // the chunks [off[e], off[e+1]) / 128 (none for an empty group).
     // (values read from LDS are made wave-uniform explicitly, so that the
     // loop bounds and addresses derived from them stay scalar)
-    const int tiles_g = (int)((M + TBM - 1) / TBM);
     auto set_group = [&](int64_t& tm0) {
         if (GMODE == 1) {
             int lo = 0, hi = p.G - 1;
@@ -595,7 +625,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
         const int64_t cm0 = m0, cn0 = n0;
         const bool store_tile = tile_live;
         ti += nwg;
-        const bool more = ti < range_len;
+        const bool more = ti < tiles_here;
         const uint32_t slot_out = lds_addr(Stg) + (uint32_t)(wave * 16384 + lane * 16);
         const uint32_t slot_in = lds_addr(Stg) + (uint32_t)(((wave + 4) & 7) * 16384 + lane * 16);
         auto finish = [&](auto half) {
