@@ -320,6 +320,30 @@ def main():
     hbm_copy = copy_ceiling_gbs(dev)
     moe = None if args.no_moe else moe_grouped(dev)
 
+    # The forward GEMM storing its output quantized (E4M3 codes + 1x128
+    # scales: the next layer's activation quantization) against the same GEMM
+    # with bf16 output followed by the separate 1x128 quantization of y.
+    qy = torch.empty((M, N), dtype=u8, device=dev)
+    sy = torch.empty((M, NB), dtype=f32, device=dev)
+    fused = {}
+    for name, fn in (
+            ("gemm_bf16_out", lambda: fq.fp8_gemm_blockscaled(qx, sx, fq.ROW_1x128, qw, sw, fq.BLOCK_128x128,
+                                                              fq.B_NK, c=y)),
+            ("quant_1x128_y", lambda: fq.fp8_quant_blockwise(y, fq.ROW_1x128, q=qy, s=sy)),
+            ("gemm_e4m3_out", lambda: fq.fp8_gemm_blockscaled_e4m3(qx, sx, fq.ROW_1x128, qw, sw, fq.BLOCK_128x128,
+                                                                   fq.B_NK, out=(qy, sy)))):
+        fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fused[name + "_us"] = round(e0.elapsed_time(e1) * 1e3 / args.steps, 2)
+    fused["saving_us"] = round(fused["gemm_bf16_out_us"] + fused["quant_1x128_y_us"] - fused["gemm_e4m3_out_us"], 2)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x_bits, w_bits, dy_bits, args.cpu_rows)
@@ -347,6 +371,7 @@ def main():
         "wall_s_timed": round(wall, 3),
         "hbm_copy_GBps": hbm_copy,
         "moe_grouped": moe,
+        "fwd_quantize_on_store": fused,
     }
     print(json.dumps(out))
 

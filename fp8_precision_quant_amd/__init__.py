@@ -42,18 +42,21 @@ _lib.fp8_gemm_blockscaled.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _int
                                       _p, _i64, _int, _p, _i64, _int, _p, _i64, _int, _p]
 _lib.fp8_grouped_gemm.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _p,
                                   _p, _p, _p, _i64, _int, _p]
+_lib.fp8_gemm_blockscaled_e4m3.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _int,
+                                           _p, _i64, _int, _p, _i64, _int, _p, _i64, _p, _i64, _p]
 _lib.fp8_grouped_gemm_dgrad.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _p,
                                         _p, _p, _p, _i64, _int, _p]
 _lib.fp8_grouped_gemm_wgrad.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _p, _i64,
                                         _p, _i64, _p, _i64, _p, _p, _i64, _p]
 for _f in ("fp8_quant_blockwise", "fp8_quant_transpose", "fp8_gemm_blockscaled",
-           "fp8_grouped_gemm", "fp8_grouped_gemm_dgrad", "fp8_grouped_gemm_wgrad"):
+           "fp8_gemm_blockscaled_e4m3", "fp8_grouped_gemm", "fp8_grouped_gemm_dgrad",
+           "fp8_grouped_gemm_wgrad"):
     getattr(_lib, _f).restype = _int
 _lib.fp8q_status_string.argtypes = [_int]
 _lib.fp8q_status_string.restype = ctypes.c_char_p
 
 SYMBOLS = ("fp8_quant_blockwise", "fp8_quant_transpose", "fp8_gemm_blockscaled",
-           "fp8_grouped_gemm", "fp8_grouped_gemm_dgrad", "fp8_grouped_gemm_wgrad",
+           "fp8_gemm_blockscaled_e4m3", "fp8_grouped_gemm", "fp8_grouped_gemm_dgrad", "fp8_grouped_gemm_wgrad",
            "fp8q_status_string")
 
 
@@ -175,6 +178,30 @@ def fp8_gemm_blockscaled(a: torch.Tensor, sa: torch.Tensor, sa_kind: int,
                                    _ptr(c), _ld(c), cd, _stream(a.device, stream))
     _check(st, "fp8_gemm_blockscaled")
     return c
+
+
+def fp8_gemm_blockscaled_e4m3(a: torch.Tensor, sa: torch.Tensor, sa_kind: int,
+                              b: torch.Tensor, sb: torch.Tensor, sb_kind: int, b_layout: int = B_NK,
+                              out: Optional[tuple] = None, stream=None):
+    """The block-scaled product stored quantized: (codes[M, N] uint8,
+    scales[M, ceil(N/128)] float32), the 1x128 quantization of the fp32
+    result along N."""
+    M, K = a.shape
+    N = b.shape[0] if b_layout == B_NK else b.shape[1]
+    if (b.shape[1] if b_layout == B_NK else b.shape[0]) != K:
+        raise ValueError("contraction sizes differ: a %s, b %s" % (tuple(a.shape), tuple(b.shape)))
+    if out is not None:
+        q, s = out
+    else:
+        q = _empty_aligned(M, N, torch.uint8, a.device, 16)
+        s = torch.empty((M, _cdiv(N, TILE)), dtype=torch.float32, device=a.device)
+    ldsa = _ld(sa) if sa.dim() == 2 else 1
+    ldsb = _ld(sb) if sb.dim() == 2 else 1
+    st = _lib.fp8_gemm_blockscaled_e4m3(M, N, K, _ptr(a), _ld(a), _ptr(sa), ldsa, sa_kind,
+                                        _ptr(b), _ld(b), b_layout, _ptr(sb), ldsb, sb_kind,
+                                        _ptr(q), _ld(q), _ptr(s), _ld(s), _stream(a.device, stream))
+    _check(st, "fp8_gemm_blockscaled_e4m3")
+    return q, s
 
 
 def fp8_grouped_gemm(a: torch.Tensor, sa: torch.Tensor, group_offsets: torch.Tensor,

@@ -125,6 +125,59 @@ int fp8_quant_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols, 
     return launch_status();
 }
 
+// Validation of the operands of a dense GEMM (everything but the output).
+// Returns FP8Q_OK, or a status; *empty is set when there is nothing to do.
+static int gemm_operands_status(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
+                                const float* sa, int64_t ldsa, int sa_kind, const uint8_t* b,
+                                int64_t ldb, int b_layout, const float* sb, int64_t ldsb, int sb_kind,
+                                bool* empty)
+{
+    *empty = false;
+    if (b_layout != FP8Q_B_NK && b_layout != FP8Q_B_KN) return FP8Q_ERR_UNSUPPORTED;
+    if (sa_kind != FP8Q_ROW_1x128 && sa_kind != FP8Q_TENSOR) return FP8Q_ERR_UNSUPPORTED;
+    if (sb_kind != FP8Q_ROW_1x128 && sb_kind != FP8Q_BLOCK_128x128 && sb_kind != FP8Q_TENSOR)
+        return FP8Q_ERR_UNSUPPORTED;
+    if (sb_kind == FP8Q_ROW_1x128 && b_layout == FP8Q_B_KN) return FP8Q_ERR_UNSUPPORTED;
+    if (M < 0 || N < 0 || K < 0) return FP8Q_ERR_SHAPE;
+    if (M == 0 || N == 0) {
+        *empty = true;
+        return FP8Q_OK;
+    }
+    if (K > 0 && (!a || !b || !sa || !sb)) return FP8Q_ERR_NULL;
+    const int64_t KB = cdiv(K, kTile);
+    if (lda < K) return FP8Q_ERR_SHAPE;
+    if (b_layout == FP8Q_B_NK ? ldb < K : ldb < N) return FP8Q_ERR_SHAPE;
+    if (sa_kind == FP8Q_ROW_1x128 && ldsa < KB) return FP8Q_ERR_SHAPE;
+    if (sb_kind == FP8Q_ROW_1x128 && ldsb < KB) return FP8Q_ERR_SHAPE;
+    if (sb_kind == FP8Q_BLOCK_128x128 && (b_layout == FP8Q_B_NK ? ldsb < KB : ldsb < cdiv(N, kTile)))
+        return FP8Q_ERR_SHAPE;
+    if (cdiv(M, 256) * cdiv(N, 128) >= kMaxIndex || KB >= kMaxIndex) return FP8Q_ERR_SHAPE;
+    if (K > 0 && (!aligned16(a) || !aligned16(b) || lda % 16 || ldb % 16)) return FP8Q_ERR_ALIGN;
+    return FP8Q_OK;
+}
+
+int fp8_gemm_blockscaled_e4m3(int64_t M, int64_t N, int64_t K,
+                              const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, int sa_kind,
+                              const uint8_t* b, int64_t ldb, int b_layout,
+                              const float* sb, int64_t ldsb, int sb_kind,
+                              uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream)
+{
+    bool empty;
+    int st = gemm_operands_status(M, N, K, a, lda, sa, ldsa, sa_kind, b, ldb, b_layout, sb, ldsb,
+                                  sb_kind, &empty);
+    if (st != FP8Q_OK || empty) return st;
+    if (sb_kind == FP8Q_ROW_1x128) return FP8Q_ERR_UNSUPPORTED;
+    if (!q || !s) return FP8Q_ERR_NULL;
+    if (ldq < N || lds < cdiv(N, kTile)) return FP8Q_ERR_SHAPE;
+    if (!aligned16(q) || ldq % 16) return FP8Q_ERR_ALIGN;
+    st = check_device();
+    if (st != FP8Q_OK) return st;
+    if (!fp8q::launch_gemm_e4m3(M, N, K, a, lda, sa, ldsa, sa_kind, b, ldb, b_layout, sb, ldsb, sb_kind,
+                                q, ldq, s, lds, static_cast<hipStream_t>(stream)))
+        return FP8Q_ERR_UNSUPPORTED;
+    return launch_status();
+}
+
 int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K,
                          const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, int sa_kind,
                          const uint8_t* b, int64_t ldb, int b_layout,

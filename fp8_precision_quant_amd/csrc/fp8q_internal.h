@@ -35,6 +35,10 @@ bool launch_grouped_gemm_wgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K, c
                                int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b,
                                int64_t ldb, const float* sb, int64_t ldsb, const int32_t* offsets,
                                float* c, int64_t ldc, hipStream_t st);
+bool launch_gemm_e4m3(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const float* sa,
+                      int64_t ldsa, int sa_kind, const uint8_t* b, int64_t ldb, int b_layout,
+                      const float* sb, int64_t ldsb, int sb_kind, uint8_t* q, int64_t ldq, float* s,
+                      int64_t lds, hipStream_t st);
 void launch_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K, const uint8_t* a,
                          int64_t lda, const float* sa, int64_t ldsa, const int32_t* offsets,
                          const uint8_t* b, const float* sb, void* c, int64_t ldc, int c_dtype,

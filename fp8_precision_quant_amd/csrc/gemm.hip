@@ -364,7 +364,7 @@ void launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
         const int sa_mode = sa_kind == FP8Q_ROW_1x128 ? SA_ROW : SA_TENSOR;
         const int sb_mode = sb_kind == FP8Q_ROW_1x128 ? SB_ROW
                           : (sb_kind == FP8Q_BLOCK_128x128 ? SB_BLOCK : SB_TENSOR);
-        if (launch_gemm_nk(g, sa_mode, sb_mode, kn, bf, st)) return;
+        if (launch_gemm_nk(g, sa_mode, sb_mode, kn, bf ? OUT_BF16 : OUT_F32, st)) return;
     }
     if (sa_kind == FP8Q_ROW_1x128) {
         if (sb_kind == FP8Q_BLOCK_128x128) {
@@ -387,6 +387,25 @@ void launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,
             else launch_typed<SA_TENSOR, SB_TENSOR, false>(g, bf, st);
         }
     }
+}
+
+bool launch_gemm_e4m3(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const float* sa,
+                      int64_t ldsa, int sa_kind, const uint8_t* b, int64_t ldb, int b_layout,
+                      const float* sb, int64_t ldsb, int sb_kind, uint8_t* q, int64_t ldq, float* s,
+                      int64_t lds, hipStream_t st)
+{
+    GemmArgs g{};
+    g.M = M; g.N = N; g.K = K;
+    g.a = a; g.lda = lda; g.sa = sa; g.ldsa = ldsa;
+    g.b = b; g.ldb = ldb; g.sb = sb; g.ldsb = ldsb;
+    g.c = q; g.ldc = ldq;
+    g.cs = s; g.ldcs = lds;
+    g.KB = (int)((K + BK - 1) / BK);
+    g.num_cus = device_cu_count();
+    const int sa_mode = sa_kind == FP8Q_ROW_1x128 ? SA_ROW : SA_TENSOR;
+    if (sb_kind == FP8Q_ROW_1x128) return false;   // row-scaled B: fp32/bf16 output only
+    const int sb_mode = sb_kind == FP8Q_BLOCK_128x128 ? SB_BLOCK : SB_TENSOR;
+    return launch_gemm_nk(g, sa_mode, sb_mode, b_layout == FP8Q_B_KN, OUT_E4M3, st);
 }
 
 void launch_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K, const uint8_t* a,

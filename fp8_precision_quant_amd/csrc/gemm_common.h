@@ -7,6 +7,8 @@ namespace fp8q {
 
 enum { SA_ROW = 0, SA_TENSOR = 2 };
 enum { SB_ROW = 0, SB_BLOCK = 1, SB_TENSOR = 2 };
+// output of the GEMM: fp32, bf16, or E4M3 codes with 1x128 scales along N
+enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_E4M3 = 2 };
 
 struct GemmArgs {
     int64_t M, N, K;
@@ -28,6 +30,8 @@ struct GemmArgs {
     int G;
     int64_t b_group_stride, sb_group_stride;
     int64_t c_group_stride;  // groups of K: elements between groups' output blocks
+    float* cs;               // E4M3 output: its 1x128 scales cs[m * ldcs + n / 128]
+    int64_t ldcs;
 };
 
 __device__ __forceinline__ uint32_t bf16_rne(float f)
@@ -54,7 +58,8 @@ __device__ __forceinline__ uint4 mask_bytes(uint4 v, int valid)
 // Launch of the LDS-DMA pipelined kernel (forward, dgrad, wgrad,
 // per-tensor); returns false if that kernel does not cover the call (the
 // caller then uses the general kernel).
-bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, bool out_bf16, hipStream_t st);
+// `out` is OUT_F32, OUT_BF16 or OUT_E4M3 (codes in c, scales in cs).
+bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, int out, hipStream_t st);
 // Grouped (MoE) launch of the same kernel: A row tiles select their expert
 // through the device group offsets (B per expert as [N][K] for the forward,
 // read as [K][N] for dgrad); false if the call is not covered.

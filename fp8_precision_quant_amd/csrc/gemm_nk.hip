@@ -231,7 +231,7 @@ __device__ __forceinline__ v4f col_scales(uint32_t a, int j)
 // group selects the expert's B and B scales); 2 groups of K (MoE weight
 // gradient: tile rows index the virtual matrix [G][M], the group's token
 // chunks are the K loop and each group has its own output block).
-template <int SA_MODE, int SB_MODE, bool B_KN, bool OUT_BF16, int GMODE>
+template <int SA_MODE, int SB_MODE, bool B_KN, int OUT, int GMODE>
 __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
 {
     constexpr int kSbStages = SB_MODE == SB_ROW ? 4 : kStages;
@@ -660,6 +660,71 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
                 asm volatile("" : "+v"(in[q2]));
                 acc[h * 4 + q2 / 4][q2 % 4] += in[q2];
             }
+            if (OUT == OUT_E4M3) {
+                // Quantize-on-store: the output's 1x128 tiles along N.  A
+                // tile is the 64 columns of this wave and those of wave ^ 1
+                // (same rows).  Columns past N are left out of the amax (with
+                // [K][N] B they are computed from bytes past the row's end).
+                float mx[4];
+                const int64_t ncol0 = cn0 + 64 * wq + 4 * kgrp;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < NNI; ++j)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (ncol0 + 16 * j + r < N) v = fmaxf(v, fabsf(acc[h * 4 + i][j][r]));
+                    v = fmaxf(v, __shfl_xor(v, 16));
+                    mx[i] = fmaxf(v, __shfl_xor(v, 32));
+                }
+                // row maxima of the two waves of a tile meet past the
+                // exchange slots in the ring
+                const uint32_t am = lds_addr(Stg) + 8u * 16384u;
+                if (kgrp == 0) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        *reinterpret_cast<__attribute__((address_space(3))) float*>(
+                            (uintptr_t)(am + (uint32_t)(wave * 64 + 16 * i + lrow) * 4)) = mx[i];
+                }
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    mx[i] = fmaxf(mx[i], *reinterpret_cast<__attribute__((address_space(3))) const float*>(
+                                             (uintptr_t)(am + (uint32_t)((wave ^ 1) * 64 + 16 * i + lrow) * 4)));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const TileScale ts = make_scale(mx[i]);
+                    uint32_t code[NNI];
+                    float v[8];
+#pragma unroll
+                    for (int jp = 0; jp < NNI / 2; ++jp) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            v[r] = acc[h * 4 + i][2 * jp][r];
+                            v[4 + r] = acc[h * 4 + i][2 * jp + 1][r];
+                        }
+                        quant8(v, ts, code[2 * jp], code[2 * jp + 1]);
+                    }
+                    const int64_t m = cm0 + 64 * h + 16 * i + lrow;
+                    if (m >= M || !store_tile) continue;
+                    uint8_t* qrow = reinterpret_cast<uint8_t*>(p.c) + m * p.ldc;
+#pragma unroll
+                    for (int j = 0; j < NNI; ++j) {
+                        const int64_t n = cn0 + 64 * wq + 16 * j + 4 * kgrp;
+                        if (n + 3 < N) {
+                            *reinterpret_cast<uint32_t*>(qrow + n) = code[j];
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (n + r < N) qrow[n + r] = (uint8_t)(code[j] >> (8 * r));
+                        }
+                    }
+                    const int64_t n_tile = cn0 + 64 * wq;
+                    if (kgrp == 0 && (wq & 1) == 0 && n_tile < N) p.cs[m * p.ldcs + n_tile / 128] = ts.s;
+                }
+                return;
+            }
             // lane l holds C[m][n .. n+3] of each kept block
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -670,7 +735,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
                     const int64_t n = cn0 + 64 * wq + 16 * j + 4 * kgrp;
                     const v4f v = acc[h * 4 + i][j];
                     if (n + 3 < N) {
-                        if (OUT_BF16) {
+                        if (OUT == OUT_BF16) {
                             const uint32_t lo = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
                             const uint32_t hi = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
                             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.c) + c_off + m * p.ldc + n) = make_uint2(lo, hi);
@@ -681,7 +746,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             if (n + r < N) {
-                                if (OUT_BF16)
+                                if (OUT == OUT_BF16)
                                     reinterpret_cast<uint16_t*>(p.c)[c_off + m * p.ldc + n + r] = (uint16_t)bf16_rne(v[r]);
                                 else
                                     reinterpret_cast<float*>(p.c)[c_off + m * p.ldc + n + r] = v[r];
@@ -704,18 +769,23 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     wait_vm<0>();
 }
 
-template <int SA_MODE, int SB_MODE, bool B_KN, int GMODE = 0>
-static void launch_tiles(const GemmArgs& g, bool bf, hipStream_t st)
+template <int SA_MODE, int SB_MODE, bool B_KN, int OUT, int GMODE = 0>
+static void launch_out(const GemmArgs& g, hipStream_t st)
 {
     GemmArgs a = g;
     a.tiles_m = (int)((g.M + TBM - 1) / TBM) * (GMODE == 2 ? g.G : 1);
     a.tiles_n = (int)((g.N + TBN - 1) / TBN);
     const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
     dim3 grid((uint32_t)(tiles < g.num_cus ? tiles : g.num_cus));
-    if (bf)
-        hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, B_KN, true, GMODE>), grid, dim3(kThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, B_KN, false, GMODE>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, B_KN, OUT, GMODE>), grid, dim3(kThreads), 0, st, a);
+}
+
+template <int SA_MODE, int SB_MODE, bool B_KN, int GMODE = 0>
+static void launch_tiles(const GemmArgs& g, int out, hipStream_t st)
+{
+    if (out == OUT_BF16) launch_out<SA_MODE, SB_MODE, B_KN, OUT_BF16, GMODE>(g, st);
+    else if (out == OUT_F32) launch_out<SA_MODE, SB_MODE, B_KN, OUT_F32, GMODE>(g, st);
+    else if constexpr (GMODE == 0 && SB_MODE != SB_ROW) launch_out<SA_MODE, SB_MODE, B_KN, OUT_E4M3, GMODE>(g, st);
 }
 
 bool launch_grouped_gemm_nk(const GemmArgs& g, bool out_bf16, bool b_kn, hipStream_t st)
@@ -725,8 +795,9 @@ bool launch_grouped_gemm_nk(const GemmArgs& g, bool out_bf16, bool b_kn, hipStre
     if (g.G > kMaxLdsGroups || g.M * g.lda >= lim || (b_rows + TBK) * g.ldb >= lim ||
         g.M * g.ldsa * 4 >= lim || g.sb_group_stride * 4 >= lim || (int64_t)g.KB * TBK >= lim)
         return false;
-    if (b_kn) launch_tiles<SA_ROW, SB_BLOCK, true, 1>(g, out_bf16, st);
-    else launch_tiles<SA_ROW, SB_BLOCK, false, 1>(g, out_bf16, st);
+    const int out = out_bf16 ? OUT_BF16 : OUT_F32;
+    if (b_kn) launch_tiles<SA_ROW, SB_BLOCK, true, 1>(g, out, st);
+    else launch_tiles<SA_ROW, SB_BLOCK, false, 1>(g, out, st);
     return true;
 }
 
@@ -737,11 +808,11 @@ bool launch_grouped_wgrad_nk(const GemmArgs& g, hipStream_t st)
         g.M * g.ldsa * 4 >= lim || g.N * g.ldsb * 4 >= lim || (int64_t)g.KB * TBK >= lim ||
         (int64_t)g.G * ((g.M + TBM - 1) / TBM) >= lim)
         return false;
-    launch_tiles<SA_ROW, SB_ROW, false, 2>(g, false, st);
+    launch_out<SA_ROW, SB_ROW, false, OUT_F32, 2>(g, st);
     return true;
 }
 
-bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, bool out_bf16, hipStream_t st)
+bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, int out, hipStream_t st)
 {
     // 32-bit buffer offsets: every operand and scale grid must span < 2 GiB
     const int64_t lim = (int64_t)1 << 31;
@@ -752,22 +823,22 @@ bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, bool
     if (b_kn) {
         if (sb_mode == SB_ROW) return false;
         if (sa_mode == SA_ROW) {
-            if (sb_mode == SB_BLOCK) launch_tiles<SA_ROW, SB_BLOCK, true>(g, out_bf16, st);
-            else launch_tiles<SA_ROW, SB_TENSOR, true>(g, out_bf16, st);
+            if (sb_mode == SB_BLOCK) launch_tiles<SA_ROW, SB_BLOCK, true>(g, out, st);
+            else launch_tiles<SA_ROW, SB_TENSOR, true>(g, out, st);
         } else {
-            if (sb_mode == SB_BLOCK) launch_tiles<SA_TENSOR, SB_BLOCK, true>(g, out_bf16, st);
-            else launch_tiles<SA_TENSOR, SB_TENSOR, true>(g, out_bf16, st);
+            if (sb_mode == SB_BLOCK) launch_tiles<SA_TENSOR, SB_BLOCK, true>(g, out, st);
+            else launch_tiles<SA_TENSOR, SB_TENSOR, true>(g, out, st);
         }
         return true;
     }
     if (sa_mode == SA_ROW) {
-        if (sb_mode == SB_BLOCK) launch_tiles<SA_ROW, SB_BLOCK, false>(g, out_bf16, st);
-        else if (sb_mode == SB_ROW) launch_tiles<SA_ROW, SB_ROW, false>(g, out_bf16, st);
-        else launch_tiles<SA_ROW, SB_TENSOR, false>(g, out_bf16, st);
+        if (sb_mode == SB_BLOCK) launch_tiles<SA_ROW, SB_BLOCK, false>(g, out, st);
+        else if (sb_mode == SB_ROW) launch_tiles<SA_ROW, SB_ROW, false>(g, out, st);
+        else launch_tiles<SA_ROW, SB_TENSOR, false>(g, out, st);
     } else {
-        if (sb_mode == SB_BLOCK) launch_tiles<SA_TENSOR, SB_BLOCK, false>(g, out_bf16, st);
-        else if (sb_mode == SB_ROW) launch_tiles<SA_TENSOR, SB_ROW, false>(g, out_bf16, st);
-        else launch_tiles<SA_TENSOR, SB_TENSOR, false>(g, out_bf16, st);
+        if (sb_mode == SB_BLOCK) launch_tiles<SA_TENSOR, SB_BLOCK, false>(g, out, st);
+        else if (sb_mode == SB_ROW) launch_tiles<SA_TENSOR, SB_ROW, false>(g, out, st);
+        else launch_tiles<SA_TENSOR, SB_TENSOR, false>(g, out, st);
     }
     return true;
 }

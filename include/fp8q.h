@@ -153,6 +153,30 @@ int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K,
                          void* c, int64_t ldc, int c_dtype, void* stream);
 
 /*
+ * fp8_gemm_blockscaled_e4m3 -- the same product, stored quantized: the
+ * output's E4M3 codes and its 1x128 scales along N (the next layer's dynamic
+ * activation quantization, Ling 2.0 FP8 blog "fine-grained quantization";
+ * "FP8-RL" article, section 一, activations quantized on the fly), with no
+ * fp32/bf16 round trip through memory.
+ *
+ * With C the fp32 result of fp8_gemm_blockscaled for the same arguments, the
+ * codes and scales are exactly those fp8_quant_blockwise(FP8Q_ROW_1x128)
+ * gives for C (see Numerics).
+ *  a .. sb_kind : as fp8_gemm_blockscaled, except that sb_kind
+ *                 FP8Q_ROW_1x128 (the weight-gradient operands, whose result
+ *                 feeds the optimizer in fp32) is FP8Q_ERR_UNSUPPORTED.
+ *  q, ldq       : codes [M][N], ldq >= N (multiple of 16, q 16-byte aligned).
+ *  s, lds       : scales s[m*lds + n/128], lds >= ceil(N/128).
+ * Returns FP8Q_ERR_UNSUPPORTED (nothing enqueued) if an operand spans 2 GiB
+ * or more.
+ */
+int fp8_gemm_blockscaled_e4m3(int64_t M, int64_t N, int64_t K,
+                              const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, int sa_kind,
+                              const uint8_t* b, int64_t ldb, int b_layout,
+                              const float* sb, int64_t ldsb, int sb_kind,
+                              uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream);
+
+/*
  * fp8_grouped_gemm -- MoE expert GEMM over padded groups.
  *
  * For each group e in [0, G): rows [off[e], off[e+1]) of A times expert

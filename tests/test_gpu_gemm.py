@@ -125,6 +125,47 @@ def test_random_codes_parity(shape, modes):
     _parity(A, sa, sa_kind, B, sb, sb_kind, layout)
 
 
+E4M3_MODES = [("row", "block", "NK"), ("row", "block", "KN"), ("tensor", "tensor", "NK"),
+              ("row", "tensor", "KN"), ("tensor", "block", "NK")]
+
+
+@pytest.mark.parametrize("shape", [(300, 200, 300), (256, 384, 512), (17, 700, 4100), (513, 129, 129)])
+@pytest.mark.parametrize("modes", E4M3_MODES)
+def test_e4m3_output_quantizes_the_fp32_result(shape, modes):
+    # the stored codes and 1x128 scales are (1) byte for byte the GPU
+    # quantizer's output on the same GEMM's fp32 result, and (2) a valid
+    # quantization of the oracle's result: each tile's s within the GEMM
+    # tolerance of its amax / 448, each dequantized code within half an E4M3
+    # step of the oracle's value plus that tolerance
+    M, N, K = shape
+    sa_kind, sb_kind, layout = modes
+    seed = M * 13 + N * 5 + K + 7
+    A = _codes((M, K), seed)
+    B = _codes((N, K) if layout == "NK" else (K, N), seed + 1)
+    sa = _scales((M, -(-K // 128)) if sa_kind == "row" else (1, 1), seed + 2)
+    sb = _scales(_b_scale_shape(sb_kind, layout, N, K), seed + 3)
+    q, qs = fq.fp8_gemm_blockscaled_e4m3(to_dev(A), to_dev(sa), KIND[sa_kind], to_dev(B), to_dev(sb),
+                                         KIND[sb_kind], LAYOUT[layout])
+    c = fq.fp8_gemm_blockscaled(to_dev(A), to_dev(sa), KIND[sa_kind], to_dev(B), to_dev(sb),
+                                KIND[sb_kind], LAYOUT[layout], out_dtype=torch.float32)
+    rq, rs = fq.fp8_quant_blockwise(c, fq.ROW_1x128)
+    torch.cuda.synchronize()
+    q, qs, rq, rs = host(q), host(qs), host(rq), host(rs)
+    assert np.array_equal(q, rq)
+    assert np.array_equal(qs.view(np.uint32), rs.view(np.uint32))
+    co = oracle.gemm_blockscaled(A, sa, sa_kind, B, sb, sb_kind, layout).astype(np.float64)
+    _, R = oracle.gemm_blockscaled(A, sa, sa_kind, B, sb, sb_kind, layout, f64=True)
+    NB = -(-N // 128)
+    pad = NB * 128 - N
+    amax_o = np.abs(np.pad(co, ((0, 0), (0, pad)))).reshape(M, NB, 128).max(axis=2)
+    tol_t = 1e-3 * np.pad(R, ((0, 0), (0, pad))).reshape(M, NB, 128).max(axis=2)
+    assert np.all(np.abs(qs.astype(np.float64) * 448 - amax_o) <= tol_t * 1.0001 + 1e-30)
+    s_full = np.repeat(qs.astype(np.float64), 128, axis=1)[:, :N]
+    deq = oracle.e4m3_decode(q).astype(np.float64) * s_full
+    half_step = np.maximum(np.abs(co) * 2.0 ** -4, s_full * 2.0 ** -10)
+    assert np.all(np.abs(deq - co) <= half_step * 1.0001 + 1e-3 * R * 2 + 1e-30)
+
+
 def test_k_zero_and_empty():
     a = torch.zeros((5, 16), dtype=torch.uint8, device=DEV)[:, :0]      # K = 0, lda = 16
     b = torch.zeros((7, 16), dtype=torch.uint8, device=DEV)[:, :0]

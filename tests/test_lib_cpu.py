@@ -23,7 +23,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert names == sorted(["fp8_quant_blockwise", "fp8_quant_transpose", "fp8_gemm_blockscaled",
-                            "fp8_grouped_gemm", "fp8_grouped_gemm_dgrad", "fp8_grouped_gemm_wgrad",
+                            "fp8_gemm_blockscaled_e4m3", "fp8_grouped_gemm", "fp8_grouped_gemm_dgrad", "fp8_grouped_gemm_wgrad",
                             "fp8q_status_string"])
 
 
@@ -139,6 +139,31 @@ def test_grouped_validation():
     assert call(a7=1) == fq.ERR_SHAPE
     assert call(a3=200, a5=256, a7=2) == fq.ERR_ALIGN      # K % 16 != 0
     assert call(a8=A16 + 2) == fq.ERR_ALIGN
+
+
+def test_gemm_e4m3_validation():
+    f = L.fp8_gemm_blockscaled_e4m3
+    # M, N, K, a, lda, sa, ldsa, sa_kind, b, ldb, layout, sb, ldsb, sb_kind, q, ldq, s, lds, stream
+    base = [256, 256, 512, A16, 512, A16, 4, fq.ROW_1x128, A16, 512, fq.B_NK, A16, 4,
+            fq.BLOCK_128x128, A16, 256, A16, 2, None]
+    def call(**ch):
+        a = list(base)
+        for i, v in ch.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a10=2) == fq.ERR_UNSUPPORTED
+    assert call(a13=fq.ROW_1x128, a10=fq.B_KN, a9=256) == fq.ERR_UNSUPPORTED
+    assert call(a13=fq.ROW_1x128) == fq.ERR_UNSUPPORTED    # row-scaled B: not stored as E4M3
+    assert call(a1=0, a14=None) == fq.OK                   # empty output
+    assert call(a14=None) == fq.ERR_NULL
+    assert call(a16=None) == fq.ERR_NULL
+    assert call(a3=None) == fq.ERR_NULL
+    assert call(a15=200) == fq.ERR_SHAPE                   # ldq < N
+    assert call(a17=1) == fq.ERR_SHAPE                     # lds < ceil(N/128)
+    assert call(a6=3) == fq.ERR_SHAPE
+    assert call(a15=264) == fq.ERR_ALIGN                   # ldq % 16 != 0
+    assert call(a14=A16 + 1) == fq.ERR_ALIGN
+    assert call(a3=MIS) == fq.ERR_ALIGN
 
 
 def test_grouped_dgrad_validation():
