@@ -65,6 +65,10 @@ def lib() -> ctypes.CDLL:
             L.orc_decode_array.argtypes = [p, i64, p]
             L.orc_encode_array.argtypes = [p, i64, p]
             L.orc_quant_tiles.argtypes = [p, i64, i64, i64, i64, p, p]
+            L.orc_quant_tiles_pow2.argtypes = [p, i64, i64, i64, i64, p, p]
+            L.orc_pow2_exponent.argtypes = [ctypes.c_float]
+            L.orc_pow2_exponent.restype = ctypes.c_int
+            L.orc_e8m0_decode_array.argtypes = [p, i64, p]
             L.orc_gemm_f32.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p]
             L.orc_gemm_f64.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p, p]
             L.orc_f32_to_bf16.argtypes = [p, i64, p]
@@ -156,6 +160,60 @@ def quant_transpose(x):
 
 def quantize(x, kind: str):
     return {"row": quant_1x128, "block": quant_128x128, "tensor": quant_tensor}[kind](x)
+
+
+# ---------------------------------------------------------------------------
+# power-of-two (E8M0) scales: the micro-scaling variant of block scaling
+# (Introl FP8 infrastructure guide, scaling strategies and the Blackwell
+# section: MXFP8 block scales applied by the hardware).  Reading: the same
+# tiles, s = 2^e with e the smallest integer >= -126 such that amax <= 448 2^e,
+# stored as the byte e + 127.
+# ---------------------------------------------------------------------------
+
+def pow2_exponent(amax: float) -> int:
+    """e of one tile from its fp32 amax."""
+    return int(lib().orc_pow2_exponent(float(np.float32(amax))))
+
+
+def e8m0_decode(b) -> np.ndarray:
+    """E8M0 bytes -> fp32 2^(b-127) (NaN for 255)."""
+    b = _c(b, np.uint8)
+    out = np.empty(b.shape, np.float32)
+    lib().orc_e8m0_decode_array(_ptr(b), b.size, _ptr(out))
+    return out
+
+
+def quant_tiles_pow2(x, tile_rows: int, tile_cols: int):
+    """Like ``quant_tiles`` with power-of-two scales.
+
+    Returns ``(q uint8[R, C], e uint8[ceil(R/tr), ceil(C/tc)])``, ``e`` the
+    E8M0 scale bytes.
+    """
+    x = _c(x, np.float32)
+    assert x.ndim == 2
+    R, C = x.shape
+    q = np.empty((R, C), np.uint8)
+    e = np.empty((-(-R // tile_rows), -(-C // tile_cols)), np.uint8)
+    if R and C:
+        lib().orc_quant_tiles_pow2(_ptr(x), R, C, tile_rows, tile_cols, _ptr(q), _ptr(e))
+    return q, e
+
+
+def quant_1x128_pow2(x):
+    return quant_tiles_pow2(x, 1, TILE)
+
+
+def quant_128x128_pow2(x):
+    return quant_tiles_pow2(x, TILE, TILE)
+
+
+def quant_transpose_pow2(x):
+    """Row tiles of X and of X^T with power-of-two scales:
+    ``(q_row, e_row, q_colT, e_colT)``."""
+    x = _c(x, np.float32)
+    q_row, e_row = quant_1x128_pow2(x)
+    q_colT, e_colT = quant_1x128_pow2(np.ascontiguousarray(x.T))
+    return q_row, e_row, q_colT, e_colT
 
 
 # ---------------------------------------------------------------------------

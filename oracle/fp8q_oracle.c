@@ -174,6 +174,66 @@ void orc_quant_tiles(const float* x, int64_t rows, int64_t cols, int64_t tr,
     }
 }
 
+/* Power-of-two scales, the micro-scaling variant of block scaling
+ * (Introl FP8 infrastructure guide, section on scaling strategies: Blackwell's
+ * MXFP8 gives each block of a tensor its own scale factor; its Blackwell
+ * section: the block scaling is done in hardware).  The pages do not say how
+ * the block scale is chosen or stored; the reading taken here keeps the tile
+ * shapes above and restricts s to a power of two 2^e, stored as the 8-bit
+ * exponent byte e + 127 (E8M0), with
+ *   e = the smallest integer >= -126 such that amax <= 448 * 2^e,
+ * i.e. s = 2^ceil(log2(amax / 448)) taken without rounding, so that no value
+ * of the tile saturates, and amax = 0 gives e = -126.  The comparison is made
+ * in double, where 448 * 2^e and every fp32 amax are exact.  Codes are
+ * encode(fp32(x / 2^e)); the quotient is exact unless it is below 2^-126,
+ * where every code is a signed zero anyway. */
+int orc_pow2_exponent(float amax)
+{
+    int e = -126;
+    if ((double)amax > 448.0 * ldexp(1.0, e)) {
+        int k;
+        frexp((double)amax, &k);            /* amax = f * 2^k, 0.5 <= f < 1 */
+        e = k - 10;                         /* 448 * 2^(k-10) < 2^(k-1) <= amax */
+        while ((double)amax > 448.0 * ldexp(1.0, e))
+            e++;
+    }
+    return e;
+}
+
+void orc_quant_tiles_pow2(const float* x, int64_t rows, int64_t cols, int64_t tr,
+                          int64_t tc, uint8_t* q, uint8_t* ebyte)
+{
+    int64_t tiles_r = (rows + tr - 1) / tr;
+    int64_t tiles_c = (cols + tc - 1) / tc;
+#pragma omp parallel for collapse(2) schedule(dynamic, 16)
+    for (int64_t ti = 0; ti < tiles_r; ++ti) {
+        for (int64_t tj = 0; tj < tiles_c; ++tj) {
+            int64_t r0 = ti * tr, r1 = r0 + tr < rows ? r0 + tr : rows;
+            int64_t c0 = tj * tc, c1 = c0 + tc < cols ? c0 + tc : cols;
+            float amax = 0.0f;
+            for (int64_t r = r0; r < r1; ++r)
+                for (int64_t c = c0; c < c1; ++c) {
+                    float a = fabsf(x[r * cols + c]);
+                    if (a > amax)
+                        amax = a;
+                }
+            int e = orc_pow2_exponent(amax);
+            ebyte[ti * tiles_c + tj] = (uint8_t)(e + 127);
+            float scale = ldexpf(1.0f, e);
+            for (int64_t r = r0; r < r1; ++r)
+                for (int64_t c = c0; c < c1; ++c)
+                    q[r * cols + c] = orc_e4m3_encode(x[r * cols + c] / scale);
+        }
+    }
+}
+
+/* E8M0 byte -> its power of two as fp32 (2^(b-127); byte 255 is NaN). */
+void orc_e8m0_decode_array(const uint8_t* b, int64_t n, float* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = b[i] == 255 ? NAN : (float)ldexp(1.0, (int)b[i] - 127);
+}
+
 /* ------------------------------------------------------------------ */
 /* Block-scaled GEMM                                                    */
 /* ------------------------------------------------------------------ */
