@@ -344,6 +344,61 @@ def main():
         fused[name + "_us"] = round(e0.elapsed_time(e1) * 1e3 / args.steps, 2)
     fused["saving_us"] = round(fused["gemm_bf16_out_us"] + fused["quant_1x128_y_us"] - fused["gemm_e4m3_out_us"], 2)
 
+    # The same step with power-of-two scales (E8M0 bytes; the scaled MFMA
+    # applies them): per-launch times of each kernel.
+    def e8(rows, cols):
+        return torch.empty((rows, (cols + 3) // 4 * 4), dtype=u8, device=dev)[:, :cols]
+    ex, ew, edy, edyT, exT = e8(M, KB), e8(NB, KB), e8(M, NB), e8(N, MB), e8(K, MB)
+    p2_ops = [
+        ("quant_1x128 x", lambda: fq.fp8_quant_blockwise_e8m0(x, fq.ROW_1x128, q=qx, e=ex),
+         M * K * 2 + M * K + M * KB),
+        ("quant_128x128 W", lambda: fq.fp8_quant_blockwise_e8m0(w, fq.BLOCK_128x128, q=qw, e=ew),
+         N * K * 2 + N * K + NB * KB),
+        ("gemm fwd y=xW^T", lambda: fq.fp8_gemm_e8m0(qx, ex, qw, ew, fq.BLOCK_128x128, fq.B_NK, c=y), None),
+        ("quant_transpose dy", lambda: fq.fp8_quant_transpose_e8m0(dy, out=(qdy, edy, qdyT, edyT)),
+         M * N * 2 + 2 * M * N + M * NB + N * MB),
+        ("quant_transpose x (columns)", lambda: fq.fp8_quant_transpose_e8m0(
+            x, rows_out=False, out=(None, None, qxT, exT)), M * K * 2 + M * K + K * MB),
+        ("gemm dgrad dx=dyW", lambda: fq.fp8_gemm_e8m0(qdy, edy, qw, ew, fq.BLOCK_128x128, fq.B_KN, c=dx), None),
+        ("gemm wgrad dW=dy^T x", lambda: fq.fp8_gemm_e8m0(qdyT, edyT, qxT, exT, fq.ROW_1x128, fq.B_NK, c=dW),
+         None),
+    ]
+    # timed like the main step: K whole steps between two events, then K
+    # steps with an event pair around every launch
+    for _ in range(args.warmup):
+        for _, fn, _ in p2_ops:
+            fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        for _, fn, _ in p2_ops:
+            fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    p2_step_ms = e0.elapsed_time(e1) / args.steps
+    ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(len(p2_ops) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for st_i in range(args.steps):
+        ev2[st_i][0].record(stream)
+        for i, (_, fn, _) in enumerate(p2_ops):
+            fn()
+            ev2[st_i][i + 1].record(stream)
+    torch.cuda.synchronize()
+    pow2 = {"ms_per_step": round(p2_step_ms, 4),
+            "TFLOP/s": round(step_flops / (p2_step_ms * 1e-3) / 1e12, 2), "kernels": []}
+    for i, (name, _, hbm_bytes) in enumerate(p2_ops):
+        us = sum(ev2[st_i][i].elapsed_time(ev2[st_i][i + 1]) for st_i in range(args.steps)) * 1e3 / args.steps
+        rec = {"kernel": name, "us": round(us, 2)}
+        if name.startswith("gemm"):
+            rec["TFLOP/s"] = round(gemm_flops / (us * 1e-6) / 1e12, 1)
+            rec["frac_peak"] = round(gemm_flops / (us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS, 4)
+        else:
+            rec["GB/s"] = round(hbm_bytes / (us * 1e-6) / 1e9, 1)
+            rec["frac_peak"] = round(hbm_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+        pow2["kernels"].append(rec)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x_bits, w_bits, dy_bits, args.cpu_rows)
@@ -372,6 +427,7 @@ def main():
         "hbm_copy_GBps": hbm_copy,
         "moe_grouped": moe,
         "fwd_quantize_on_store": fused,
+        "pow2_scales": pow2,
     }
     print(json.dumps(out))
 

@@ -7,7 +7,9 @@ of the computation runs in the HIP kernels.  There is no fallback: if the
 library is missing the import of this module raises.
 
 Codes are ``torch.uint8`` tensors holding OCP E4M3FN bytes (view them as
-``torch.float8_e4m3fn`` if desired); scales are ``torch.float32``.
+``torch.float8_e4m3fn`` if desired); scales are ``torch.float32``, or, for
+the ``*_e8m0`` functions, ``torch.uint8`` E8M0 exponent bytes of power-of-two
+scales (2^(byte - 127)) whose row stride is a multiple of 4.
 """
 from __future__ import annotations
 
@@ -48,15 +50,22 @@ _lib.fp8_grouped_gemm_dgrad.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _p, _i
                                         _p, _p, _p, _i64, _int, _p]
 _lib.fp8_grouped_gemm_wgrad.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _p, _i64,
                                         _p, _i64, _p, _i64, _p, _p, _i64, _p]
+_lib.fp8_quant_blockwise_e8m0.argtypes = [_p, _int, _i64, _i64, _i64, _int, _p, _i64, _p, _i64, _p]
+_lib.fp8_quant_transpose_e8m0.argtypes = [_p, _int, _i64, _i64, _i64,
+                                          _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
+_lib.fp8_gemm_e8m0.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64,
+                               _p, _i64, _int, _p, _i64, _int, _p, _i64, _int, _p]
 for _f in ("fp8_quant_blockwise", "fp8_quant_transpose", "fp8_gemm_blockscaled",
            "fp8_gemm_blockscaled_e4m3", "fp8_grouped_gemm", "fp8_grouped_gemm_dgrad",
-           "fp8_grouped_gemm_wgrad"):
+           "fp8_grouped_gemm_wgrad", "fp8_quant_blockwise_e8m0", "fp8_quant_transpose_e8m0",
+           "fp8_gemm_e8m0"):
     getattr(_lib, _f).restype = _int
 _lib.fp8q_status_string.argtypes = [_int]
 _lib.fp8q_status_string.restype = ctypes.c_char_p
 
 SYMBOLS = ("fp8_quant_blockwise", "fp8_quant_transpose", "fp8_gemm_blockscaled",
            "fp8_gemm_blockscaled_e4m3", "fp8_grouped_gemm", "fp8_grouped_gemm_dgrad", "fp8_grouped_gemm_wgrad",
+           "fp8_quant_blockwise_e8m0", "fp8_quant_transpose_e8m0", "fp8_gemm_e8m0",
            "fp8q_status_string")
 
 
@@ -154,6 +163,77 @@ def fp8_quant_transpose(x: torch.Tensor, rows_out: bool = True, cols_out: bool =
         _stream(x.device, stream))
     _check(st, "fp8_quant_transpose")
     return q_row, s_row, q_colT, s_colT
+
+
+# ---------------------------------------------------------------------------
+# power-of-two (E8M0) scales
+# ---------------------------------------------------------------------------
+
+def fp8_quant_blockwise_e8m0(x: torch.Tensor, kind: int = ROW_1x128, q: Optional[torch.Tensor] = None,
+                             e: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Quantize ``x[rows, cols]`` with power-of-two tile scales: (codes,
+    E8M0 bytes ``e``).  ``kind`` ROW_1x128 -> e[rows, ceil(cols/128)];
+    BLOCK_128x128 -> e[ceil(rows/128), ceil(cols/128)] (row stride rounded up
+    to 4 bytes, as the GEMM reads it)."""
+    rows, cols = x.shape
+    if q is None:
+        q = _empty_aligned(rows, cols, torch.uint8, x.device, 16)
+    if e is None:
+        r = rows if kind == ROW_1x128 else _cdiv(rows, TILE)
+        e = _empty_aligned(r, _cdiv(cols, TILE), torch.uint8, x.device, 4)
+    st = _lib.fp8_quant_blockwise_e8m0(_ptr(x), _dtype_code(x), rows, cols, _ld(x), kind,
+                                       _ptr(q), _ld(q), _ptr(e), _ld(e), _stream(x.device, stream))
+    _check(st, "fp8_quant_blockwise_e8m0")
+    return q, e
+
+
+def fp8_quant_transpose_e8m0(x: torch.Tensor, rows_out: bool = True, cols_out: bool = True,
+                             out: Optional[tuple] = None, stream=None):
+    """``fp8_quant_transpose`` with power-of-two scales: (q_row, e_row,
+    q_colT, e_colT), the ``e`` grids uint8 E8M0 bytes."""
+    R, C = x.shape
+    if out is not None:
+        q_row, e_row, q_colT, e_colT = out
+    else:
+        q_row = _empty_aligned(R, C, torch.uint8, x.device, 16) if rows_out else None
+        e_row = _empty_aligned(R, _cdiv(C, TILE), torch.uint8, x.device, 4) if rows_out else None
+        q_colT = _empty_aligned(C, R, torch.uint8, x.device, 16) if cols_out else None
+        e_colT = _empty_aligned(C, _cdiv(R, TILE), torch.uint8, x.device, 4) if cols_out else None
+    st = _lib.fp8_quant_transpose_e8m0(
+        _ptr(x), _dtype_code(x), R, C, _ld(x),
+        _ptr(q_row), _ld(q_row) if q_row is not None else 0,
+        _ptr(e_row), _ld(e_row) if e_row is not None else 0,
+        _ptr(q_colT), _ld(q_colT) if q_colT is not None else 0,
+        _ptr(e_colT), _ld(e_colT) if e_colT is not None else 0,
+        _stream(x.device, stream))
+    _check(st, "fp8_quant_transpose_e8m0")
+    return q_row, e_row, q_colT, e_colT
+
+
+def fp8_gemm_e8m0(a: torch.Tensor, ea: torch.Tensor, b: torch.Tensor, eb: torch.Tensor,
+                  eb_kind: int = BLOCK_128x128, b_layout: int = B_NK,
+                  out_dtype: torch.dtype = torch.bfloat16, c: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """C[M, N] = block-scaled product with power-of-two scales: ``a[M, K]``
+    codes with 1x128 E8M0 row scales ``ea``; ``b`` codes (``[N, K]`` for
+    B_NK, ``[K, N]`` for B_KN) with E8M0 scales ``eb`` of ``eb_kind``
+    (BLOCK_128x128, or ROW_1x128 for B_NK)."""
+    M, K = a.shape
+    N = b.shape[0] if b_layout == B_NK else b.shape[1]
+    if (b.shape[1] if b_layout == B_NK else b.shape[0]) != K:
+        raise ValueError("contraction sizes differ: a %s, b %s" % (tuple(a.shape), tuple(b.shape)))
+    if ea.dtype != torch.uint8 or eb.dtype != torch.uint8:
+        raise ValueError("E8M0 scales must be uint8 tensors")
+    if c is None:
+        c = _empty_aligned(M, N, out_dtype, a.device, 16 // (4 if out_dtype == torch.float32 else 2))
+    if c.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("output dtype must be float32 or bfloat16")
+    cd = F32 if c.dtype == torch.float32 else BF16
+    st = _lib.fp8_gemm_e8m0(M, N, K, _ptr(a), _ld(a), _ptr(ea), _ld(ea),
+                            _ptr(b), _ld(b), b_layout, _ptr(eb), _ld(eb), eb_kind,
+                            _ptr(c), _ld(c), cd, _stream(a.device, stream))
+    _check(st, "fp8_gemm_e8m0")
+    return c
 
 
 def fp8_gemm_blockscaled(a: torch.Tensor, sa: torch.Tensor, sa_kind: int,

@@ -125,6 +125,92 @@ int fp8_quant_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols, 
     return launch_status();
 }
 
+int fp8_quant_blockwise_e8m0(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                             int kind, uint8_t* q, int64_t ldq, uint8_t* e, int64_t lde, void* stream)
+{
+    if (!dtype_ok(x_dtype)) return FP8Q_ERR_UNSUPPORTED;
+    if (kind != FP8Q_ROW_1x128 && kind != FP8Q_BLOCK_128x128) return FP8Q_ERR_UNSUPPORTED;
+    if (rows < 0 || cols < 0) return FP8Q_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return FP8Q_OK;
+    if (!x || !q || !e) return FP8Q_ERR_NULL;
+    const int64_t tiles_c = cdiv(cols, kTile);
+    if (ldx < cols || ldq < cols || lde < tiles_c) return FP8Q_ERR_SHAPE;
+    if (kind == FP8Q_ROW_1x128 && rows * tiles_c >= kMaxIndex) return FP8Q_ERR_SHAPE;
+    if (kind == FP8Q_BLOCK_128x128 && cdiv(rows, kTile) * tiles_c >= kMaxIndex) return FP8Q_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(q) || (ldx * elem_size(x_dtype)) % 16 || ldq % 16)
+        return FP8Q_ERR_ALIGN;
+    int st = check_device();
+    if (st != FP8Q_OK) return st;
+    fp8q::launch_quant_blockwise_e8m0(x, x_dtype, rows, cols, ldx, kind, q, ldq, e, lde,
+                                      static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+int fp8_quant_transpose_e8m0(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                             uint8_t* q_row, int64_t ldq_row, uint8_t* e_row, int64_t lde_row,
+                             uint8_t* q_colT, int64_t ldq_colT, uint8_t* e_colT, int64_t lde_colT,
+                             void* stream)
+{
+    if (!dtype_ok(x_dtype)) return FP8Q_ERR_UNSUPPORTED;
+    if (rows < 0 || cols < 0) return FP8Q_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return FP8Q_OK;
+    const bool want_row = q_row || e_row;
+    const bool want_col = q_colT || e_colT;
+    if (!x) return FP8Q_ERR_NULL;
+    if (want_row && (!q_row || !e_row)) return FP8Q_ERR_NULL;
+    if (want_col && (!q_colT || !e_colT)) return FP8Q_ERR_NULL;
+    if (!want_row && !want_col) return FP8Q_OK;
+    if (ldx < cols) return FP8Q_ERR_SHAPE;
+    if (want_row && (ldq_row < cols || lde_row < cdiv(cols, kTile))) return FP8Q_ERR_SHAPE;
+    if (want_col && (ldq_colT < rows || lde_colT < cdiv(rows, kTile))) return FP8Q_ERR_SHAPE;
+    if (cdiv(rows, kTile) > kMaxGridY || cdiv(rows, kTile) * cdiv(cols, kTile) >= kMaxIndex) return FP8Q_ERR_SHAPE;
+    if (!aligned16(x) || (ldx * elem_size(x_dtype)) % 16) return FP8Q_ERR_ALIGN;
+    if (want_row && (!aligned16(q_row) || ldq_row % 16)) return FP8Q_ERR_ALIGN;
+    if (want_col && (!aligned16(q_colT) || ldq_colT % 16)) return FP8Q_ERR_ALIGN;
+    int st = check_device();
+    if (st != FP8Q_OK) return st;
+    fp8q::launch_quant_transpose_e8m0(x, x_dtype, rows, cols, ldx, want_row ? q_row : nullptr, ldq_row,
+                                      e_row, lde_row, want_col ? q_colT : nullptr, ldq_colT, e_colT,
+                                      lde_colT, static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+int fp8_gemm_e8m0(int64_t M, int64_t N, int64_t K,
+                  const uint8_t* a, int64_t lda, const uint8_t* ea, int64_t ldea,
+                  const uint8_t* b, int64_t ldb, int b_layout,
+                  const uint8_t* eb, int64_t ldeb, int eb_kind,
+                  void* c, int64_t ldc, int c_dtype, void* stream)
+{
+    if (!dtype_ok(c_dtype)) return FP8Q_ERR_UNSUPPORTED;
+    if (b_layout != FP8Q_B_NK && b_layout != FP8Q_B_KN) return FP8Q_ERR_UNSUPPORTED;
+    if (eb_kind != FP8Q_ROW_1x128 && eb_kind != FP8Q_BLOCK_128x128) return FP8Q_ERR_UNSUPPORTED;
+    if (eb_kind == FP8Q_ROW_1x128 && b_layout == FP8Q_B_KN) return FP8Q_ERR_UNSUPPORTED;
+    if (M < 0 || N < 0 || K < 0) return FP8Q_ERR_SHAPE;
+    if (M == 0 || N == 0) return FP8Q_OK;
+    if (!c) return FP8Q_ERR_NULL;
+    if (K > 0 && (!a || !b || !ea || !eb)) return FP8Q_ERR_NULL;
+    const int64_t KB = cdiv(K, kTile);
+    if (lda < K || ldc < N) return FP8Q_ERR_SHAPE;
+    if (b_layout == FP8Q_B_NK ? ldb < K : ldb < N) return FP8Q_ERR_SHAPE;
+    if (ldea < KB) return FP8Q_ERR_SHAPE;
+    if (eb_kind == FP8Q_ROW_1x128 && ldeb < KB) return FP8Q_ERR_SHAPE;
+    if (eb_kind == FP8Q_BLOCK_128x128 && (b_layout == FP8Q_B_NK ? ldeb < KB : ldeb < cdiv(N, kTile)))
+        return FP8Q_ERR_SHAPE;
+    if (cdiv(M, 256) * cdiv(N, 128) >= kMaxIndex || KB >= kMaxIndex) return FP8Q_ERR_SHAPE;
+    if (K > 0 && (!aligned16(a) || !aligned16(b) || lda % 16 || ldb % 16)) return FP8Q_ERR_ALIGN;
+    // the kernel reads each scale row as 4-byte words
+    if (K > 0 && ((reinterpret_cast<uintptr_t>(ea) & 3u) || (reinterpret_cast<uintptr_t>(eb) & 3u) ||
+                  ldea % 4 || ldeb % 4))
+        return FP8Q_ERR_ALIGN;
+    if (!aligned16(c) || (ldc * elem_size(c_dtype)) % 16) return FP8Q_ERR_ALIGN;
+    int st = check_device();
+    if (st != FP8Q_OK) return st;
+    if (!fp8q::launch_gemm_e8m0(M, N, K, a, lda, ea, ldea, b, ldb, b_layout, eb, ldeb, eb_kind, c, ldc,
+                                c_dtype, static_cast<hipStream_t>(stream)))
+        return FP8Q_ERR_UNSUPPORTED;
+    return launch_status();
+}
+
 // Validation of the operands of a dense GEMM (everything but the output).
 // Returns FP8Q_OK, or a status; *empty is set when there is nothing to do.
 static int gemm_operands_status(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda,

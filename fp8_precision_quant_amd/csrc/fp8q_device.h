@@ -39,7 +39,8 @@ __device__ __forceinline__ float dpp_max16(float v)
 struct TileScale {
     float s;
     float y;
-    int mode;   // 0: s == 0 (signed zeros), 1: corrected reciprocal, 2: IEEE quotient
+    int mode;   // 0: s == 0 (signed zeros), 1: corrected reciprocal, 2: IEEE quotient,
+                // 3: power of two (x * y is exact)
 };
 
 __device__ __forceinline__ TileScale make_scale(float amax)
@@ -110,6 +111,54 @@ __device__ __forceinline__ void quant8(const float v[8], const TileScale& t, uin
     } else {
         lo = quant4(v[0], v[1], v[2], v[3], t);
         hi = quant4(v[4], v[5], v[6], v[7], t);
+    }
+}
+
+// Power-of-two scales, stored as E8M0 exponent bytes (the micro-scaling
+// variant of block scaling; Introl FP8 infrastructure guide, scaling
+// strategies and the Blackwell section).  s = 2^e with e the smallest integer
+// >= -126 such that amax <= 448 * 2^e.  With amax = m * 2^k (1 <= m < 2) and
+// 448 = 1.75 * 2^8 that is e = k - 8 if m <= 1.75 (mantissa field at most
+// 0x600000), else k - 7; a zero or subnormal amax gives the floor -126.  The
+// quotient x / s = x * 2^-e is then exact (or below 2^-126, where every code
+// is a signed zero), so no division is needed, and |x / s| <= 448.
+__device__ __forceinline__ int pow2_exponent(float amax)
+{
+    const uint32_t u = __float_as_uint(amax);
+    if (u < 0x00800000u) return -126;
+    const int e = (int)(u >> 23) - 135 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    return e < -126 ? -126 : e;
+}
+
+// Tile constants for a scale stored as S: float (s = amax / 448) or uint8_t
+// (E8M0 byte of a power-of-two s; mode 3, y = 2^-e exactly).
+template <typename S> __device__ __forceinline__ TileScale make_tile_scale(float amax);
+template <> __device__ __forceinline__ TileScale make_tile_scale<float>(float amax) { return make_scale(amax); }
+template <> __device__ __forceinline__ TileScale make_tile_scale<uint8_t>(float amax)
+{
+    const int e = pow2_exponent(amax);
+    TileScale t;
+    t.s = __uint_as_float((uint32_t)(e + 127) << 23);
+    t.y = __uint_as_float((uint32_t)(127 - e) << 23);
+    t.mode = 3;
+    return t;
+}
+
+template <typename S> __device__ __forceinline__ S stored_scale(const TileScale& t);
+template <> __device__ __forceinline__ float stored_scale<float>(const TileScale& t) { return t.s; }
+template <> __device__ __forceinline__ uint8_t stored_scale<uint8_t>(const TileScale& t)
+{
+    return (uint8_t)(__float_as_uint(t.s) >> 23);
+}
+
+template <typename S>
+__device__ __forceinline__ void quant8_as(const float v[8], const TileScale& t, uint32_t& lo, uint32_t& hi)
+{
+    if constexpr (sizeof(S) == 4) {
+        quant8(v, t, lo, hi);
+    } else {
+        lo = pack4_e4m3(v[0] * t.y, v[1] * t.y, v[2] * t.y, v[3] * t.y);
+        hi = pack4_e4m3(v[4] * t.y, v[5] * t.y, v[6] * t.y, v[7] * t.y);
     }
 }
 

@@ -22,6 +22,15 @@ void launch_quant_transpose(const void* x, int x_dtype, int64_t rows, int64_t co
                             uint8_t* q_colT, int64_t ldq_colT, float* s_colT, int64_t lds_colT,
                             hipStream_t st);
 
+// power-of-two scales as E8M0 bytes (row tiles and 128x128 blocks)
+void launch_quant_blockwise_e8m0(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                                 int kind, uint8_t* q, int64_t ldq, uint8_t* e, int64_t lde,
+                                 hipStream_t st);
+void launch_quant_transpose_e8m0(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                                 uint8_t* q_row, int64_t ldq_row, uint8_t* e_row, int64_t lde_row,
+                                 uint8_t* q_colT, int64_t ldq_colT, uint8_t* e_colT, int64_t lde_colT,
+                                 hipStream_t st);
+
 void launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const float* sa,
                  int64_t ldsa, int sa_kind, const uint8_t* b, int64_t ldb, int b_layout,
                  const float* sb, int64_t ldsb, int sb_kind, void* c, int64_t ldc, int c_dtype,
@@ -39,6 +48,9 @@ bool launch_gemm_e4m3(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t
                       int64_t ldsa, int sa_kind, const uint8_t* b, int64_t ldb, int b_layout,
                       const float* sb, int64_t ldsb, int sb_kind, uint8_t* q, int64_t ldq, float* s,
                       int64_t lds, hipStream_t st);
+bool launch_gemm_e8m0(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* ea,
+                      int64_t ldea, const uint8_t* b, int64_t ldb, int b_layout, const uint8_t* eb,
+                      int64_t ldeb, int eb_kind, void* c, int64_t ldc, int c_dtype, hipStream_t st);
 void launch_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K, const uint8_t* a,
                          int64_t lda, const float* sa, int64_t ldsa, const int32_t* offsets,
                          const uint8_t* b, const float* sb, void* c, int64_t ldc, int c_dtype,

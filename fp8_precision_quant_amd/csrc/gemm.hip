@@ -408,6 +408,21 @@ bool launch_gemm_e4m3(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t
     return launch_gemm_nk(g, sa_mode, sb_mode, b_layout == FP8Q_B_KN, OUT_E4M3, st);
 }
 
+bool launch_gemm_e8m0(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* ea,
+                      int64_t ldea, const uint8_t* b, int64_t ldb, int b_layout, const uint8_t* eb,
+                      int64_t ldeb, int eb_kind, void* c, int64_t ldc, int c_dtype, hipStream_t st)
+{
+    GemmArgs g{};
+    g.M = M; g.N = N; g.K = K;
+    g.a = a; g.lda = lda; g.sa = reinterpret_cast<const float*>(ea); g.ldsa = ldea;
+    g.b = b; g.ldb = ldb; g.sb = reinterpret_cast<const float*>(eb); g.ldsb = ldeb;
+    g.c = c; g.ldc = ldc;
+    g.KB = (int)((K + BK - 1) / BK);
+    g.num_cus = device_cu_count();
+    return launch_gemm_nk_e8m0(g, eb_kind == FP8Q_ROW_1x128 ? SB_ROW : SB_BLOCK, b_layout == FP8Q_B_KN,
+                               c_dtype == FP8Q_BF16, st);
+}
+
 void launch_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K, const uint8_t* a,
                          int64_t lda, const float* sa, int64_t ldsa, const int32_t* offsets,
                          const uint8_t* b, const float* sb, void* c, int64_t ldc, int c_dtype,

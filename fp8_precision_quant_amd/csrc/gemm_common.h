@@ -64,6 +64,10 @@ bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, int 
 // through the device group offsets (B per expert as [N][K] for the forward,
 // read as [K][N] for dgrad); false if the call is not covered.
 bool launch_grouped_gemm_nk(const GemmArgs& g, bool out_bf16, bool b_kn, hipStream_t st);
+// Dense launch with power-of-two scales: p.sa / p.sb point at E8M0 bytes
+// (row-scaled A; block-scaled B as [N][K] or [K][N], or row-scaled [N][K]
+// B), whose row strides are multiples of 4; false if the call is not covered.
+bool launch_gemm_nk_e8m0(const GemmArgs& g, int sb_mode, bool b_kn, bool out_bf16, hipStream_t st);
 // Grouped weight gradient: for each group, the product over the group's
 // token chunks only, into the group's own fp32 output block.
 bool launch_grouped_wgrad_nk(const GemmArgs& g, hipStream_t st);

@@ -147,6 +147,15 @@ __device__ __forceinline__ float ds32(uint32_t addr)
     return v;
 }
 
+// one byte of LDS, zero-extended (the E8M0 scale bytes)
+template <int OFF>
+__device__ __forceinline__ int ds_u8(uint32_t addr)
+{
+    int v;
+    asm volatile("ds_read_u8 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+
 typedef int v2i __attribute__((ext_vector_type(2)));
 
 // Transposing LDS read: within each 16-lane group, lane i receives byte
@@ -202,6 +211,9 @@ struct Frags {
     v8i a[PMI], b[NNI];
     float s[PMI];    // combined scale of the lane's row in block i for the chunk
     float sbk;       // SB of the wave's 128-column block (block-scaled B)
+    // power-of-two scales: E8M0 bytes of the lane's A row in block i, of its
+    // B row in block j (row-scaled B), of the wave's column block
+    int e[PMI], eb[NNI], ebk;
 };
 
 template <int OFF>
@@ -231,11 +243,17 @@ __device__ __forceinline__ v4f col_scales(uint32_t a, int j)
 // group selects the expert's B and B scales); 2 groups of K (MoE weight
 // gradient: tile rows index the virtual matrix [G][M], the group's token
 // chunks are the K loop and each group has its own output block).
-template <int SA_MODE, int SB_MODE, bool B_KN, int OUT, int GMODE>
+// P2: power-of-two scales given as E8M0 bytes (p.sa / p.sb point at bytes),
+// applied by the scaled MFMA itself: the chunk's product is accumulated in
+// place, with no partial sum and no scale FMA.  A scale grid's rows are read
+// as 4-byte words, each holding the bytes of four consecutive chunks.
+template <int SA_MODE, int SB_MODE, bool B_KN, int OUT, int GMODE, bool P2>
 __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
 {
     constexpr int kSbStages = SB_MODE == SB_ROW ? 4 : kStages;
     static_assert(!(B_KN && SB_MODE == SB_ROW), "row-scaled B is [N][K] only");
+    static_assert(!P2 || (GMODE == 0 && SA_MODE == SA_ROW && SB_MODE != SB_TENSOR && OUT != OUT_E4M3),
+                  "power-of-two scales: dense, row-scaled A, block- or row-scaled B, fp32/bf16 out");
     __shared__ int32_t goff[GMODE != 0 ? kMaxLdsGroups + 1 : 1];
     // groups of K: this XCD's groups, largest first
     __shared__ int32_t xlist[GMODE == 2 ? kMaxLdsGroups / 8 + 1 : 1];
@@ -361,11 +379,16 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     const int64_t nblocks = (N + 127) / 128;
     const bool load_sa = SA_MODE == SA_ROW && wq < 2;
     const bool load_sb = SB_MODE == SB_ROW || (SB_MODE == SB_BLOCK && wq == 2);
-    const __amdgpu_buffer_rsrc_t rsa = rsrc(p.sa, SA_MODE == SA_ROW ? ((M - 1) * p.ldsa + KBg) * 4 : 4);
+    // (E8M0 grids: byte extents, each row's last word included)
+    const int64_t kb_words = (KBg + 3) & ~3, nb_words = (nblocks + 3) & ~3;
+    const __amdgpu_buffer_rsrc_t rsa = rsrc(p.sa, SA_MODE != SA_ROW ? 4
+                                                  : P2 ? (M - 1) * p.ldsa + kb_words
+                                                       : ((M - 1) * p.ldsa + KBg) * 4);
     auto sb_rsrc = [&]() {
-        if (SB_MODE == SB_ROW) return rsrc(p.sb, ((N - 1) * p.ldsb + KBg) * 4);
+        if (SB_MODE == SB_ROW) return rsrc(p.sb, P2 ? (N - 1) * p.ldsb + kb_words : ((N - 1) * p.ldsb + KBg) * 4);
         if (SB_MODE == SB_BLOCK) {
             const float* sbg = p.sb + (GMODE == 1 ? (int64_t)grp_e * p.sb_group_stride : 0);
+            if (P2) return rsrc(sbg, B_KN ? (int64_t)(KBg - 1) * p.ldsb + nb_words : (nblocks - 1) * p.ldsb + kb_words);
             if (B_KN) return rsrc(sbg, ((int64_t)(KBg - 1) * p.ldsb + nblocks) * 4);
             return rsrc(sbg, ((nblocks - 1) * p.ldsb + KBg) * 4);
         }
@@ -402,9 +425,14 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
                 o.vb[h] = (uint32_t)((n0 + 64 * wq + (l >> 3)) * p.ldb) + 16u * (uint32_t)((l & 7) ^ (l >> 3) ^ h);
             }
         }
-        o.vsa = (uint32_t)((m0 + 64 * wq + l) * p.ldsa * 4);
-        o.vsb = SB_MODE == SB_ROW ? (uint32_t)((n0 + 64 * wq + l) * p.ldsb * 4)
-                                  : (uint32_t)((n0 / 128 + (l < 1 ? l : 1)) * (B_KN ? 4 : p.ldsb * 4));
+        constexpr int se = P2 ? 1 : 4;   // bytes per scale
+        o.vsa = (uint32_t)((m0 + 64 * wq + l) * p.ldsa * se);
+        if (SB_MODE == SB_ROW)
+            o.vsb = (uint32_t)((n0 + 64 * wq + l) * p.ldsb * se);
+        else if (P2 && B_KN)   // one word holds both column blocks (n0 / 128 is even)
+            o.vsb = (uint32_t)((n0 / 128) & ~(int64_t)3);
+        else
+            o.vsb = (uint32_t)((n0 / 128 + (l < 1 ? l : 1)) * (B_KN ? 4 : p.ldsb * se));
         return o;
     };
     auto issue = [&](int kb) {
@@ -424,11 +452,12 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
 #pragma unroll
         for (int t = 0; t < 8; ++t)
             dma16_at(rb, b_lds + (uint32_t)(B_KN ? 4 * t * TBN : 8 * t * TBK), o.vb[t & 1], b_soff + t * b_step);
-        if (load_sa) dma4(rsa, &SAs[st][64 * wq], o.vsa, kg * 4);
+        const uint32_t s_soff = P2 ? (kg & ~3u) : kg * 4;   // the chunk's word of a scale row
+        if (load_sa) dma4(rsa, &SAs[st][64 * wq], o.vsa, s_soff);
         if (SB_MODE == SB_ROW)
-            dma4(rsb, &SBs[kb % kSbStages][64 * wq], o.vsb, kg * 4);
+            dma4(rsb, &SBs[kb % kSbStages][64 * wq], o.vsb, s_soff);
         else if (load_sb)
-            dma4(rsb, &SBs[st][0], o.vsb, B_KN ? kg * (uint32_t)p.ldsb * 4 : kg * 4);
+            dma4(rsb, &SBs[st][0], o.vsb, B_KN ? kg * (uint32_t)p.ldsb * (P2 ? 1 : 4) : s_soff);
     };
 
     v4f acc[PMI][NNI];
@@ -470,12 +499,36 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     };
     // A fragments and scales of the chunk in stage st (A rows are loaded by
     // all four waves of the group: read after the phase barrier)
-    auto read_a = [&](int st, Frags& f) {
+    auto read_a = [&](int st, Frags& f, int c) {
         int l = lane;
         asm volatile("" : "+v"(l));
         const int lrow = l & 15, kgrp = l >> 4;
         const uint32_t so = lds_addr(Stg) + (uint32_t)st * kStageBytes;
-        if (SA_MODE == SA_ROW) {
+        if (P2) {
+            // byte c & 3 of the scale words (dense: the chunk index is kg)
+            const uint32_t sel = (uint32_t)(c & 3);
+            const uint32_t sa = lds_addr(SAs) + (uint32_t)(st * TBM + lrow) * 4 + sel;
+            f.e[0] = ds_u8<0>(sa);
+            f.e[1] = ds_u8<64>(sa);
+            f.e[2] = ds_u8<128>(sa);
+            f.e[3] = ds_u8<192>(sa);
+            f.e[4] = ds_u8<256>(sa);
+            f.e[5] = ds_u8<320>(sa);
+            f.e[6] = ds_u8<384>(sa);
+            f.e[7] = ds_u8<448>(sa);
+            if (SB_MODE == SB_BLOCK) {
+                const uint32_t byte = B_KN ? (uint32_t)((n0 >> 7) & 3) + (uint32_t)(wq >> 1)
+                                           : (uint32_t)(wq >> 1) * 4 + sel;
+                f.ebk = ds_u8<0>(lds_addr(SBs) + (uint32_t)(st * 64) * 4 + byte);
+            }
+            if (SB_MODE == SB_ROW) {
+                const uint32_t sb = lds_addr(SBs) + (uint32_t)((c % kSbStages) * TBN + 64 * wq + lrow) * 4 + sel;
+                f.eb[0] = ds_u8<0>(sb);
+                f.eb[1] = ds_u8<64>(sb);
+                f.eb[2] = ds_u8<128>(sb);
+                f.eb[3] = ds_u8<192>(sb);
+            }
+        } else if (SA_MODE == SA_ROW) {
             const uint32_t sa = lds_addr(SAs) + (uint32_t)(st * TBM + lrow) * 4;
             f.s[0] = ds32<0>(sa);
             f.s[1] = ds32<64>(sa);
@@ -486,7 +539,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
             f.s[6] = ds32<384>(sa);
             f.s[7] = ds32<448>(sa);
         }
-        if (SB_MODE == SB_BLOCK) f.sbk = ds32<0>(lds_addr(SBs) + (uint32_t)(st * 64 + (wq >> 1)) * 4);
+        if (!P2 && SB_MODE == SB_BLOCK) f.sbk = ds32<0>(lds_addr(SBs) + (uint32_t)(st * 64 + (wq >> 1)) * 4);
         const uint32_t a0 = so + sw(lrow, 2 * kgrp), a1 = so + sw(lrow, 2 * kgrp + 1);
         f.a[0] = frag_nk<0>(a0, a1);
         f.a[1] = frag_nk<1>(a0, a1);
@@ -503,6 +556,13 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
         pin4(f.a[0], f.a[1], f.a[2], f.a[3]);
         asm volatile("" : "+v"(f.a[4]), "+v"(f.a[5]), "+v"(f.a[6]));
         pin4(f.b[0], f.b[1], f.b[2], f.b[3]);
+        if (P2) {
+            asm volatile("" : "+v"(f.e[0]), "+v"(f.e[1]), "+v"(f.e[2]), "+v"(f.e[3]),
+                              "+v"(f.e[4]), "+v"(f.e[5]), "+v"(f.e[6]), "+v"(f.e[7]));
+            if (SB_MODE == SB_ROW) asm volatile("" : "+v"(f.eb[0]), "+v"(f.eb[1]), "+v"(f.eb[2]), "+v"(f.eb[3]));
+            if (SB_MODE == SB_BLOCK) asm volatile("" : "+v"(f.ebk));
+            return;
+        }
         if (SA_MODE == SA_ROW)
             asm volatile("" : "+v"(f.s[0]), "+v"(f.s[1]), "+v"(f.s[2]), "+v"(f.s[3]),
                               "+v"(f.s[4]), "+v"(f.s[5]), "+v"(f.s[6]), "+v"(f.s[7]));
@@ -533,6 +593,22 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     // read from LDS while the MFMAs of block j-1 run, and each FMA takes
     // the product of its row and column scale.
     auto compute = [&](Frags& f, int c) {
+        if constexpr (P2) {
+            // the scaled MFMA: first scale for the first operand (B rows,
+            // lane l: row l % 16), second for A rows; each lane gives the
+            // byte of the row it holds, the same for its four 32-wide K groups
+#pragma unroll
+            for (int u = 0; u < PMI * NNI; ++u) {
+                const int j = u / PMI, i = u % PMI;
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    f.b[j], f.a[i], acc[i][j], 0, 0, 0, SB_MODE == SB_ROW ? f.eb[j] : f.ebk, 0, f.e[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < PMI; ++i)
+#pragma unroll
+                for (int j = 0; j < NNI; ++j) asm volatile("" : "+v"(acc[i][j]));
+            return;
+        }
         uint32_t sbp = 0;
         v4f sc[NNI];
         if (SB_MODE == SB_ROW) {
@@ -604,7 +680,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
                 bar();
                 if (c + 2 < KB) issue(c + 2);
                 if (!kEarlyB) read_b(c % kStages, f);
-                read_a(c % kStages, f);
+                read_a(c % kStages, f, c);
                 reads_wait(f);
                 // (groups of K are whole 128-token chunks: no partial chunk)
                 if (GMODE != 2 && c == KB - 1 && k_tail < TBK) mask_k_tail(f);
@@ -769,7 +845,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     wait_vm<0>();
 }
 
-template <int SA_MODE, int SB_MODE, bool B_KN, int OUT, int GMODE = 0>
+template <int SA_MODE, int SB_MODE, bool B_KN, int OUT, int GMODE = 0, bool P2 = false>
 static void launch_out(const GemmArgs& g, hipStream_t st)
 {
     GemmArgs a = g;
@@ -777,7 +853,7 @@ static void launch_out(const GemmArgs& g, hipStream_t st)
     a.tiles_n = (int)((g.N + TBN - 1) / TBN);
     const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
     dim3 grid((uint32_t)(tiles < g.num_cus ? tiles : g.num_cus));
-    hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, B_KN, OUT, GMODE>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((gemm_nk_kernel<SA_MODE, SB_MODE, B_KN, OUT, GMODE, P2>), grid, dim3(kThreads), 0, st, a);
 }
 
 template <int SA_MODE, int SB_MODE, bool B_KN, int GMODE = 0>
@@ -809,6 +885,27 @@ bool launch_grouped_wgrad_nk(const GemmArgs& g, hipStream_t st)
         (int64_t)g.G * ((g.M + TBM - 1) / TBM) >= lim)
         return false;
     launch_out<SA_ROW, SB_ROW, false, OUT_F32, 2>(g, st);
+    return true;
+}
+
+bool launch_gemm_nk_e8m0(const GemmArgs& g, int sb_mode, bool b_kn, bool out_bf16, hipStream_t st)
+{
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t b_rows = b_kn ? g.K : g.N;
+    if (g.M * g.lda >= lim || (b_rows + TBK) * g.ldb >= lim || g.M * g.ldsa >= lim ||
+        (g.N + (int64_t)g.KB) * g.ldsb >= lim || (int64_t)g.KB * TBK >= lim)
+        return false;
+    if (b_kn && sb_mode != SB_BLOCK) return false;
+    if (b_kn) {
+        if (out_bf16) launch_out<SA_ROW, SB_BLOCK, true, OUT_BF16, 0, true>(g, st);
+        else launch_out<SA_ROW, SB_BLOCK, true, OUT_F32, 0, true>(g, st);
+    } else if (sb_mode == SB_BLOCK) {
+        if (out_bf16) launch_out<SA_ROW, SB_BLOCK, false, OUT_BF16, 0, true>(g, st);
+        else launch_out<SA_ROW, SB_BLOCK, false, OUT_F32, 0, true>(g, st);
+    } else {
+        if (out_bf16) launch_out<SA_ROW, SB_ROW, false, OUT_BF16, 0, true>(g, st);
+        else launch_out<SA_ROW, SB_ROW, false, OUT_F32, 0, true>(g, st);
+    }
     return true;
 }
 

@@ -1,5 +1,5 @@
 // Tile quantizers for gfx950: 1x128 row tiles, 128x128 blocks and one scale
-// per tensor.
+// per tensor; the tile kernels also write power-of-two scales as E8M0 bytes.
 //
 // Per tile: amax = max |x|, s = amax / 448, code = E4M3(RN(x / s)) (FP8-LM
 // review, section 三, tensor scaling; Ling 2.0 FP8 blog, fine-grained
@@ -136,10 +136,10 @@ constexpr int kRowThreads = 256;
 constexpr int kRowUnroll = 4;
 constexpr int kRowTilesPerBlock = (kRowThreads / 16) * kRowUnroll;
 
-template <typename T>
+template <typename T, typename S>
 __global__ __launch_bounds__(kRowThreads) void quant_row_kernel(
     const T* __restrict__ x, int64_t cols, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
-    float* __restrict__ s, int64_t lds, uint32_t total_tiles, FastDiv tiles_per_row)
+    S* __restrict__ s, int64_t lds, uint32_t total_tiles, FastDiv tiles_per_row)
 {
     const int lane16 = threadIdx.x & 15;
     const int group = threadIdx.x >> 4;
@@ -161,15 +161,15 @@ __global__ __launch_bounds__(kRowThreads) void quant_row_kernel(
     for (int u = 0; u < kRowUnroll; ++u) {
         uint32_t t = base + u * (kRowThreads / 16) + group;
         float amax = dpp_max16(absmax8(v[u]));
-        TileScale ts = make_scale(amax);
+        TileScale ts = make_tile_scale<S>(amax);
         uint32_t lo, hi;
-        quant8(v[u], ts, lo, hi);
+        quant8_as<S>(v[u], ts, lo, hi);
         if (t < total_tiles) {
             int64_t c = (int64_t)tcol[u] * kTile + lane16 * 8;
             if (c < cols)
                 store8(q + (int64_t)row[u] * ldq, c, cols, lo, hi);
             if (lane16 == 0)
-                s[(int64_t)row[u] * lds + tcol[u]] = ts.s;
+                s[(int64_t)row[u] * lds + tcol[u]] = stored_scale<S>(ts);
         }
     }
 }
@@ -185,10 +185,10 @@ __global__ __launch_bounds__(kRowThreads) void quant_row_kernel(
 
 constexpr int kBlockThreads = 256;
 
-template <typename T>
+template <typename T, typename S>
 __global__ __launch_bounds__(kBlockThreads) void quant_block_kernel(
     const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* __restrict__ q,
-    int64_t ldq, float* __restrict__ s, int64_t lds, uint32_t total_blocks, FastDiv blocks_per_row)
+    int64_t ldq, S* __restrict__ s, int64_t lds, uint32_t total_blocks, FastDiv blocks_per_row)
 {
     __shared__ float wave_max[2][kBlockThreads / 64];
     const int l = threadIdx.x & 15;
@@ -230,19 +230,19 @@ __global__ __launch_bounds__(kBlockThreads) void quant_block_kernel(
         __syncthreads();
         const float amax = fmaxf(fmaxf(wave_max[parity][0], wave_max[parity][1]),
                                  fmaxf(wave_max[parity][2], wave_max[parity][3]));
-        const TileScale ts = make_scale(amax);
+        const TileScale ts = make_tile_scale<S>(amax);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int64_t r = r0 + g + 16 * u;
             float v[8];
             raw_f32(R[u], c, cols, v);
             uint32_t lo, hi;
-            quant8(v, ts, lo, hi);
+            quant8_as<S>(v, ts, lo, hi);
             if (r < rows && c < cols)
                 store8(q + r * ldq, c, cols, lo, hi);
         }
         if (threadIdx.x == 0)
-            s[(int64_t)(r0 / kTile) * lds + (c - l * 8) / kTile] = ts.s;
+            s[(int64_t)(r0 / kTile) * lds + (c - l * 8) / kTile] = stored_scale<S>(ts);
     };
 
     Raw8<T> A[8], B[8];
@@ -329,9 +329,9 @@ __global__ void tensor_finish_kernel(uint32_t* cell)
 // launchers
 // ---------------------------------------------------------------------------
 
-template <typename T>
-static void launch_quant(const void* xv, int64_t rows, int64_t cols, int64_t ldx, int kind,
-                         uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st)
+template <typename T, typename S>
+static void launch_tiles(const void* xv, int64_t rows, int64_t cols, int64_t ldx, int kind,
+                         uint8_t* q, int64_t ldq, S* s, int64_t lds, hipStream_t st)
 {
     const T* x = static_cast<const T*>(xv);
     const int64_t tiles_c = (cols + kTile - 1) / kTile;
@@ -339,15 +339,25 @@ static void launch_quant(const void* xv, int64_t rows, int64_t cols, int64_t ldx
     if (kind == FP8Q_ROW_1x128) {
         uint32_t total = (uint32_t)(rows * tiles_c);
         uint32_t blocks = (total + kRowTilesPerBlock - 1) / kRowTilesPerBlock;
-        hipLaunchKernelGGL(quant_row_kernel<T>, dim3(blocks), dim3(kRowThreads), 0, st, x, cols,
+        hipLaunchKernelGGL((quant_row_kernel<T, S>), dim3(blocks), dim3(kRowThreads), 0, st, x, cols,
                            ldx, q, ldq, s, lds, total, make_fastdiv((uint32_t)tiles_c));
-    } else if (kind == FP8Q_BLOCK_128x128) {
+    } else {
         const uint32_t total = (uint32_t)(tiles_c * ((rows + kTile - 1) / kTile));
         // two resident workgroups per CU (about 220 VGPRs per lane)
         uint32_t blocks = total < (uint32_t)(cus * 2) ? total : (uint32_t)(cus * 2);
-        hipLaunchKernelGGL(quant_block_kernel<T>, dim3(blocks), dim3(kBlockThreads), 0, st, x, rows,
-                           cols, ldx, q, ldq, s, lds, total, make_fastdiv((uint32_t)tiles_c));
+        hipLaunchKernelGGL((quant_block_kernel<T, S>), dim3(blocks), dim3(kBlockThreads), 0, st, x,
+                           rows, cols, ldx, q, ldq, s, lds, total, make_fastdiv((uint32_t)tiles_c));
+    }
+}
+
+template <typename T>
+static void launch_quant(const void* xv, int64_t rows, int64_t cols, int64_t ldx, int kind,
+                         uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t st)
+{
+    if (kind != FP8Q_TENSOR) {
+        launch_tiles<T, float>(xv, rows, cols, ldx, kind, q, ldq, s, lds, st);
     } else {
+        const T* x = static_cast<const T*>(xv);
         uint32_t* cell = reinterpret_cast<uint32_t*>(s);
         int64_t cpr = (cols + 7) / 8;
         uint32_t total = (uint32_t)(rows * cpr);
@@ -371,6 +381,16 @@ void launch_quant_blockwise(const void* x, int x_dtype, int64_t rows, int64_t co
         launch_quant<uint16_t>(x, rows, cols, ldx, kind, q, ldq, s, lds, st);
     else
         launch_quant<float>(x, rows, cols, ldx, kind, q, ldq, s, lds, st);
+}
+
+void launch_quant_blockwise_e8m0(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                                 int kind, uint8_t* q, int64_t ldq, uint8_t* e, int64_t lde,
+                                 hipStream_t st)
+{
+    if (x_dtype == FP8Q_BF16)
+        launch_tiles<uint16_t, uint8_t>(x, rows, cols, ldx, kind, q, ldq, e, lde, st);
+    else
+        launch_tiles<float, uint8_t>(x, rows, cols, ldx, kind, q, ldq, e, lde, st);
 }
 
 }  // namespace fp8q

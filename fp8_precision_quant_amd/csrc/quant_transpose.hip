@@ -78,11 +78,11 @@ __device__ __forceinline__ void qt_load8<float>(const float* row, int64_t c, int
     }
 }
 
-template <typename T>
+template <typename T, typename S>
 __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
     const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
-    uint8_t* __restrict__ q_row, int64_t ldq_row, float* __restrict__ s_row, int64_t lds_row,
-    uint8_t* __restrict__ q_colT, int64_t ldq_colT, float* __restrict__ s_colT, int64_t lds_colT)
+    uint8_t* __restrict__ q_row, int64_t ldq_row, S* __restrict__ s_row, int64_t lds_row,
+    uint8_t* __restrict__ q_colT, int64_t ldq_colT, S* __restrict__ s_colT, int64_t lds_colT)
 {
     __shared__ float col_part[16 * kColPitch];   // per row-group column maxima
     __shared__ float row_amax[kTile];
@@ -133,20 +133,20 @@ __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
         float m = col_part[ci];
 #pragma unroll
         for (int k = 1; k < 16; ++k) m = fmaxf(m, col_part[k * kColPitch + ci]);
-        TileScale ts = make_scale(m);
+        TileScale ts = make_tile_scale<S>(m);
         col_s[tid] = ts.s;
         col_y[tid] = ts.y;
         col_mode[tid] = ts.mode;
         if (do_col && c0 + tid < cols)
-            s_colT[(c0 + tid) * lds_colT + rb] = ts.s;
+            s_colT[(c0 + tid) * lds_colT + rb] = stored_scale<S>(ts);
     } else {
         int i = tid - kTile;
-        TileScale ts = make_scale(row_amax[i]);
+        TileScale ts = make_tile_scale<S>(row_amax[i]);
         row_s[i] = ts.s;
         row_y[i] = ts.y;
         row_mode[i] = ts.mode;
         if (do_row && r0 + i < rows)
-            s_row[(r0 + i) * lds_row + cb] = ts.s;
+            s_row[(r0 + i) * lds_row + cb] = stored_scale<S>(ts);
     }
     __syncthreads();
 
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
             int i = 8 * g + u;
             TileScale ts{row_s[i], row_y[i], row_mode[i]};
             uint32_t lo, hi;
-            quant8(v[u], ts, lo, hi);
+            quant8_as<S>(v[u], ts, lo, hi);
             int64_t r = r0 + i;
             if (r < rows && c < cols) {
                 uint8_t* dst = q_row + r * ldq_row;
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
             TileScale ts{col_s[cj], col_y[cj], col_mode[cj]};
             const float cv[8] = {v[0][j], v[1][j], v[2][j], v[3][j], v[4][j], v[5][j], v[6][j], v[7][j]};
             uint32_t lo, hi;
-            quant8(cv, ts, lo, hi);
+            quant8_as<S>(cv, ts, lo, hi);
             *reinterpret_cast<uint2*>(stage + cj * kStagePitch + 8 * (g ^ stage_key(cj))) = make_uint2(lo, hi);
         }
         __syncthreads();
@@ -205,20 +205,38 @@ __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
     }
 }
 
+template <typename S>
+static void launch_qt(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                      uint8_t* q_row, int64_t ldq_row, S* s_row, int64_t lds_row,
+                      uint8_t* q_colT, int64_t ldq_colT, S* s_colT, int64_t lds_colT, hipStream_t st)
+{
+    dim3 grid((uint32_t)((cols + kTile - 1) / kTile), (uint32_t)((rows + kTile - 1) / kTile));
+    if (x_dtype == FP8Q_BF16)
+        hipLaunchKernelGGL((quant_transpose_kernel<uint16_t, S>), grid, dim3(kQtThreads), 0, st,
+                           static_cast<const uint16_t*>(x), rows, cols, ldx, q_row, ldq_row, s_row,
+                           lds_row, q_colT, ldq_colT, s_colT, lds_colT);
+    else
+        hipLaunchKernelGGL((quant_transpose_kernel<float, S>), grid, dim3(kQtThreads), 0, st,
+                           static_cast<const float*>(x), rows, cols, ldx, q_row, ldq_row, s_row,
+                           lds_row, q_colT, ldq_colT, s_colT, lds_colT);
+}
+
 void launch_quant_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
                             uint8_t* q_row, int64_t ldq_row, float* s_row, int64_t lds_row,
                             uint8_t* q_colT, int64_t ldq_colT, float* s_colT, int64_t lds_colT,
                             hipStream_t st)
 {
-    dim3 grid((uint32_t)((cols + kTile - 1) / kTile), (uint32_t)((rows + kTile - 1) / kTile));
-    if (x_dtype == FP8Q_BF16)
-        hipLaunchKernelGGL(quant_transpose_kernel<uint16_t>, grid, dim3(kQtThreads), 0, st,
-                           static_cast<const uint16_t*>(x), rows, cols, ldx, q_row, ldq_row, s_row,
-                           lds_row, q_colT, ldq_colT, s_colT, lds_colT);
-    else
-        hipLaunchKernelGGL(quant_transpose_kernel<float>, grid, dim3(kQtThreads), 0, st,
-                           static_cast<const float*>(x), rows, cols, ldx, q_row, ldq_row, s_row,
-                           lds_row, q_colT, ldq_colT, s_colT, lds_colT);
+    launch_qt<float>(x, x_dtype, rows, cols, ldx, q_row, ldq_row, s_row, lds_row, q_colT, ldq_colT,
+                     s_colT, lds_colT, st);
+}
+
+void launch_quant_transpose_e8m0(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                                 uint8_t* q_row, int64_t ldq_row, uint8_t* e_row, int64_t lde_row,
+                                 uint8_t* q_colT, int64_t ldq_colT, uint8_t* e_colT, int64_t lde_colT,
+                                 hipStream_t st)
+{
+    launch_qt<uint8_t>(x, x_dtype, rows, cols, ldx, q_row, ldq_row, e_row, lde_row, q_colT, ldq_colT,
+                       e_colT, lde_colT, st);
 }
 
 }  // namespace fp8q

@@ -254,6 +254,70 @@ int fp8_grouped_gemm_wgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K,
                            const int32_t* group_offsets,
                            float* c, int64_t ldc, void* stream);
 
+/*
+ * Power-of-two (E8M0) scales -- the micro-scaling variant of block scaling.
+ *
+ * Blackwell's MXFP8 gives each block of a tensor its own scale factor and
+ * applies it in hardware (Introl FP8 infrastructure guide, scaling strategies
+ * and the Blackwell section).  Here the tiles stay 1x128 / 128x128 and the
+ * scale is restricted to a power of two, s = 2^e, which gfx950's scaled MFMA
+ * applies itself (no scale arithmetic on the accumulators).  Per tile:
+ *   e = the smallest integer >= -126 with amax <= 448 * 2^e (exactly; amax
+ *       = 0 gives -126), stored as the byte e + 127 (E8M0: 2^(byte - 127));
+ *   code = E4M3(RN_fp32(x / 2^e)), the quotient exact in fp32 (or below
+ *       2^-126, where the code is a signed zero).  No value saturates.
+ * Compared with s = amax / 448 the scale is up to 2x larger, so small values
+ * underflow more easily; the product needs no scale multiplication.
+ * E8M0 grids are uint8 with row stride lde in bytes; the GEMM reads each row
+ * as 4-byte words, so a grid it consumes needs a 4-byte aligned pointer and
+ * lde % 4 == 0 (the quantizers accept any lde >= the grid width).
+ */
+
+/*
+ * fp8_quant_blockwise_e8m0 -- fp8_quant_blockwise with power-of-two scales.
+ *  kind : FP8Q_ROW_1x128 (e[rows][ceil(cols/128)]) or FP8Q_BLOCK_128x128
+ *         (e[ceil(rows/128)][ceil(cols/128)]); FP8Q_TENSOR is unsupported.
+ *  e, lde : output E8M0 bytes, row stride lde >= ceil(cols/128).
+ * Other arguments, alignment and errors as fp8_quant_blockwise.
+ */
+int fp8_quant_blockwise_e8m0(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                             int kind, uint8_t* q, int64_t ldq, uint8_t* e, int64_t lde,
+                             void* stream);
+
+/*
+ * fp8_quant_transpose_e8m0 -- fp8_quant_transpose with power-of-two scales:
+ * row tiles e_row[rows][ceil(cols/128)] and transposed column tiles
+ * e_colT[cols][ceil(rows/128)] as E8M0 bytes (strides lde_row, lde_colT).
+ * Other arguments and errors as fp8_quant_transpose.
+ */
+int fp8_quant_transpose_e8m0(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
+                             uint8_t* q_row, int64_t ldq_row, uint8_t* e_row, int64_t lde_row,
+                             uint8_t* q_colT, int64_t ldq_colT, uint8_t* e_colT, int64_t lde_colT,
+                             void* stream);
+
+/*
+ * fp8_gemm_e8m0 -- the block-scaled product (see Numerics) with SA, SB the
+ * powers of two 2^(byte - 127) of E8M0 grids.  The chunk's scales are
+ * applied inside the MFMA: each chunk's product, times 2^(ea + eb), is added
+ * to the fp32 accumulator.
+ *  a, lda, ea, ldea : A codes [M][K]; A scales 1x128, EA(m,kb) = ea[m*ldea + kb],
+ *                     ldea >= ceil(K/128).
+ *  b, ldb, b_layout : as fp8_gemm_blockscaled.
+ *  eb, ldeb, eb_kind: FP8Q_BLOCK_128x128 (NK: eb[(n/128)*ldeb + kb]; KN:
+ *                     eb[kb*ldeb + n/128]) or FP8Q_ROW_1x128 (NK only:
+ *                     eb[n*ldeb + kb]).
+ *  c, ldc, c_dtype  : output [M][N], FP8Q_F32 or FP8Q_BF16.
+ * ea and eb must be 4-byte aligned with ldea % 4 == ldeb % 4 == 0
+ * (FP8Q_ERR_ALIGN otherwise).  Scale bytes 0 and 255 are outside the
+ * contract (the quantizers write 1..247).  Returns FP8Q_ERR_UNSUPPORTED
+ * (nothing enqueued) if an operand spans 2 GiB or more.
+ */
+int fp8_gemm_e8m0(int64_t M, int64_t N, int64_t K,
+                  const uint8_t* a, int64_t lda, const uint8_t* ea, int64_t ldea,
+                  const uint8_t* b, int64_t ldb, int b_layout,
+                  const uint8_t* eb, int64_t ldeb, int eb_kind,
+                  void* c, int64_t ldc, int c_dtype, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* fp8q_status_string(int status);
 

@@ -24,6 +24,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     assert names == sorted(["fp8_quant_blockwise", "fp8_quant_transpose", "fp8_gemm_blockscaled",
                             "fp8_gemm_blockscaled_e4m3", "fp8_grouped_gemm", "fp8_grouped_gemm_dgrad", "fp8_grouped_gemm_wgrad",
+                            "fp8_quant_blockwise_e8m0", "fp8_quant_transpose_e8m0", "fp8_gemm_e8m0",
                             "fp8q_status_string"])
 
 
@@ -213,3 +214,65 @@ def test_grouped_wgrad_validation():
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is present: valid fake pointers would launch")
 def test_valid_arguments_without_gpu_report_device_error():
     assert q_blockwise() == fq.ERR_DEVICE
+
+
+def test_quant_e8m0_validation():
+    f = L.fp8_quant_blockwise_e8m0
+    # x, dtype, rows, cols, ldx, kind, q, ldq, e, lde, stream
+    base = [A16, fq.BF16, 4, 256, 256, fq.ROW_1x128, A16, 256, A16, 2, None]
+    def call(**ch):
+        a = list(base)
+        for i, v in ch.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a5=fq.TENSOR) == fq.ERR_UNSUPPORTED         # power-of-two scales are per tile
+    assert call(a1=5) == fq.ERR_UNSUPPORTED
+    assert call(a2=-1) == fq.ERR_SHAPE
+    assert call(a2=0, a0=None) == fq.OK                      # empty input
+    assert call(a8=None) == fq.ERR_NULL
+    assert call(a9=1) == fq.ERR_SHAPE                        # lde < ceil(cols/128)
+    assert call(a7=200) == fq.ERR_SHAPE
+    assert call(a0=MIS) == fq.ERR_ALIGN
+    assert call(a7=264) == fq.ERR_ALIGN
+    g = L.fp8_quant_transpose_e8m0
+    # x, dtype, rows, cols, ldx, q_row, ldq_row, e_row, lde_row, q_colT, ldq_colT, e_colT, lde_colT, stream
+    tb = [A16, fq.BF16, 256, 256, 256, A16, 256, A16, 2, A16, 256, A16, 2, None]
+    def tcall(**ch):
+        a = list(tb)
+        for i, v in ch.items():
+            a[int(i[1:])] = v
+        return g(*a)
+    assert tcall(a7=None) == fq.ERR_NULL                     # half of the row pair
+    assert tcall(a5=None, a7=None, a9=None, a11=None) == fq.OK
+    assert tcall(a12=1) == fq.ERR_SHAPE
+    assert tcall(a10=200) == fq.ERR_SHAPE
+    assert tcall(a9=MIS) == fq.ERR_ALIGN
+
+
+def test_gemm_e8m0_validation():
+    f = L.fp8_gemm_e8m0
+    # M, N, K, a, lda, ea, ldea, b, ldb, layout, eb, ldeb, eb_kind, c, ldc, cdt, stream
+    base = [256, 256, 512, A16, 512, A16, 4, A16, 512, fq.B_NK, A16, 4, fq.BLOCK_128x128,
+            A16, 256, fq.BF16, None]
+    def call(**ch):
+        a = list(base)
+        for i, v in ch.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a15=3) == fq.ERR_UNSUPPORTED
+    assert call(a9=2) == fq.ERR_UNSUPPORTED
+    assert call(a12=fq.TENSOR) == fq.ERR_UNSUPPORTED
+    assert call(a12=fq.ROW_1x128, a9=fq.B_KN, a8=256) == fq.ERR_UNSUPPORTED
+    assert call(a0=0, a13=None) == fq.OK                     # empty output
+    assert call(a13=None) == fq.ERR_NULL
+    assert call(a5=None) == fq.ERR_NULL
+    assert call(a10=None) == fq.ERR_NULL
+    assert call(a6=3) == fq.ERR_SHAPE                        # ldea < ceil(K/128)
+    assert call(a9=fq.B_KN, a8=256, a11=1) == fq.ERR_SHAPE   # KN block grid: ldeb < ceil(N/128)
+    assert call(a14=200) == fq.ERR_SHAPE
+    assert call(a6=6) == fq.ERR_ALIGN                        # scale rows read as 4-byte words
+    assert call(a11=6) == fq.ERR_ALIGN
+    assert call(a5=A16 + 2) == fq.ERR_ALIGN
+    assert call(a10=A16 + 1) == fq.ERR_ALIGN
+    assert call(a3=MIS) == fq.ERR_ALIGN
+    assert call(a13=A16 + 4) == fq.ERR_ALIGN
