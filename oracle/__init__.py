@@ -69,6 +69,9 @@ def lib() -> ctypes.CDLL:
             L.orc_pow2_exponent.argtypes = [ctypes.c_float]
             L.orc_pow2_exponent.restype = ctypes.c_int
             L.orc_e8m0_decode_array.argtypes = [p, i64, p]
+            f64 = ctypes.c_double
+            L.orc_adamw_step.argtypes = [i64, p, p, p, p, f64, f64, f64, f64, f64, i64]
+            L.orc_adamw_fp8_step.argtypes = [i64, p, p, p, p, p, p, f64, f64, f64, f64, f64, i64]
             L.orc_gemm_f32.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p]
             L.orc_gemm_f64.argtypes = [i64, i64, i64, p, p, p, p, p, i64, p, p]
             L.orc_f32_to_bf16.argtypes = [p, i64, p]
@@ -423,6 +426,34 @@ def grouped_gemm_wgrad(at, sat, bt, sbt, offsets, rows=None, f64=False):
         else:
             out[e] = res
     return (out, R) if f64 else out
+
+
+# ---------------------------------------------------------------------------
+# Adam with FP8 moments (Ling 2.0 FP8 blog, "FP8 Optimizer")
+# ---------------------------------------------------------------------------
+
+def adamw_step(p, g, m, v, lr, beta1, beta2, eps, wd, t):
+    """One fp32 AdamW step (see ``orc_adamw_step``); returns new ``(p, m, v)``."""
+    p = _c(p, np.float32).copy()
+    g = _c(g, np.float32)
+    m = _c(m, np.float32).copy()
+    v = _c(v, np.float32).copy()
+    lib().orc_adamw_step(p.size, _ptr(p), _ptr(g), _ptr(m), _ptr(v), lr, beta1, beta2, eps, wd, t)
+    return p, m, v
+
+
+def adamw_fp8_step(p, g, mq, ms, vq, vs, lr, beta1, beta2, eps, wd, t):
+    """One AdamW step with E4M3 moments and one fp32 scale per 128 elements:
+    returns new ``(p, mq, ms, vq, vs)`` (flat arrays)."""
+    p = _c(p, np.float32).reshape(-1).copy()
+    g = _c(g, np.float32).reshape(-1)
+    mq, vq = _c(mq, np.uint8).reshape(-1).copy(), _c(vq, np.uint8).reshape(-1).copy()
+    ms, vs = _c(ms, np.float32).reshape(-1).copy(), _c(vs, np.float32).reshape(-1).copy()
+    n = p.size
+    assert g.size == n and mq.size == n and vq.size == n and ms.size == vs.size == -(-n // TILE)
+    lib().orc_adamw_fp8_step(n, _ptr(p), _ptr(g), _ptr(mq), _ptr(ms), _ptr(vq), _ptr(vs),
+                             lr, beta1, beta2, eps, wd, t)
+    return p, mq, ms, vq, vs
 
 
 # ---------------------------------------------------------------------------

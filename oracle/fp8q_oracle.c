@@ -370,6 +370,77 @@ void orc_gemm_f64(int64_t M, int64_t N, int64_t K, const uint8_t* A,
     free(SBT);
 }
 
+/* ------------------------------------------------------------------ */
+/* Adam with FP8 moments                                                */
+/* ------------------------------------------------------------------ */
+
+/* One AdamW step on fp32 parameters and fp32 moments (the decoupled-weight-
+ * decay Adam of Loshchilov and Hutter, bias-corrected as in Kingma and Ba).
+ * The hyperparameters are doubles; each derived scalar is computed in double
+ * and rounded once to fp32:
+ *   b1 = beta1, b2 = beta2, omb1 = 1 - beta1, omb2 = 1 - beta2,
+ *   decay = 1 - lr * wd, step_size = lr / (1 - beta1^t),
+ *   bc2_sqrt = sqrt(1 - beta2^t), epsf = eps;
+ * then per element, every operation one fp32 rounding, in this order:
+ *   p = p * decay;  m = b1 * m + omb1 * g;  v = b2 * v + (omb2 * g) * g;
+ *   den = sqrt(v) / bc2_sqrt + epsf;  p = p - step_size * (m / den).
+ * The pages name Adam's two moments as the optimizer state (Ling 2.0 FP8
+ * blog, "FP8 Optimizer"); the step itself is the textbook one. */
+void orc_adamw_step(int64_t n, float* p, const float* g, float* m, float* v, double lr, double beta1,
+                    double beta2, double eps, double wd, int64_t t)
+{
+    const float b1 = (float)beta1, b2 = (float)beta2;
+    const float omb1 = (float)(1.0 - beta1);
+    const float omb2 = (float)(1.0 - beta2);
+    const float decay = (float)(1.0 - lr * wd);
+    const float step_size = (float)(lr / (1.0 - pow(beta1, (double)t)));
+    const float bc2_sqrt = (float)sqrt(1.0 - pow(beta2, (double)t));
+    const float epsf = (float)eps;
+    for (int64_t i = 0; i < n; ++i) {
+        float pi = p[i] * decay;
+        float a = b1 * m[i];
+        float b = omb1 * g[i];
+        float mi = a + b;
+        float c = b2 * v[i];
+        float d = omb2 * g[i];
+        float e = d * g[i];
+        float vi = c + e;
+        float r = sqrtf(vi);
+        float q = r / bc2_sqrt;
+        float den = q + epsf;
+        float u = mi / den;
+        float w = step_size * u;
+        p[i] = pi - w;
+        m[i] = mi;
+        v[i] = vi;
+    }
+}
+
+/* The same step with both moments held as E4M3 codes plus one fp32 scale per
+ * 128 consecutive elements (the fine-grained compression of the moments in
+ * the Ling 2.0 FP8 blog, "FP8 Optimizer", which points to block-wise
+ * quantization): decode (code value times its block's scale), the fp32 step
+ * above, and the 1x128 tile quantization of the new moments
+ * (orc_quant_tiles on the flat vector).  mq/vq: n codes; ms/vs:
+ * ceil(n/128) scales; all updated in place. */
+void orc_adamw_fp8_step(int64_t n, float* p, const float* g, uint8_t* mq, float* ms, uint8_t* vq,
+                        float* vs, double lr, double beta1, double beta2, double eps, double wd, int64_t t)
+{
+    if (n <= 0)
+        return;
+    float* m = (float*)malloc(sizeof(float) * (size_t)n);
+    float* v = (float*)malloc(sizeof(float) * (size_t)n);
+    for (int64_t i = 0; i < n; ++i) {
+        m[i] = orc_e4m3_decode(mq[i]) * ms[i / 128];
+        v[i] = orc_e4m3_decode(vq[i]) * vs[i / 128];
+    }
+    orc_adamw_step(n, p, g, m, v, lr, beta1, beta2, eps, wd, t);
+    orc_quant_tiles(m, 1, n, 1, 128, mq, ms);
+    orc_quant_tiles(v, 1, n, 1, 128, vq, vs);
+    free(m);
+    free(v);
+}
+
 /* fp32 -> bf16 bit pattern, round to nearest even (finite inputs). */
 void orc_f32_to_bf16(const float* x, int64_t n, uint16_t* out)
 {
