@@ -399,6 +399,31 @@ def main():
             rec["frac_peak"] = round(hbm_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
         pow2["kernels"].append(rec)
 
+    # The optimizer step of the same layer: AdamW with FP8 moments on an fp32
+    # master copy of W, the step's fp32 dW as gradient.
+    n_w = N * K
+    p_w = w.float().reshape(-1).contiguous()
+    g_w = dW.reshape(-1)
+    st8 = fq.fp8_adam_state(n_w, dev)
+    for t in range(1, args.warmup + 1):
+        fq.fp8_adam_step(p_w, g_w, st8, lr=1e-4, weight_decay=0.1, step=t)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for t in range(args.warmup + 1, args.warmup + 1 + args.steps):
+        fq.fp8_adam_step(p_w, g_w, st8, lr=1e-4, weight_decay=0.1, step=t)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    adam_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    # algorithmic bytes: parameters read and written (8), fp32 gradient (4),
+    # both moments' codes read and written (4), their scales (16 per 128)
+    adam_bytes = n_w * 16 + (n_w // 128) * 16
+    adam = {"params": n_w, "us": round(adam_us, 2), "GB/s": round(adam_bytes / (adam_us * 1e-6) / 1e9, 1),
+            "frac_peak": round(adam_bytes / (adam_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "state_bytes_per_param": 2 + 8 / 128}
+    del p_w, st8
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x_bits, w_bits, dy_bits, args.cpu_rows)
@@ -428,6 +453,7 @@ def main():
         "moe_grouped": moe,
         "fwd_quantize_on_store": fused,
         "pow2_scales": pow2,
+        "fp8_adam": adam,
     }
     print(json.dumps(out))
 

@@ -55,10 +55,12 @@ _lib.fp8_quant_transpose_e8m0.argtypes = [_p, _int, _i64, _i64, _i64,
                                           _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p]
 _lib.fp8_gemm_e8m0.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64,
                                _p, _i64, _int, _p, _i64, _int, _p, _i64, _int, _p]
+_d = ctypes.c_double
+_lib.fp8_adam_step.argtypes = [_i64, _p, _p, _int, _p, _p, _p, _p, _d, _d, _d, _d, _d, _i64, _p]
 for _f in ("fp8_quant_blockwise", "fp8_quant_transpose", "fp8_gemm_blockscaled",
            "fp8_gemm_blockscaled_e4m3", "fp8_grouped_gemm", "fp8_grouped_gemm_dgrad",
            "fp8_grouped_gemm_wgrad", "fp8_quant_blockwise_e8m0", "fp8_quant_transpose_e8m0",
-           "fp8_gemm_e8m0"):
+           "fp8_gemm_e8m0", "fp8_adam_step"):
     getattr(_lib, _f).restype = _int
 _lib.fp8q_status_string.argtypes = [_int]
 _lib.fp8q_status_string.restype = ctypes.c_char_p
@@ -66,7 +68,7 @@ _lib.fp8q_status_string.restype = ctypes.c_char_p
 SYMBOLS = ("fp8_quant_blockwise", "fp8_quant_transpose", "fp8_gemm_blockscaled",
            "fp8_gemm_blockscaled_e4m3", "fp8_grouped_gemm", "fp8_grouped_gemm_dgrad", "fp8_grouped_gemm_wgrad",
            "fp8_quant_blockwise_e8m0", "fp8_quant_transpose_e8m0", "fp8_gemm_e8m0",
-           "fp8q_status_string")
+           "fp8_adam_step", "fp8q_status_string")
 
 
 class Fp8qError(RuntimeError):
@@ -234,6 +236,37 @@ def fp8_gemm_e8m0(a: torch.Tensor, ea: torch.Tensor, b: torch.Tensor, eb: torch.
                             _ptr(c), _ld(c), cd, _stream(a.device, stream))
     _check(st, "fp8_gemm_e8m0")
     return c
+
+
+def fp8_adam_state(n: int, device) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
+    """A fresh (all-zero) FP8 moment state for ``n`` parameters:
+    (mq[n] uint8, ms[ceil(n/128)] fp32, vq[n], vs[ceil(n/128)])."""
+    nb = _cdiv(n, TILE)
+    return (torch.zeros(n, dtype=torch.uint8, device=device), torch.zeros(nb, dtype=torch.float32, device=device),
+            torch.zeros(n, dtype=torch.uint8, device=device), torch.zeros(nb, dtype=torch.float32, device=device))
+
+
+def fp8_adam_step(p: torch.Tensor, g: torch.Tensor, state, lr: float, beta1: float = 0.9,
+                  beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.0, step: int = 1,
+                  stream=None) -> None:
+    """One AdamW step in place on fp32 parameters ``p`` (any shape,
+    contiguous) with gradient ``g`` (same number of elements, fp32 or bf16,
+    contiguous) and FP8 moments ``state = (mq, ms, vq, vs)`` (see
+    ``fp8_adam_state``)."""
+    mq, ms, vq, vs = state
+    n = p.numel()
+    if g.numel() != n or mq.numel() != n or vq.numel() != n or ms.numel() != _cdiv(n, TILE) \
+            or vs.numel() != ms.numel():
+        raise ValueError("parameter, gradient and state sizes differ")
+    for t in (p, g, mq, ms, vq, vs):
+        if not t.is_contiguous():
+            raise ValueError("fp8_adam_step needs contiguous tensors")
+    if p.dtype != torch.float32 or mq.dtype != torch.uint8 or vq.dtype != torch.uint8 \
+            or ms.dtype != torch.float32 or vs.dtype != torch.float32:
+        raise ValueError("parameters and scales are float32, codes uint8")
+    st = _lib.fp8_adam_step(n, _ptr(p), _ptr(g), _dtype_code(g), _ptr(mq), _ptr(ms), _ptr(vq), _ptr(vs),
+                            lr, beta1, beta2, eps, weight_decay, step, _stream(p.device, stream))
+    _check(st, "fp8_adam_step")
 
 
 def fp8_gemm_blockscaled(a: torch.Tensor, sa: torch.Tensor, sa_kind: int,

@@ -5,6 +5,7 @@
 // launch error as FP8Q_ERR_LAUNCH.  Operation semantics are documented in
 // include/fp8q.h.
 #include <atomic>
+#include <cmath>
 #include <cstring>
 
 #include "fp8q_internal.h"
@@ -208,6 +209,37 @@ int fp8_gemm_e8m0(int64_t M, int64_t N, int64_t K,
     if (!fp8q::launch_gemm_e8m0(M, N, K, a, lda, ea, ldea, b, ldb, b_layout, eb, ldeb, eb_kind, c, ldc,
                                 c_dtype, static_cast<hipStream_t>(stream)))
         return FP8Q_ERR_UNSUPPORTED;
+    return launch_status();
+}
+
+int fp8_adam_step(int64_t n, float* p, const void* g, int g_dtype, uint8_t* mq, float* ms,
+                  uint8_t* vq, float* vs, double lr, double beta1, double beta2, double eps,
+                  double weight_decay, int64_t step, void* stream)
+{
+    if (!dtype_ok(g_dtype)) return FP8Q_ERR_UNSUPPORTED;
+    if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) || step < 1 ||
+        !std::isfinite(lr) || !std::isfinite(eps) || !std::isfinite(weight_decay))
+        return FP8Q_ERR_UNSUPPORTED;
+    if (n < 0) return FP8Q_ERR_SHAPE;
+    if (n == 0) return FP8Q_OK;
+    if (!p || !g || !mq || !ms || !vq || !vs) return FP8Q_ERR_NULL;
+    if (cdiv(n, kTile) >= kMaxIndex) return FP8Q_ERR_SHAPE;
+    if (!aligned16(p) || !aligned16(g) || !aligned16(mq) || !aligned16(vq) ||
+        (reinterpret_cast<uintptr_t>(ms) & 3u) || (reinterpret_cast<uintptr_t>(vs) & 3u))
+        return FP8Q_ERR_ALIGN;
+    int st = check_device();
+    if (st != FP8Q_OK) return st;
+    // derived scalars: computed in double, each rounded once to fp32
+    fp8q::AdamScalars a;
+    a.b1 = (float)beta1;
+    a.b2 = (float)beta2;
+    a.omb1 = (float)(1.0 - beta1);
+    a.omb2 = (float)(1.0 - beta2);
+    a.decay = (float)(1.0 - lr * weight_decay);
+    a.step_size = (float)(lr / (1.0 - std::pow(beta1, (double)step)));
+    a.bc2_sqrt = (float)std::sqrt(1.0 - std::pow(beta2, (double)step));
+    a.eps = (float)eps;
+    fp8q::launch_adam_fp8(n, p, g, g_dtype, mq, ms, vq, vs, a, static_cast<hipStream_t>(stream));
     return launch_status();
 }
 

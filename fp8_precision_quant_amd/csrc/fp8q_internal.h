@@ -56,4 +56,12 @@ void launch_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K, const u
                          const uint8_t* b, const float* sb, void* c, int64_t ldc, int c_dtype,
                          hipStream_t st);
 
+// AdamW with E4M3 moments: the step's fp32 scalars, each derived on the host
+// in double from the hyperparameters and rounded once
+struct AdamScalars {
+    float b1, b2, omb1, omb2, decay, step_size, bc2_sqrt, eps;
+};
+void launch_adam_fp8(int64_t n, float* p, const void* g, int g_dtype, uint8_t* mq, float* ms,
+                     uint8_t* vq, float* vs, const AdamScalars& a, hipStream_t st);
+
 }  // namespace fp8q

@@ -318,6 +318,41 @@ int fp8_gemm_e8m0(int64_t M, int64_t N, int64_t K,
                   const uint8_t* eb, int64_t ldeb, int eb_kind,
                   void* c, int64_t ldc, int c_dtype, void* stream);
 
+/*
+ * fp8_adam_step -- one AdamW step with both moments held in FP8.
+ *
+ * Adam keeps a first and a second moment per parameter, twice the
+ * parameters' memory; held as E4M3 codes with fine-grained scales they take a
+ * quarter of it and barely change convergence (Ling 2.0 FP8 blog, "FP8
+ * Optimizer", after block-wise quantization of optimizer states).  Here each
+ * moment is a flat vector of n E4M3 codes plus one fp32 scale per 128
+ * consecutive elements (the 1x128 tile rule of fp8_quant_blockwise along the
+ * flat vector: s = amax / 448, see Numerics).  The step (decoupled weight
+ * decay, bias-corrected moments), with every fp32 operation rounded once in
+ * this order:
+ *   scalars, computed in double and rounded once to fp32:
+ *     b1 = beta1, b2 = beta2, omb1 = 1 - beta1, omb2 = 1 - beta2,
+ *     decay = 1 - lr * weight_decay, step_size = lr / (1 - beta1^step),
+ *     bc2_sqrt = sqrt(1 - beta2^step), epsf = eps;
+ *   per element:  m0 = dec(mq) * ms[i/128];  v0 = dec(vq) * vs[i/128];
+ *     p = p * decay;  m = b1 * m0 + omb1 * g;  v = b2 * v0 + (omb2 * g) * g;
+ *     p = p - step_size * (m / (sqrt(v) / bc2_sqrt + epsf));
+ *   then m and v are re-quantized (codes into mq / vq, scales into ms / vs).
+ *  n        : number of parameters (any n >= 0; the last block may be short).
+ *  p        : fp32 parameters [n], updated in place.
+ *  g        : gradient [n], g_dtype FP8Q_F32 or FP8Q_BF16.
+ *  mq, ms   : first moment: codes [n], scales [ceil(n/128)], updated in place.
+ *  vq, vs   : second moment, likewise.  A fresh state is all zero bytes.
+ *  step     : the step number t >= 1 (bias correction).
+ * p, g, mq and vq must be 16-byte aligned, ms and vs 4-byte aligned.
+ * beta1 or beta2 outside [0, 1), step < 1 or a non-finite lr, eps or
+ * weight_decay: FP8Q_ERR_UNSUPPORTED.  eps = 0 with a zero second moment
+ * gives NaN, as the textbook step does.
+ */
+int fp8_adam_step(int64_t n, float* p, const void* g, int g_dtype, uint8_t* mq, float* ms,
+                  uint8_t* vq, float* vs, double lr, double beta1, double beta2, double eps,
+                  double weight_decay, int64_t step, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* fp8q_status_string(int status);
 

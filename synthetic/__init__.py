@@ -20,6 +20,10 @@ Workloads (shapes and distributions; the pages give no dataset for this path):
   without replacement), groups padded with zero rows to a multiple of 128.
 * long-K: x [16384 x 8192] bf16 with per-row log-normal magnitude,
   x[m,k] = exp(2 u_m) z_mk; W [8192 x 8192] bf16 ~N(0, 0.02).
+* optimizer step: fp32 parameters ~N(0, 0.02) (the MLP weight's size by
+  default), gradients 1e-3 N(0,1) with the backward's heavy tail, and earlier
+  moments m ~ 1e-3 N(0,1), v = (1e-3 z)^2 (fp32 values; each side encodes
+  them itself).
 """
 from __future__ import annotations
 
@@ -181,3 +185,12 @@ def sample_rows(M: int, n: int, seed: int) -> np.ndarray:
     """n distinct sorted row indices of [0, M), seeded."""
     n = min(n, M)
     return np.sort(rng(seed).permutation(M)[:n])
+
+
+def adam_inputs(n=14336 * 4096, seed=601):
+    """(p fp32 [n], g fp32 [n], m fp32 [n], v fp32 [n]) for an optimizer step."""
+    p = normal_f32((n,), seed, 0.02)
+    g = heavy_tail_f32(normal_f32((n,), seed + 1, 1e-3), 0.001, seed + 2)
+    m = normal_f32((n,), seed + 3, 1e-3)
+    v = np.square(normal_f32((n,), seed + 4, 1e-3))
+    return p, g, m, v

@@ -25,7 +25,7 @@ def test_header_declares_the_entry_points():
     assert names == sorted(["fp8_quant_blockwise", "fp8_quant_transpose", "fp8_gemm_blockscaled",
                             "fp8_gemm_blockscaled_e4m3", "fp8_grouped_gemm", "fp8_grouped_gemm_dgrad", "fp8_grouped_gemm_wgrad",
                             "fp8_quant_blockwise_e8m0", "fp8_quant_transpose_e8m0", "fp8_gemm_e8m0",
-                            "fp8q_status_string"])
+                            "fp8_adam_step", "fp8q_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -276,3 +276,27 @@ def test_gemm_e8m0_validation():
     assert call(a10=A16 + 1) == fq.ERR_ALIGN
     assert call(a3=MIS) == fq.ERR_ALIGN
     assert call(a13=A16 + 4) == fq.ERR_ALIGN
+
+
+def test_adam_validation():
+    f = L.fp8_adam_step
+    # n, p, g, g_dtype, mq, ms, vq, vs, lr, beta1, beta2, eps, wd, step, stream
+    base = [1000, A16, A16, fq.BF16, A16, A16, A16, A16, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, None]
+    def call(**ch):
+        a = list(base)
+        for i, v in ch.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a3=7) == fq.ERR_UNSUPPORTED
+    assert call(a9=1.0) == fq.ERR_UNSUPPORTED               # beta1 outside [0, 1)
+    assert call(a10=-0.1) == fq.ERR_UNSUPPORTED
+    assert call(a13=0) == fq.ERR_UNSUPPORTED                # step < 1: no bias correction
+    assert call(a8=float("nan")) == fq.ERR_UNSUPPORTED
+    assert call(a11=float("inf")) == fq.ERR_UNSUPPORTED
+    assert call(a0=-1) == fq.ERR_SHAPE
+    assert call(a0=0, a1=None) == fq.OK                      # nothing to update
+    assert call(a1=None) == fq.ERR_NULL
+    assert call(a7=None) == fq.ERR_NULL
+    assert call(a2=MIS) == fq.ERR_ALIGN
+    assert call(a4=A16 + 8) == fq.ERR_ALIGN
+    assert call(a5=A16 + 2) == fq.ERR_ALIGN
