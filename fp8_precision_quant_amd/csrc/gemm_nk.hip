@@ -468,10 +468,14 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     // the LDS reads of one chunk (addresses rebuilt from the lane id)
     // B fragments of the chunk in stage st: the wave's own 64 columns.  For
     // [N][K] B those are exactly the B rows this wave loaded, so they may be
-    // read as soon as its own loads have landed; [K][N] B rows are loaded
-    // across all columns by every wave of the group, so those are read after
-    // the phase barrier like A.
-    constexpr bool kEarlyB = !B_KN;
+    // read as soon as its own loads have landed, right after the wave's
+    // compute phase; that pays only where the compute phase is short (scaled
+    // MFMAs, no scale FMAs).  Otherwise, and for [K][N] B (rows loaded
+    // across all columns by every wave of the group), B is read after the
+    // phase barrier like A.  (Per-wave s_memtime stamps, forward shape: the
+    // compute phase with fp32 scales is ~1360 cycles and the early read
+    // ~350 more, both on the phase's critical path.)
+    constexpr bool kEarlyB = !B_KN && P2;
     auto read_b = [&](int st, Frags& f) {
         int l = lane;
         asm volatile("" : "+v"(l));
@@ -678,9 +682,14 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
             for (int c = grp; c < KB; c += 2) {
                 if (!kEarlyB) wait_vm<0>();
                 bar();
-                if (c + 2 < KB) issue(c + 2);
+                // the fragment reads go first: they complete while the loads
+                // of chunk c + 2 are being issued (issuing them waits on the
+                // CU's vector-memory queue, ~850 cycles per chunk per wave)
                 if (!kEarlyB) read_b(c % kStages, f);
                 read_a(c % kStages, f, c);
+                __builtin_amdgcn_sched_barrier(0);
+                if (c + 2 < KB) issue(c + 2);
+                __builtin_amdgcn_sched_barrier(0);
                 reads_wait(f);
                 // (groups of K are whole 128-token chunks: no partial chunk)
                 if (GMODE != 2 && c == KB - 1 && k_tail < TBK) mask_k_tail(f);
