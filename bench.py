@@ -273,29 +273,6 @@ def main():
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
 
-    # timed region 1b (reported beside the value): the same step captured
-    # once as a HIP graph (all seven launches, nothing else) and replayed K
-    # times, bracketed the same way; replays skip the per-launch host work
-    graph_ms = None
-    graph_note = None
-    try:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-        g0 = torch.cuda.Event(enable_timing=True)
-        g1 = torch.cuda.Event(enable_timing=True)
-        g0.record(stream)
-        for _ in range(args.steps):
-            graph.replay()
-        g1.record(stream)
-        torch.cuda.synchronize()
-        graph_ms = g0.elapsed_time(g1) / args.steps
-    except RuntimeError as e:   # capture unavailable: the eager figure stands
-        graph_note = "graph capture failed: %s" % e
-    eager_ms_per_step = ms_per_step
 
     # timed region 2: the same K steps with an event pair around every launch
     # (on the launch stream) for per-kernel durations; events add a few us to
@@ -473,10 +450,6 @@ def main():
         "kernels": breakdown,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
-        "step_timing": {"value_from": "eager launches",
-                        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
-                        "eager_ms_per_step": round(eager_ms_per_step, 4),
-                        "note": graph_note},
         "hbm_copy_GBps": hbm_copy,
         "moe_grouped": moe,
         "fwd_quantize_on_store": fused,
