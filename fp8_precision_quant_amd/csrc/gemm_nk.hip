@@ -474,8 +474,12 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     // across all columns by every wave of the group), B is read after the
     // phase barrier like A.  (Per-wave s_memtime stamps, forward shape: the
     // compute phase with fp32 scales is ~1360 cycles and the early read
-    // ~350 more, both on the phase's critical path.)
-    constexpr bool kEarlyB = !B_KN && P2;
+    // ~350 more, both on the phase's critical path.)  Which order wins was
+    // measured per mode: the quantize-on-store output keeps the early read
+    // (+19% without it), and it and the scaled-MFMA dgrad keep issuing the
+    // loads before the reads (+4% for that dgrad otherwise).
+    constexpr bool kEarlyB = !B_KN && (P2 || OUT == OUT_E4M3);
+    constexpr bool kReadsFirst = OUT != OUT_E4M3 && !(P2 && B_KN);
     auto read_b = [&](int st, Frags& f) {
         int l = lane;
         asm volatile("" : "+v"(l));
@@ -685,10 +689,11 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
                 // the fragment reads go first: they complete while the loads
                 // of chunk c + 2 are being issued (issuing them waits on the
                 // CU's vector-memory queue, ~850 cycles per chunk per wave)
+                if (!kReadsFirst && c + 2 < KB) issue(c + 2);
                 if (!kEarlyB) read_b(c % kStages, f);
                 read_a(c % kStages, f, c);
                 __builtin_amdgcn_sched_barrier(0);
-                if (c + 2 < KB) issue(c + 2);
+                if (kReadsFirst && c + 2 < KB) issue(c + 2);
                 __builtin_amdgcn_sched_barrier(0);
                 reads_wait(f);
                 // (groups of K are whole 128-token chunks: no partial chunk)
