@@ -233,6 +233,37 @@ def test_mlp_forward_full_size_sampled_rows():
     _parity(qx, sx, "row", qw, sw, "block", "NK", rows=rows)
 
 
+def test_e4m3_output_mlp_full_size_sampled_rows():
+    """Quantize-on-store at the forward workload's full size (y = x W^T,
+    M = 4096, N = 14336, K = 4096, the launch the bench times): codes and
+    1x128 scales byte-identical, over the whole output, to the GPU quantizer
+    applied to the same GEMM's fp32 output; on sampled rows, a valid
+    quantization of the oracle's result (scale within the GEMM tolerance of
+    amax / 448, each dequantized code within half an E4M3 step plus it)."""
+    x, w, qx, sx, qw, sw = _quantized_mlp()
+    A, SA, B, SB = to_dev(qx), to_dev(sx), to_dev(qw), to_dev(sw)
+    q, qs = fq.fp8_gemm_blockscaled_e4m3(A, SA, fq.ROW_1x128, B, SB, fq.BLOCK_128x128, fq.B_NK)
+    c = fq.fp8_gemm_blockscaled(A, SA, fq.ROW_1x128, B, SB, fq.BLOCK_128x128, fq.B_NK,
+                                out_dtype=torch.float32)
+    rq, rs = fq.fp8_quant_blockwise(c, fq.ROW_1x128)
+    torch.cuda.synchronize()
+    assert torch.equal(q, rq)
+    assert torch.equal(qs.view(torch.int32), rs.view(torch.int32))
+    rows = synthetic.sample_rows(qx.shape[0], 16, 63)
+    ridx = torch.from_numpy(rows.astype(np.int64)).to(DEV)
+    qh, qsh = host(q.index_select(0, ridx)), host(qs.index_select(0, ridx))
+    co = oracle.gemm_blockscaled(qx, sx, "row", qw, sw, "block", "NK", rows=rows).astype(np.float64)
+    _, R = oracle.gemm_blockscaled(qx, sx, "row", qw, sw, "block", "NK", rows=rows, f64=True)
+    n, N = co.shape
+    amax_o = np.abs(co).reshape(n, N // 128, 128).max(axis=2)
+    tol_t = 1e-3 * R.reshape(n, N // 128, 128).max(axis=2)
+    assert np.all(np.abs(qsh.astype(np.float64) * 448 - amax_o) <= tol_t * 1.0001 + 1e-30)
+    s_full = np.repeat(qsh.astype(np.float64), 128, axis=1)
+    deq = oracle.e4m3_decode(qh).astype(np.float64) * s_full
+    half_step = np.maximum(np.abs(co) * 2.0 ** -4, s_full * 2.0 ** -10)
+    assert np.all(np.abs(deq - co) <= half_step * 1.0001 + 1e-3 * R * 2 + 1e-30)
+
+
 def test_mlp_backward_full_size_sampled_rows():
     x, w, _, _, qw, sw = _quantized_mlp()
     dy = synthetic.mlp_backward_dy()
