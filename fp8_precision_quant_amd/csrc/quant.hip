@@ -128,19 +128,22 @@ __device__ __forceinline__ void raw_f32(const Raw8<float>& r, int64_t c, int64_t
 // 1x128 row tiles
 // ---------------------------------------------------------------------------
 // A 16-lane DPP row owns one tile (8 elements per lane).  A 256-thread
-// workgroup covers 16 consecutive tiles per step and runs kRowUnroll steps
-// with all loads issued first, so each lane keeps kRowUnroll 16-byte loads
-// (32 for fp32 input) in flight.
+// workgroup covers 16 consecutive tiles per step and runs U steps with all
+// loads issued first, so each lane keeps U 16-byte loads (2U for fp32 input)
+// in flight.  U = 1 (more, shorter workgroups) is fastest up to ~2^19 tiles
+// (x 4096 x 4096: 12 us against 15 us with U = 4), U = 2 above (16384 x 8192:
+// 74 us against 77 us).
 
 constexpr int kRowThreads = 256;
-constexpr int kRowUnroll = 4;
-constexpr int kRowTilesPerBlock = (kRowThreads / 16) * kRowUnroll;
+constexpr uint32_t kRowSmallTiles = 1u << 19;
 
-template <typename T, typename S>
+template <typename T, typename S, int U>
 __global__ __launch_bounds__(kRowThreads) void quant_row_kernel(
     const T* __restrict__ x, int64_t cols, int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
     S* __restrict__ s, int64_t lds, uint32_t total_tiles, FastDiv tiles_per_row)
 {
+    constexpr int kRowUnroll = U;
+    constexpr int kRowTilesPerBlock = (kRowThreads / 16) * kRowUnroll;
     const int lane16 = threadIdx.x & 15;
     const int group = threadIdx.x >> 4;
     const uint32_t base = blockIdx.x * kRowTilesPerBlock;
@@ -337,10 +340,16 @@ static void launch_tiles(const void* xv, int64_t rows, int64_t cols, int64_t ldx
     const int64_t tiles_c = (cols + kTile - 1) / kTile;
     const int64_t cus = device_cu_count();
     if (kind == FP8Q_ROW_1x128) {
-        uint32_t total = (uint32_t)(rows * tiles_c);
-        uint32_t blocks = (total + kRowTilesPerBlock - 1) / kRowTilesPerBlock;
-        hipLaunchKernelGGL((quant_row_kernel<T, S>), dim3(blocks), dim3(kRowThreads), 0, st, x, cols,
-                           ldx, q, ldq, s, lds, total, make_fastdiv((uint32_t)tiles_c));
+        const uint32_t total = (uint32_t)(rows * tiles_c);
+        if (total <= kRowSmallTiles) {
+            const uint32_t blocks = (total + 15) / 16;
+            hipLaunchKernelGGL((quant_row_kernel<T, S, 1>), dim3(blocks), dim3(kRowThreads), 0, st, x, cols,
+                               ldx, q, ldq, s, lds, total, make_fastdiv((uint32_t)tiles_c));
+        } else {
+            const uint32_t blocks = (total + 31) / 32;
+            hipLaunchKernelGGL((quant_row_kernel<T, S, 2>), dim3(blocks), dim3(kRowThreads), 0, st, x, cols,
+                               ldx, q, ldq, s, lds, total, make_fastdiv((uint32_t)tiles_c));
+        }
     } else {
         const uint32_t total = (uint32_t)(tiles_c * ((rows + kTile - 1) / kTile));
         // two resident workgroups per CU (about 220 VGPRs per lane)
