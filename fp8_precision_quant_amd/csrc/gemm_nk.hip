@@ -476,10 +476,10 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     // compute phase with fp32 scales is ~1360 cycles and the early read
     // ~350 more, both on the phase's critical path.)  Which order wins was
     // measured per mode: the quantize-on-store output keeps the early read
-    // (+19% without it), and it and the scaled-MFMA dgrad keep issuing the
-    // loads before the reads (+4% for that dgrad otherwise).
+    // (+19% without it), and the scaled-MFMA dgrad keeps issuing the loads
+    // before the reads (+4% for it otherwise).
     constexpr bool kEarlyB = !B_KN && (P2 || OUT == OUT_E4M3);
-    constexpr bool kReadsFirst = OUT != OUT_E4M3 && !(P2 && B_KN);
+    constexpr bool kReadsFirst = !(P2 && B_KN);
     auto read_b = [&](int st, Frags& f) {
         int l = lane;
         asm volatile("" : "+v"(l));
