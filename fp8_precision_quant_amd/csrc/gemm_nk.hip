@@ -480,6 +480,15 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     // before the reads (+4% for it otherwise).
     constexpr bool kEarlyB = !B_KN && (P2 || OUT == OUT_E4M3);
     constexpr bool kReadsFirst = !(P2 && B_KN);
+    // Wave priority between the two groups on a SIMD (each SIMD holds one
+    // wave of each).  The instruction arbiter otherwise favours the older
+    // waves (group 0), so group 1's read phase ran ~300 cycles longer than
+    // group 0's.  With a uniform B scale the read phase is the longer one
+    // and the reading wave is raised (forward -6%, dgrad -4%); with row
+    // scales the two scale operations per output make the compute phase
+    // the longer one and the computing wave is raised (wgrad -2%).  The
+    // scaled-MFMA and quantize-on-store kernels measured no difference.
+    constexpr int kPrio = (P2 || OUT == OUT_E4M3) ? 0 : (SB_MODE == SB_ROW ? 2 : 1);
     auto read_b = [&](int st, Frags& f) {
         int l = lane;
         asm volatile("" : "+v"(l));
@@ -686,6 +695,8 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
             for (int c = grp; c < KB; c += 2) {
                 if (!kEarlyB) wait_vm<0>();
                 bar();
+                if (kPrio == 1) __builtin_amdgcn_s_setprio(1);
+                if (kPrio == 2) __builtin_amdgcn_s_setprio(0);
                 // the fragment reads go first: they complete while the loads
                 // of chunk c + 2 are being issued (issuing them waits on the
                 // CU's vector-memory queue, ~850 cycles per chunk per wave)
@@ -698,6 +709,8 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
                 reads_wait(f);
                 // (groups of K are whole 128-token chunks: no partial chunk)
                 if (GMODE != 2 && c == KB - 1 && k_tail < TBK) mask_k_tail(f);
+                if (kPrio == 1) __builtin_amdgcn_s_setprio(0);
+                if (kPrio == 2) __builtin_amdgcn_s_setprio(1);
                 bar();
                 compute(f, c);
                 if (kEarlyB && c + 2 < KB) {
@@ -708,6 +721,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
             }
             if (q == KB) bar();
         }
+        if (kPrio == 2) __builtin_amdgcn_s_setprio(0);
         // Add the two groups' halves: group 0 finishes rows [0, 64), group 1
         // rows [64, 128).  Each wave sends the other half to its partner (the
         // wave of the other group with the same columns) through a 16 KB slot
