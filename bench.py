@@ -6,10 +6,10 @@ operands on the MLP up-projection shape (x [4096 x 4096] bf16 ~N(0,1),
 W [14336 x 4096] bf16 ~N(0,0.02), dy [4096 x 14336] bf16 ~1e-3 N(0,1) with
 0.1% heavy-tailed outliers):
 
-  forward   qx,sx   = quant 1x128 (x)              y  = gemm(qx, qW^T)   bf16 out
-            qW,sW   = quant 128x128 (W)
+  forward   x       -> quant + transpose (rows and columns; one read of x,
+                       the transposed codes are kept for the backward)
+            qW,sW   = quant 128x128 (W)          y  = gemm(qx, qW^T)   bf16 out
   backward  dy      -> quant + transpose (rows and columns)
-            x       -> transposed quantization (columns)
             dx = gemm(q_row(dy), qW stored [N][K] read as KN)          bf16 out
             dW = gemm(q_colT(dy), q_colT(x), row x row scales)          fp32 out
 
@@ -226,8 +226,8 @@ def main():
     gemm_flops = 2.0 * M * N * K
     # algorithmic bytes: what each kernel must read and write at least
     ops = [
-        ("quant_1x128 x", lambda: fq.fp8_quant_blockwise(x, fq.ROW_1x128, q=qx, s=sx),
-         "hbm", M * K * 2 + M * K + M * KB * 4),
+        ("quant_transpose x", lambda: fq.fp8_quant_transpose(x, out=(qx, sx, qxT, sxT)),
+         "hbm", M * K * 2 + 2 * M * K + 4 * (M * KB + K * MB)),
         ("quant_128x128 W", lambda: fq.fp8_quant_blockwise(w, fq.BLOCK_128x128, q=qw, s=sw),
          "hbm", N * K * 2 + N * K + NB * KB * 4),
         ("gemm fwd y=xW^T", lambda: fq.fp8_gemm_blockscaled(qx, sx, fq.ROW_1x128, qw, sw,
@@ -235,9 +235,6 @@ def main():
          "mfma", gemm_flops),
         ("quant_transpose dy", lambda: fq.fp8_quant_transpose(dy, out=(qdy, sdy, qdyT, sdyT)),
          "hbm", M * N * 2 + 2 * M * N + 4 * (M * NB + N * MB)),
-        ("quant_transpose x (columns)", lambda: fq.fp8_quant_transpose(
-            x, rows_out=False, out=(None, None, qxT, sxT)),
-         "hbm", M * K * 2 + M * K + 4 * K * MB),
         ("gemm dgrad dx=dyW", lambda: fq.fp8_gemm_blockscaled(qdy, sdy, fq.ROW_1x128, qw, sw,
                                                              fq.BLOCK_128x128, fq.B_KN, c=dx),
          "mfma", gemm_flops),
@@ -246,8 +243,8 @@ def main():
          "mfma", gemm_flops),
     ]
 
-    group_of = {"quant_1x128 x": "quant", "quant_128x128 W": "quant",
-                "quant_transpose dy": "quant_transpose", "quant_transpose x (columns)": "quant_transpose"}
+    group_of = {"quant_transpose x": "quant_transpose", "quant_128x128 W": "quant",
+                "quant_transpose dy": "quant_transpose"}
 
     def step():
         for _, fn, _, _ in ops:
@@ -351,15 +348,13 @@ def main():
         return torch.empty((rows, (cols + 3) // 4 * 4), dtype=u8, device=dev)[:, :cols]
     ex, ew, edy, edyT, exT = e8(M, KB), e8(NB, KB), e8(M, NB), e8(N, MB), e8(K, MB)
     p2_ops = [
-        ("quant_1x128 x", lambda: fq.fp8_quant_blockwise_e8m0(x, fq.ROW_1x128, q=qx, e=ex),
-         M * K * 2 + M * K + M * KB),
+        ("quant_transpose x", lambda: fq.fp8_quant_transpose_e8m0(x, out=(qx, ex, qxT, exT)),
+         M * K * 2 + 2 * M * K + M * KB + K * MB),
         ("quant_128x128 W", lambda: fq.fp8_quant_blockwise_e8m0(w, fq.BLOCK_128x128, q=qw, e=ew),
          N * K * 2 + N * K + NB * KB),
         ("gemm fwd y=xW^T", lambda: fq.fp8_gemm_e8m0(qx, ex, qw, ew, fq.BLOCK_128x128, fq.B_NK, c=y), None),
         ("quant_transpose dy", lambda: fq.fp8_quant_transpose_e8m0(dy, out=(qdy, edy, qdyT, edyT)),
          M * N * 2 + 2 * M * N + M * NB + N * MB),
-        ("quant_transpose x (columns)", lambda: fq.fp8_quant_transpose_e8m0(
-            x, rows_out=False, out=(None, None, qxT, exT)), M * K * 2 + M * K + K * MB),
         ("gemm dgrad dx=dyW", lambda: fq.fp8_gemm_e8m0(qdy, edy, qw, ew, fq.BLOCK_128x128, fq.B_KN, c=dx), None),
         ("gemm wgrad dW=dy^T x", lambda: fq.fp8_gemm_e8m0(qdyT, edyT, qxT, exT, fq.ROW_1x128, fq.B_NK, c=dW),
          None),
