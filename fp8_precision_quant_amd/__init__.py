@@ -92,6 +92,77 @@ def _stream(device: torch.device, stream) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+# ---------------------------------------------------------------------------
+# argument checks: every tensor handed to the library must be a GPU tensor on
+# the device the work is enqueued on, of the dtype the kernel reads, and at
+# least as large as the extents the kernel derives from the sizes (the kernels
+# trust those extents).  Violations raise ValueError before any launch.
+# ---------------------------------------------------------------------------
+
+_CODE_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _device(first: torch.Tensor, stream) -> torch.device:
+    """The device the call runs on: the given stream's, else the first operand's."""
+    dev = getattr(stream, "device", None)
+    dev = torch.device(dev) if dev is not None else first.device
+    if dev.type != "cuda":
+        raise ValueError("operands must be GPU tensors, got a tensor on %s" % dev)
+    return dev
+
+
+def _on(dev: torch.device, **tensors) -> None:
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise ValueError("%s must be a torch.Tensor" % name)
+        if t.device.type != "cuda" or (dev.index is not None and t.device.index != dev.index):
+            raise ValueError("%s is on %s, the call runs on %s" % (name, t.device, dev))
+
+
+def _dtype(name: str, t: Optional[torch.Tensor], allowed) -> None:
+    if t is not None and t.dtype not in allowed:
+        raise ValueError("%s must be %s, got %s" % (name, " or ".join(str(a) for a in allowed), t.dtype))
+
+
+def _min_shape(name: str, t: torch.Tensor, rows: int, cols: int) -> None:
+    """A 2-D grid with at least `rows` x `cols` entries (row stride from _ld)."""
+    if t.dim() != 2 or t.size(0) < rows or t.size(1) < cols:
+        raise ValueError("%s must be at least [%d, %d], got %s" % (name, rows, cols, tuple(t.shape)))
+
+
+def _shape(name: str, t: torch.Tensor, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _a_scales(name: str, t: torch.Tensor, kind: int, M: int, KB: int) -> int:
+    """Scale grid of A (1x128 rows or one per tensor); returns its row stride."""
+    if kind == TENSOR:
+        if t.numel() < 1:
+            raise ValueError("%s: a per-tensor scale needs one element" % name)
+        return _ld(t) if t.dim() == 2 else 1
+    _min_shape(name, t, M, KB)
+    return _ld(t)
+
+
+def _b_scales(name: str, t: torch.Tensor, kind: int, layout: int, N: int, KB: int) -> int:
+    """Scale grid of B for `kind` and `layout`; returns its row stride."""
+    NB = _cdiv(N, TILE)
+    if kind == TENSOR:
+        if t.numel() < 1:
+            raise ValueError("%s: a per-tensor scale needs one element" % name)
+        return _ld(t) if t.dim() == 2 else 1
+    if kind == ROW_1x128:
+        _min_shape(name, t, N, KB)
+    elif layout == B_NK:
+        _min_shape(name, t, NB, KB)
+    else:
+        _min_shape(name, t, KB, NB)
+    return _ld(t)
+
+
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
@@ -130,13 +201,26 @@ def fp8_quant_blockwise(x: torch.Tensor, kind: int = ROW_1x128, q: Optional[torc
     s[ceil(rows/128), ceil(cols/128)]; TENSOR -> s[1, 1].
     """
     rows, cols = x.shape
+    dev = _device(x, stream)
+    _on(dev, x=x, q=q, s=s)
+    _dtype("x", x, (torch.bfloat16, torch.float32))
+    if kind not in (ROW_1x128, BLOCK_128x128, TENSOR):
+        raise ValueError("unknown scale kind %r" % (kind,))
+    shape = {ROW_1x128: (rows, _cdiv(cols, TILE)),
+             BLOCK_128x128: (_cdiv(rows, TILE), _cdiv(cols, TILE)),
+             TENSOR: (1, 1)}[kind]
     if q is None:
         q = _empty_aligned(rows, cols, torch.uint8, x.device, 16)
     if s is None:
-        shape = {ROW_1x128: (rows, _cdiv(cols, TILE)),
-                 BLOCK_128x128: (_cdiv(rows, TILE), _cdiv(cols, TILE)),
-                 TENSOR: (1, 1)}[kind]
         s = torch.empty(shape, dtype=torch.float32, device=x.device)
+    _dtype("q", q, _CODE_DTYPES)
+    _dtype("s", s, (torch.float32,))
+    _shape("q", q, (rows, cols))
+    if kind == TENSOR:
+        if s.numel() < 1:
+            raise ValueError("s: a per-tensor scale needs one element")
+    else:
+        _min_shape("s", s, *shape)
     st = _lib.fp8_quant_blockwise(_ptr(x), _dtype_code(x), rows, cols, _ld(x), kind,
                                   _ptr(q), _ld(q), _ptr(s), _ld(s) if s.dim() == 2 else 1,
                                   _stream(x.device, stream))
@@ -144,11 +228,30 @@ def fp8_quant_blockwise(x: torch.Tensor, kind: int = ROW_1x128, q: Optional[torc
     return q, s
 
 
+def _transpose_outputs(dev, x, q_row, s_row, q_colT, s_colT, scale_dtypes, sname="s") -> None:
+    R, C = x.shape
+    _on(dev, x=x, q_row=q_row, s_row=s_row, q_colT=q_colT, s_colT=s_colT)
+    for name, q in (("q_row", q_row), ("q_colT", q_colT)):
+        _dtype(name, q, _CODE_DTYPES)
+    for name, t in ((sname + "_row", s_row), (sname + "_colT", s_colT)):
+        _dtype(name, t, scale_dtypes)
+    if (q_row is None) != (s_row is None) or (q_colT is None) != (s_colT is None):
+        raise ValueError("each output pair (codes, scales) is given or skipped as a whole")
+    if q_row is not None:
+        _shape("q_row", q_row, (R, C))
+        _min_shape(sname + "_row", s_row, R, _cdiv(C, TILE))
+    if q_colT is not None:
+        _shape("q_colT", q_colT, (C, R))
+        _min_shape(sname + "_colT", s_colT, C, _cdiv(R, TILE))
+
+
 def fp8_quant_transpose(x: torch.Tensor, rows_out: bool = True, cols_out: bool = True,
                         out: Optional[tuple] = None, stream=None):
     """One read of ``x[R, C]`` -> (q_row[R, C], s_row[R, ceil(C/128)],
     q_colT[C, R], s_colT[C, ceil(R/128)]); a skipped pair is returned as None."""
     R, C = x.shape
+    dev = _device(x, stream)
+    _dtype("x", x, (torch.bfloat16, torch.float32))
     if out is not None:
         q_row, s_row, q_colT, s_colT = out
     else:
@@ -156,6 +259,7 @@ def fp8_quant_transpose(x: torch.Tensor, rows_out: bool = True, cols_out: bool =
         s_row = torch.empty((R, _cdiv(C, TILE)), dtype=torch.float32, device=x.device) if rows_out else None
         q_colT = _empty_aligned(C, R, torch.uint8, x.device, 16) if cols_out else None
         s_colT = torch.empty((C, _cdiv(R, TILE)), dtype=torch.float32, device=x.device) if cols_out else None
+    _transpose_outputs(dev, x, q_row, s_row, q_colT, s_colT, (torch.float32,))
     st = _lib.fp8_quant_transpose(
         _ptr(x), _dtype_code(x), R, C, _ld(x),
         _ptr(q_row), _ld(q_row) if q_row is not None else 0,
@@ -178,11 +282,20 @@ def fp8_quant_blockwise_e8m0(x: torch.Tensor, kind: int = ROW_1x128, q: Optional
     BLOCK_128x128 -> e[ceil(rows/128), ceil(cols/128)] (row stride rounded up
     to 4 bytes, as the GEMM reads it)."""
     rows, cols = x.shape
+    dev = _device(x, stream)
+    _on(dev, x=x, q=q, e=e)
+    _dtype("x", x, (torch.bfloat16, torch.float32))
+    if kind not in (ROW_1x128, BLOCK_128x128):
+        raise ValueError("E8M0 scales come in ROW_1x128 or BLOCK_128x128 tiles")
+    r = rows if kind == ROW_1x128 else _cdiv(rows, TILE)
     if q is None:
         q = _empty_aligned(rows, cols, torch.uint8, x.device, 16)
     if e is None:
-        r = rows if kind == ROW_1x128 else _cdiv(rows, TILE)
         e = _empty_aligned(r, _cdiv(cols, TILE), torch.uint8, x.device, 4)
+    _dtype("q", q, _CODE_DTYPES)
+    _dtype("e", e, (torch.uint8,))
+    _shape("q", q, (rows, cols))
+    _min_shape("e", e, r, _cdiv(cols, TILE))
     st = _lib.fp8_quant_blockwise_e8m0(_ptr(x), _dtype_code(x), rows, cols, _ld(x), kind,
                                        _ptr(q), _ld(q), _ptr(e), _ld(e), _stream(x.device, stream))
     _check(st, "fp8_quant_blockwise_e8m0")
@@ -194,6 +307,8 @@ def fp8_quant_transpose_e8m0(x: torch.Tensor, rows_out: bool = True, cols_out: b
     """``fp8_quant_transpose`` with power-of-two scales: (q_row, e_row,
     q_colT, e_colT), the ``e`` grids uint8 E8M0 bytes."""
     R, C = x.shape
+    dev = _device(x, stream)
+    _dtype("x", x, (torch.bfloat16, torch.float32))
     if out is not None:
         q_row, e_row, q_colT, e_colT = out
     else:
@@ -201,6 +316,7 @@ def fp8_quant_transpose_e8m0(x: torch.Tensor, rows_out: bool = True, cols_out: b
         e_row = _empty_aligned(R, _cdiv(C, TILE), torch.uint8, x.device, 4) if rows_out else None
         q_colT = _empty_aligned(C, R, torch.uint8, x.device, 16) if cols_out else None
         e_colT = _empty_aligned(C, _cdiv(R, TILE), torch.uint8, x.device, 4) if cols_out else None
+    _transpose_outputs(dev, x, q_row, e_row, q_colT, e_colT, (torch.uint8,), "e")
     st = _lib.fp8_quant_transpose_e8m0(
         _ptr(x), _dtype_code(x), R, C, _ld(x),
         _ptr(q_row), _ld(q_row) if q_row is not None else 0,
@@ -224,15 +340,28 @@ def fp8_gemm_e8m0(a: torch.Tensor, ea: torch.Tensor, b: torch.Tensor, eb: torch.
     N = b.shape[0] if b_layout == B_NK else b.shape[1]
     if (b.shape[1] if b_layout == B_NK else b.shape[0]) != K:
         raise ValueError("contraction sizes differ: a %s, b %s" % (tuple(a.shape), tuple(b.shape)))
-    if ea.dtype != torch.uint8 or eb.dtype != torch.uint8:
-        raise ValueError("E8M0 scales must be uint8 tensors")
+    dev = _device(a, stream)
+    _on(dev, a=a, ea=ea, b=b, eb=eb, c=c)
+    _dtype("a", a, _CODE_DTYPES)
+    _dtype("b", b, _CODE_DTYPES)
+    _dtype("ea", ea, (torch.uint8,))
+    _dtype("eb", eb, (torch.uint8,))
+    if b_layout not in (B_NK, B_KN) or eb_kind not in (ROW_1x128, BLOCK_128x128):
+        raise ValueError("unknown layout or scale kind")
+    KB = _cdiv(K, TILE)
+    if K > 0:
+        _min_shape("ea", ea, M, KB)
+        ldeb = _b_scales("eb", eb, eb_kind, b_layout, N, KB)
+    else:
+        ldeb = _ld(eb)
     if c is None:
         c = _empty_aligned(M, N, out_dtype, a.device, 16 // (4 if out_dtype == torch.float32 else 2))
     if c.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("output dtype must be float32 or bfloat16")
+    _shape("c", c, (M, N))
     cd = F32 if c.dtype == torch.float32 else BF16
     st = _lib.fp8_gemm_e8m0(M, N, K, _ptr(a), _ld(a), _ptr(ea), _ld(ea),
-                            _ptr(b), _ld(b), b_layout, _ptr(eb), _ld(eb), eb_kind,
+                            _ptr(b), _ld(b), b_layout, _ptr(eb), ldeb, eb_kind,
                             _ptr(c), _ld(c), cd, _stream(a.device, stream))
     _check(st, "fp8_gemm_e8m0")
     return c
@@ -258,15 +387,35 @@ def fp8_adam_step(p: torch.Tensor, g: torch.Tensor, state, lr: float, beta1: flo
     if g.numel() != n or mq.numel() != n or vq.numel() != n or ms.numel() != _cdiv(n, TILE) \
             or vs.numel() != ms.numel():
         raise ValueError("parameter, gradient and state sizes differ")
+    dev = _device(p, stream)
+    _on(dev, p=p, g=g, mq=mq, ms=ms, vq=vq, vs=vs)
     for t in (p, g, mq, ms, vq, vs):
         if not t.is_contiguous():
             raise ValueError("fp8_adam_step needs contiguous tensors")
     if p.dtype != torch.float32 or mq.dtype != torch.uint8 or vq.dtype != torch.uint8 \
             or ms.dtype != torch.float32 or vs.dtype != torch.float32:
         raise ValueError("parameters and scales are float32, codes uint8")
+    _dtype("g", g, (torch.float32, torch.bfloat16))
     st = _lib.fp8_adam_step(n, _ptr(p), _ptr(g), _dtype_code(g), _ptr(mq), _ptr(ms), _ptr(vq), _ptr(vs),
                             lr, beta1, beta2, eps, weight_decay, step, _stream(p.device, stream))
     _check(st, "fp8_adam_step")
+
+
+def _gemm_operands(a, sa, sa_kind, b, sb, sb_kind, b_layout, M, N, K, stream):
+    """Checks of a dense GEMM's operands; returns the scale grids' row strides."""
+    dev = _device(a, stream)
+    _on(dev, a=a, sa=sa, b=b, sb=sb)
+    _dtype("a", a, _CODE_DTYPES)
+    _dtype("b", b, _CODE_DTYPES)
+    _dtype("sa", sa, (torch.float32,))
+    _dtype("sb", sb, (torch.float32,))
+    if sa_kind not in (ROW_1x128, TENSOR) or sb_kind not in (ROW_1x128, BLOCK_128x128, TENSOR) \
+            or b_layout not in (B_NK, B_KN):
+        raise ValueError("unknown scale kind or layout")
+    KB = _cdiv(K, TILE)
+    if K == 0:
+        return (_ld(sa) if sa.dim() == 2 else 1), (_ld(sb) if sb.dim() == 2 else 1)
+    return _a_scales("sa", sa, sa_kind, M, KB), _b_scales("sb", sb, sb_kind, b_layout, N, KB)
 
 
 def fp8_gemm_blockscaled(a: torch.Tensor, sa: torch.Tensor, sa_kind: int,
@@ -279,13 +428,14 @@ def fp8_gemm_blockscaled(a: torch.Tensor, sa: torch.Tensor, sa_kind: int,
     N = b.shape[0] if b_layout == B_NK else b.shape[1]
     if (b.shape[1] if b_layout == B_NK else b.shape[0]) != K:
         raise ValueError("contraction sizes differ: a %s, b %s" % (tuple(a.shape), tuple(b.shape)))
+    ldsa, ldsb = _gemm_operands(a, sa, sa_kind, b, sb, sb_kind, b_layout, M, N, K, stream)
     if c is None:
         c = _empty_aligned(M, N, out_dtype, a.device, 16 // (4 if out_dtype == torch.float32 else 2))
-    cd = F32 if c.dtype == torch.float32 else BF16
+    _on(_device(a, stream), c=c)
     if c.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("output dtype must be float32 or bfloat16")
-    ldsa = _ld(sa) if sa.dim() == 2 else 1
-    ldsb = _ld(sb) if sb.dim() == 2 else 1
+    _shape("c", c, (M, N))
+    cd = F32 if c.dtype == torch.float32 else BF16
     st = _lib.fp8_gemm_blockscaled(M, N, K, _ptr(a), _ld(a), _ptr(sa), ldsa, sa_kind,
                                    _ptr(b), _ld(b), b_layout, _ptr(sb), ldsb, sb_kind,
                                    _ptr(c), _ld(c), cd, _stream(a.device, stream))
@@ -303,13 +453,17 @@ def fp8_gemm_blockscaled_e4m3(a: torch.Tensor, sa: torch.Tensor, sa_kind: int,
     N = b.shape[0] if b_layout == B_NK else b.shape[1]
     if (b.shape[1] if b_layout == B_NK else b.shape[0]) != K:
         raise ValueError("contraction sizes differ: a %s, b %s" % (tuple(a.shape), tuple(b.shape)))
+    ldsa, ldsb = _gemm_operands(a, sa, sa_kind, b, sb, sb_kind, b_layout, M, N, K, stream)
     if out is not None:
         q, s = out
     else:
         q = _empty_aligned(M, N, torch.uint8, a.device, 16)
         s = torch.empty((M, _cdiv(N, TILE)), dtype=torch.float32, device=a.device)
-    ldsa = _ld(sa) if sa.dim() == 2 else 1
-    ldsb = _ld(sb) if sb.dim() == 2 else 1
+    _on(_device(a, stream), q=q, s=s)
+    _dtype("q", q, _CODE_DTYPES)
+    _dtype("s", s, (torch.float32,))
+    _shape("q", q, (M, N))
+    _min_shape("s", s, M, _cdiv(N, TILE))
     st = _lib.fp8_gemm_blockscaled_e4m3(M, N, K, _ptr(a), _ld(a), _ptr(sa), ldsa, sa_kind,
                                         _ptr(b), _ld(b), b_layout, _ptr(sb), ldsb, sb_kind,
                                         _ptr(q), _ld(q), _ptr(s), _ld(s), _stream(a.device, stream))
@@ -331,8 +485,20 @@ def fp8_grouped_gemm(a: torch.Tensor, sa: torch.Tensor, group_offsets: torch.Ten
         raise ValueError("group_offsets must be int32 with G+1 entries")
     if not (b.is_contiguous() and sb.is_contiguous() and group_offsets.is_contiguous()):
         raise ValueError("b, sb and group_offsets must be contiguous")
+    dev = _device(a, stream)
+    _on(dev, a=a, sa=sa, group_offsets=group_offsets, b=b, sb=sb, c=c)
+    _dtype("a", a, _CODE_DTYPES)
+    _dtype("b", b, _CODE_DTYPES)
+    _dtype("sa", sa, (torch.float32,))
+    _dtype("sb", sb, (torch.float32,))
+    _min_shape("sa", sa, M_pad, _cdiv(K, TILE))
+    _shape("sb", sb, (G, _cdiv(N, TILE), _cdiv(K, TILE)))
     if c is None:
         c = _empty_aligned(M_pad, N, out_dtype, a.device, 16 // (4 if out_dtype == torch.float32 else 2))
+    if c.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("output dtype must be float32 or bfloat16")
+    _on(dev, c=c)
+    _shape("c", c, (M_pad, N))
     cd = F32 if c.dtype == torch.float32 else BF16
     st = _lib.fp8_grouped_gemm(G, M_pad, N, K, _ptr(a), _ld(a), _ptr(sa), _ld(sa),
                                _ptr(group_offsets), _ptr(b), _ptr(sb), _ptr(c), _ld(c), cd,
@@ -356,8 +522,20 @@ def fp8_grouped_gemm_dgrad(a: torch.Tensor, sa: torch.Tensor, group_offsets: tor
         raise ValueError("group_offsets must be int32 with G+1 entries")
     if not (w.is_contiguous() and sw.is_contiguous() and group_offsets.is_contiguous()):
         raise ValueError("w, sw and group_offsets must be contiguous")
+    dev = _device(a, stream)
+    _on(dev, a=a, sa=sa, group_offsets=group_offsets, w=w, sw=sw, c=c)
+    _dtype("a", a, _CODE_DTYPES)
+    _dtype("w", w, _CODE_DTYPES)
+    _dtype("sa", sa, (torch.float32,))
+    _dtype("sw", sw, (torch.float32,))
+    _min_shape("sa", sa, M_pad, _cdiv(N, TILE))
+    _shape("sw", sw, (G, _cdiv(N, TILE), _cdiv(K, TILE)))
     if c is None:
         c = _empty_aligned(M_pad, K, out_dtype, a.device, 16 // (4 if out_dtype == torch.float32 else 2))
+    if c.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("output dtype must be float32 or bfloat16")
+    _on(dev, c=c)
+    _shape("c", c, (M_pad, K))
     cd = F32 if c.dtype == torch.float32 else BF16
     st = _lib.fp8_grouped_gemm_dgrad(G, M_pad, N, K, _ptr(a), _ld(a), _ptr(sa), _ld(sa),
                                      _ptr(group_offsets), _ptr(w), _ptr(sw), _ptr(c), _ld(c), cd,
@@ -379,8 +557,17 @@ def fp8_grouped_gemm_wgrad(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, s
     G = group_offsets.numel() - 1
     if group_offsets.dtype != torch.int32 or G < 1 or not group_offsets.is_contiguous():
         raise ValueError("group_offsets must be a contiguous int32 tensor with G+1 entries")
+    dev = _device(a, stream)
+    _on(dev, a=a, sa=sa, b=b, sb=sb, group_offsets=group_offsets, c=c)
+    _dtype("a", a, _CODE_DTYPES)
+    _dtype("b", b, _CODE_DTYPES)
+    _dtype("sa", sa, (torch.float32,))
+    _dtype("sb", sb, (torch.float32,))
+    _min_shape("sa", sa, N, M_pad // TILE)
+    _min_shape("sb", sb, K, M_pad // TILE)
     if c is None:
         c = torch.empty((G, N, K), dtype=torch.float32, device=a.device)
+    _on(dev, c=c)
     if c.dtype != torch.float32 or c.dim() != 3 or c.shape != (G, N, K) or c.stride(0) != N * c.stride(1) \
             or c.stride(2) != 1:
         raise ValueError("c must be float32 [G, N, K] with group stride N * row stride")

@@ -15,6 +15,8 @@ namespace {
 constexpr int64_t kTile = 128;
 constexpr int64_t kMaxGridY = 65535;
 constexpr int64_t kMaxIndex = (int64_t)1 << 31;
+// grouped GEMMs keep the group offsets in LDS
+constexpr int64_t kMaxGroups = 1024;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -325,8 +327,9 @@ int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K,
     if (K > 0 && (!aligned16(a) || !aligned16(b) || lda % 16 || ldb % 16)) return FP8Q_ERR_ALIGN;
     int st = check_device();
     if (st != FP8Q_OK) return st;
-    fp8q::launch_gemm(M, N, K, a, lda, sa, ldsa, sa_kind, b, ldb, b_layout, sb, ldsb, sb_kind, c,
-                      ldc, c_dtype, static_cast<hipStream_t>(stream));
+    if (!fp8q::launch_gemm(M, N, K, a, lda, sa, ldsa, sa_kind, b, ldb, b_layout, sb, ldsb, sb_kind, c,
+                           ldc, c_dtype, static_cast<hipStream_t>(stream)))
+        return FP8Q_ERR_UNSUPPORTED;
     return launch_status();
 }
 
@@ -338,6 +341,7 @@ int fp8_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K,
 {
     if (!dtype_ok(c_dtype)) return FP8Q_ERR_UNSUPPORTED;
     if (G < 1 || M_pad < 0 || N < 0 || K < 0 || M_pad % kTile) return FP8Q_ERR_SHAPE;
+    if (G > kMaxGroups) return FP8Q_ERR_UNSUPPORTED;
     if (M_pad == 0 || N == 0) return FP8Q_OK;
     if (!group_offsets || !c) return FP8Q_ERR_NULL;
     if (K > 0 && (!a || !sa || !b || !sb)) return FP8Q_ERR_NULL;
@@ -349,8 +353,9 @@ int fp8_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K,
     if (reinterpret_cast<uintptr_t>(group_offsets) & 3u) return FP8Q_ERR_ALIGN;
     int st = check_device();
     if (st != FP8Q_OK) return st;
-    fp8q::launch_grouped_gemm(G, M_pad, N, K, a, lda, sa, ldsa, group_offsets, b, sb, c, ldc,
-                              c_dtype, static_cast<hipStream_t>(stream));
+    if (!fp8q::launch_grouped_gemm(G, M_pad, N, K, a, lda, sa, ldsa, group_offsets, b, sb, c, ldc,
+                                   c_dtype, static_cast<hipStream_t>(stream)))
+        return FP8Q_ERR_UNSUPPORTED;
     return launch_status();
 }
 
@@ -362,6 +367,7 @@ int fp8_grouped_gemm_dgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K,
 {
     if (!dtype_ok(c_dtype)) return FP8Q_ERR_UNSUPPORTED;
     if (G < 1 || M_pad < 0 || N < 0 || K < 0 || M_pad % kTile) return FP8Q_ERR_SHAPE;
+    if (G > kMaxGroups) return FP8Q_ERR_UNSUPPORTED;
     if (M_pad == 0 || K == 0) return FP8Q_OK;
     if (!group_offsets || !c) return FP8Q_ERR_NULL;
     if (N > 0 && (!a || !sa || !w || !sw)) return FP8Q_ERR_NULL;
@@ -385,6 +391,7 @@ int fp8_grouped_gemm_wgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K,
                            float* c, int64_t ldc, void* stream)
 {
     if (G < 1 || M_pad < 0 || N < 0 || K < 0 || M_pad % kTile) return FP8Q_ERR_SHAPE;
+    if (G > kMaxGroups) return FP8Q_ERR_UNSUPPORTED;
     if (N == 0 || K == 0) return FP8Q_OK;
     if (!group_offsets || !c) return FP8Q_ERR_NULL;
     if (M_pad > 0 && (!a || !sa || !b || !sb)) return FP8Q_ERR_NULL;

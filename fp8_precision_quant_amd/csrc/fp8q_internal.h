@@ -31,7 +31,9 @@ void launch_quant_transpose_e8m0(const void* x, int x_dtype, int64_t rows, int64
                                  uint8_t* q_colT, int64_t ldq_colT, uint8_t* e_colT, int64_t lde_colT,
                                  hipStream_t st);
 
-void launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const float* sa,
+// The GEMM launchers return false (nothing enqueued) for calls the kernel
+// does not cover.
+bool launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const float* sa,
                  int64_t ldsa, int sa_kind, const uint8_t* b, int64_t ldb, int b_layout,
                  const float* sb, int64_t ldsb, int sb_kind, void* c, int64_t ldc, int c_dtype,
                  hipStream_t st);
@@ -51,7 +53,7 @@ bool launch_gemm_e4m3(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t
 bool launch_gemm_e8m0(int64_t M, int64_t N, int64_t K, const uint8_t* a, int64_t lda, const uint8_t* ea,
                       int64_t ldea, const uint8_t* b, int64_t ldb, int b_layout, const uint8_t* eb,
                       int64_t ldeb, int eb_kind, void* c, int64_t ldc, int c_dtype, hipStream_t st);
-void launch_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K, const uint8_t* a,
+bool launch_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K, const uint8_t* a,
                          int64_t lda, const float* sa, int64_t ldsa, const int32_t* offsets,
                          const uint8_t* b, const float* sb, void* c, int64_t ldc, int c_dtype,
                          hipStream_t st);

@@ -916,13 +916,27 @@ bool launch_grouped_wgrad_nk(const GemmArgs& g, hipStream_t st)
     return true;
 }
 
-bool launch_gemm_nk_e8m0(const GemmArgs& g, int sb_mode, bool b_kn, bool out_bf16, hipStream_t st)
+// Every operand of one dense launch must span less than 2 GiB: the kernel
+// addresses them through 32-bit buffer offsets, and reads up to a tile of
+// rows past the end of A, B and the scale grids (clamped to zero by the
+// buffer bounds).  `sbytes` is the size of one scale (4 fp32, 1 E8M0).
+static bool dense_fits(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, int sbytes)
 {
     const int64_t lim = (int64_t)1 << 31;
+    const int64_t pad = 256;
     const int64_t b_rows = b_kn ? g.K : g.N;
-    if (g.M * g.lda >= lim || (b_rows + TBK) * g.ldb >= lim || g.M * g.ldsa >= lim ||
-        (g.N + (int64_t)g.KB) * g.ldsb >= lim || (int64_t)g.KB * TBK >= lim)
-        return false;
+    const int64_t nblocks = (g.N + 127) / 128;
+    int64_t sb_ext = 4;
+    if (sb_mode == SB_ROW) sb_ext = (g.N + pad) * g.ldsb * sbytes;
+    else if (sb_mode == SB_BLOCK) sb_ext = (b_kn ? (int64_t)g.KB + 1 : nblocks + 2) * g.ldsb * sbytes;
+    const int64_t sa_ext = sa_mode == SA_ROW ? (g.M + pad) * g.ldsa * sbytes : 4;
+    return (g.M + pad) * g.lda < lim && (b_rows + pad) * g.ldb < lim && sa_ext < lim && sb_ext < lim &&
+           (int64_t)g.KB * TBK < lim;
+}
+
+bool launch_gemm_nk_e8m0(const GemmArgs& g, int sb_mode, bool b_kn, bool out_bf16, hipStream_t st)
+{
+    if (!dense_fits(g, SA_ROW, sb_mode, b_kn, 1)) return false;
     if (b_kn && sb_mode != SB_BLOCK) return false;
     if (b_kn) {
         if (out_bf16) launch_out<SA_ROW, SB_BLOCK, true, OUT_BF16, 0, true>(g, st);
@@ -939,12 +953,7 @@ bool launch_gemm_nk_e8m0(const GemmArgs& g, int sb_mode, bool b_kn, bool out_bf1
 
 bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, int out, hipStream_t st)
 {
-    // 32-bit buffer offsets: every operand and scale grid must span < 2 GiB
-    const int64_t lim = (int64_t)1 << 31;
-    const int64_t b_rows = b_kn ? g.K : g.N;
-    if (g.M * g.lda >= lim || (b_rows + TBK) * g.ldb >= lim || g.M * g.ldsa * 4 >= lim ||
-        (g.N + (int64_t)g.KB) * g.ldsb * 4 >= lim || (int64_t)g.KB * TBK >= lim)
-        return false;
+    if (!dense_fits(g, sa_mode, sb_mode, b_kn, 4)) return false;
     if (b_kn) {
         if (sb_mode == SB_ROW) return false;
         if (sa_mode == SA_ROW) {

@@ -145,6 +145,10 @@ int fp8_quant_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols, 
  * Typical uses: forward y = x W^T (ROW x BLOCK, NK); dgrad dx = dy W
  * (ROW x BLOCK, KN); wgrad dW = dy^T x (ROW x ROW, NK, operands from
  * fp8_quant_transpose's column outputs).
+ * Operands of 2 GiB or more are handled by several launches over slices of
+ * M (and, for FP8Q_B_NK, of N).  Returns FP8Q_ERR_UNSUPPORTED (nothing
+ * enqueued) if a FP8Q_B_KN operand spans 2 GiB or more, or a single 256-row
+ * slice of an operand does.
  */
 int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K,
                          const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, int sa_kind,
@@ -167,8 +171,8 @@ int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K,
  *                 feeds the optimizer in fp32) is FP8Q_ERR_UNSUPPORTED.
  *  q, ldq       : codes [M][N], ldq >= N (multiple of 16, q 16-byte aligned).
  *  s, lds       : scales s[m*lds + n/128], lds >= ceil(N/128).
- * Returns FP8Q_ERR_UNSUPPORTED (nothing enqueued) if an operand spans 2 GiB
- * or more.
+ * Large operands are sliced as for fp8_gemm_blockscaled, with the same
+ * FP8Q_ERR_UNSUPPORTED cases.
  */
 int fp8_gemm_blockscaled_e4m3(int64_t M, int64_t N, int64_t K,
                               const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, int sa_kind,
@@ -193,7 +197,8 @@ int fp8_gemm_blockscaled_e4m3(int64_t M, int64_t N, int64_t K,
  *  b                : B codes [G][N][K] (each expert NK, row stride K; K % 16 == 0).
  *  sb               : B scales [G][ceil(N/128)][ceil(K/128)], contiguous.
  *  c, ldc, c_dtype  : output [M_pad][N].
- * M_pad must be a multiple of 128.
+ * M_pad must be a multiple of 128.  Returns FP8Q_ERR_UNSUPPORTED (nothing
+ * enqueued) if G > 1024 or an operand spans 2 GiB or more.
  */
 int fp8_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K,
                      const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
@@ -309,8 +314,8 @@ int fp8_quant_transpose_e8m0(const void* x, int x_dtype, int64_t rows, int64_t c
  *  c, ldc, c_dtype  : output [M][N], FP8Q_F32 or FP8Q_BF16.
  * ea and eb must be 4-byte aligned with ldea % 4 == ldeb % 4 == 0
  * (FP8Q_ERR_ALIGN otherwise).  Scale bytes 0 and 255 are outside the
- * contract (the quantizers write 1..247).  Returns FP8Q_ERR_UNSUPPORTED
- * (nothing enqueued) if an operand spans 2 GiB or more.
+ * contract (the quantizers write 1..247).  Large operands are sliced as for
+ * fp8_gemm_blockscaled, with the same FP8Q_ERR_UNSUPPORTED cases.
  */
 int fp8_gemm_e8m0(int64_t M, int64_t N, int64_t K,
                   const uint8_t* a, int64_t lda, const uint8_t* ea, int64_t ldea,

@@ -187,6 +187,13 @@ def sample_rows(M: int, n: int, seed: int) -> np.ndarray:
     return np.sort(rng(seed).permutation(M)[:n])
 
 
+def rows_per_tile(M: int, seed: int, tile: int = 128) -> np.ndarray:
+    """One seeded row index inside every tile of `tile` rows of [0, M), sorted."""
+    g = rng(seed)
+    starts = np.arange(0, M, tile)
+    return starts + g.integers(0, np.minimum(tile, M - starts))
+
+
 def adam_inputs(n=14336 * 4096, seed=601):
     """(p fp32 [n], g fp32 [n], m fp32 [n], v fp32 [n]) for an optimizer step."""
     p = normal_f32((n,), seed, 0.02)

@@ -257,11 +257,12 @@ def test_k_zero_canaries_and_strides():
 # workloads
 # ---------------------------------------------------------------------------
 
-def test_mlp_step_full_size_sampled_rows():
+def test_mlp_step_full_size():
     """MLP up-projection (x [4096x4096], W [14336x4096], dy [4096x14336]) with
     power-of-two scales throughout: the GPU quantizers bit-exact on the whole
-    tensors, then forward, dgrad (W as stored) and wgrad (transposed
-    re-quantized operands) on sampled output rows."""
+    tensors, then forward and dgrad (W as stored) on every output element
+    and wgrad (transposed re-quantized operands) on one row of every
+    128-row tile."""
     x, w = synthetic.mlp_forward()
     dy = synthetic.mlp_backward_dy()
     xd, wd, dyd = to_dev_bf16(x), to_dev_bf16(w), to_dev_bf16(dy)
@@ -275,10 +276,9 @@ def test_mlp_step_full_size_sampled_rows():
     o_dy = oracle.quant_transpose_pow2(dyf)
     for got, want in zip((qx, ex, qxT, exT, qw, ew, qdy, edy, qdyT, edyT), o_x + o_w + o_dy):
         assert np.array_equal(host(got), want)
-    rows = synthetic.sample_rows(4096, 16, 71)
-    _parity(o_x[0], o_x[1], o_w[0], o_w[1], "block", "NK", rows=rows)          # y = x W^T
-    _parity(o_dy[0], o_dy[1], o_w[0], o_w[1], "block", "KN", rows=rows, bf16=False)   # dx = dy W
-    rows = synthetic.sample_rows(14336, 16, 72)
+    _parity(o_x[0], o_x[1], o_w[0], o_w[1], "block", "NK")                       # y = x W^T
+    _parity(o_dy[0], o_dy[1], o_w[0], o_w[1], "block", "KN", bf16=False)           # dx = dy W
+    rows = synthetic.rows_per_tile(14336, 72)
     _parity(o_dy[2], o_dy[3], o_x[2], o_x[3], "row", "NK", rows=rows, bf16=False)     # dW = dy^T x
 
 

@@ -9,7 +9,8 @@ representable cases (a permutation operand, unit codes with power-of-two
 chunk scales) must match exactly.  Every scale mode and layout is covered:
 forward (row x block, B [N][K]), dgrad (row x block, B stored [K][N]),
 wgrad (row x row), per-tensor and mixed, ragged shapes on all three axes,
-K = 0, canaries, and the workloads' full sizes on sampled output rows.
+K = 0, canaries, and the workloads' full sizes (whole outputs for the forward
+and dgrad, one row in every 128-row tile elsewhere).
 """
 import numpy as np
 import pytest
@@ -227,10 +228,12 @@ def _quantized_mlp():
     return x, w, qx, sx, qw, sw
 
 
-def test_mlp_forward_full_size_sampled_rows():
+def test_mlp_forward_full_size_whole_output():
+    """y = x W^T at the forward workload's full size (M = 4096, N = 14336,
+    K = 4096, the launch the bench times): every output element, fp32 and
+    bf16 (each workgroup walks several tiles here)."""
     x, w, qx, sx, qw, sw = _quantized_mlp()
-    rows = synthetic.sample_rows(qx.shape[0], 24, 60)
-    _parity(qx, sx, "row", qw, sw, "block", "NK", rows=rows)
+    _parity(qx, sx, "row", qw, sw, "block", "NK")
 
 
 def test_e4m3_output_mlp_full_size_sampled_rows():
@@ -264,36 +267,53 @@ def test_e4m3_output_mlp_full_size_sampled_rows():
     assert np.all(np.abs(deq - co) <= half_step * 1.0001 + 1e-3 * R * 2 + 1e-30)
 
 
-def test_mlp_backward_full_size_sampled_rows():
+def test_mlp_dgrad_full_size_whole_output():
+    """dx = dy W with W read as stored ([N = 14336][K = 4096] is
+    [contraction][out]): every output element, fp32 and bf16."""
     x, w, _, _, qw, sw = _quantized_mlp()
     dy = synthetic.mlp_backward_dy()
-    q_row, s_row, q_colT, s_colT = oracle.quant_transpose(synthetic.bf16_to_f32(dy))
-    rows = synthetic.sample_rows(q_row.shape[0], 16, 61)
-    # dgrad: dx = dy W with W read as stored ([N=14336][K=4096] is [contraction][out])
-    _parity(q_row, s_row, "row", qw, sw, "block", "KN", rows=rows)
-    # wgrad: dW = dy^T x with both operands re-quantized along tokens
+    q_row, s_row, _, _ = oracle.quant_transpose(synthetic.bf16_to_f32(dy))
+    _parity(q_row, s_row, "row", qw, sw, "block", "KN")
+
+
+def test_mlp_wgrad_full_size_row_per_tile():
+    """dW = dy^T x with both operands re-quantized along tokens (14336 x
+    4096 output): one seeded row in every 128-row tile, fp32 and bf16."""
+    x, _ = synthetic.mlp_forward()
+    dy = synthetic.mlp_backward_dy()
+    _, _, q_colT, s_colT = oracle.quant_transpose(synthetic.bf16_to_f32(dy))
     _, _, qxT, sxT = oracle.quant_transpose(synthetic.bf16_to_f32(x))
-    rows = synthetic.sample_rows(q_colT.shape[0], 16, 62)
+    rows = synthetic.rows_per_tile(q_colT.shape[0], 62)
     _parity(q_colT, s_colT, "row", qxT, sxT, "row", "NK", rows=rows)
 
 
-def test_long_k_blockwise_vs_tensor_sampled_rows():
-    """Long-K stress (K = 8192, log-normal row magnitudes): parity for both
-    scalings on sampled rows, and the pages' claim that fine-grained scaling
-    beats one scale per tensor (less underflow, smaller error vs exact)."""
+def test_long_k_blockwise_vs_tensor_sampled_rows(capsys):
+    """Long-K stress (x [16384 x 8192] with log-normal row magnitudes, K =
+    8192): parity for both scalings on 256 seeded rows, and the pages' claim
+    that fine-grained scaling beats one scale per tensor (less underflow,
+    smaller error against the exact product of the bf16 inputs).  The error
+    is reported two ways: the Frobenius norm of the sampled block relative to
+    the exact one, and the mean over rows of each row's relative error (the
+    rows span four decades, so the norm weighs only the largest rows)."""
     x, w = synthetic.long_k()
     xf, wf = synthetic.bf16_to_f32(x), synthetic.bf16_to_f32(w)
-    rows = synthetic.sample_rows(xf.shape[0], 12, 503)
+    rows = synthetic.sample_rows(xf.shape[0], 256, 503)
     exact = oracle.exact_gemm_f64(xf, wf, rows)
-    err, under = {}, {}
+    fro, rowm, under = {}, {}, {}
     for kind_a, kind_b in [("row", "block"), ("tensor", "tensor")]:
         qx, sx = oracle.quantize(xf, kind_a)
         qw, sw = oracle.quantize(wf, kind_b)
-        _parity(qx, sx, kind_a, qw, sw, kind_b, "NK", rows=rows, bf16=False)
+        c = _run(qx, sx, kind_a, qw, sw, kind_b, "NK")[rows]
         co = oracle.gemm_blockscaled(qx, sx, kind_a, qw, sw, kind_b, "NK", rows=rows)
-        # mean over rows of each row's relative error (the rows span four
-        # decades; a norm over the whole block would weigh only the largest)
-        err[kind_a] = float(np.mean(np.linalg.norm(co - exact, axis=1) / np.linalg.norm(exact, axis=1)))
+        _, R = oracle.gemm_blockscaled(qx, sx, kind_a, qw, sw, kind_b, "NK", rows=rows, f64=True)
+        gemm_parity(c, co, R)
+        fro[kind_a] = float(np.linalg.norm(co - exact) / np.linalg.norm(exact))
+        rowm[kind_a] = float(np.mean(np.linalg.norm(co - exact, axis=1) / np.linalg.norm(exact, axis=1)))
         under[kind_a] = oracle.underflow_fraction(xf, qx)
+    with capsys.disabled():
+        print("\nlong-K error vs exact (256 rows): Frobenius %s, mean row %s, underflow %s" % (
+            {k: "%.4e" % v for k, v in fro.items()}, {k: "%.4e" % v for k, v in rowm.items()},
+            {k: "%.3e" % v for k, v in under.items()}))
     assert under["row"] < under["tensor"]
-    assert err["row"] < err["tensor"]
+    assert rowm["row"] < rowm["tensor"]
+    assert fro["row"] < fro["tensor"]

@@ -96,17 +96,18 @@ def moe_inputs():
 
 
 @pytest.mark.parametrize("which", ["gate_up", "down"])
-def test_moe_full_size_sampled_rows(moe_inputs, which):
+def test_moe_full_size_row_per_tile(moe_inputs, which):
     m, gu, dn = moe_inputs
     qa, sa, qb, sb = gu if which == "gate_up" else dn
     off = m.offsets.astype(np.int64)
     c32 = host(_run(qa, sa, off, qb, sb))
     cb = host(_run(qa, sa, off, qb, sb, out=torch.bfloat16))
-    # sample rows from the most and least loaded experts and some pad rows
+    # one seeded row in every 128-row tile (every group, pad rows included),
+    # plus the first rows of the most and least loaded experts
     big = int(np.argmax(m.counts))
     small = int(np.argmin(m.counts))
     rows = np.concatenate([np.arange(off[big], off[big] + 6), np.arange(off[small], off[small] + 4),
-                           synthetic.sample_rows(qa.shape[0], 10, 404)])
+                           synthetic.rows_per_tile(qa.shape[0], 404)])
     rows = np.unique(rows)
     co = oracle.grouped_gemm(qa, sa, off, qb, sb, rows=rows)
     _, R = oracle.grouped_gemm(qa, sa, off, qb, sb, rows=rows, f64=True)
@@ -208,7 +209,7 @@ def moe_backward(moe_inputs):
 
 
 @pytest.mark.parametrize("which", ["gate_up", "down"])
-def test_moe_dgrad_full_size_sampled_rows(moe_backward, which):
+def test_moe_dgrad_full_size_row_per_tile(moe_backward, which):
     m, gu, dn, dgu, dd = moe_backward
     _, _, qw, sw = gu if which == "gate_up" else dn
     qdy, sdy = oracle.quant_1x128(dgu if which == "gate_up" else dd)
@@ -216,7 +217,7 @@ def test_moe_dgrad_full_size_sampled_rows(moe_backward, which):
     c32 = host(_run_dgrad(qdy, sdy, off, qw, sw))
     big, small = int(np.argmax(m.counts)), int(np.argmin(m.counts))
     rows = np.unique(np.concatenate([np.arange(off[big], off[big] + 6), np.arange(off[small], off[small] + 4),
-                                     synthetic.sample_rows(qdy.shape[0], 10, 407)]))
+                                     synthetic.rows_per_tile(qdy.shape[0], 407)]))
     co = oracle.grouped_gemm_dgrad(qdy, sdy, off, qw, sw, rows=rows)
     _, R = oracle.grouped_gemm_dgrad(qdy, sdy, off, qw, sw, rows=rows, f64=True)
     gemm_parity(c32[rows], co, R)
@@ -224,7 +225,7 @@ def test_moe_dgrad_full_size_sampled_rows(moe_backward, which):
 
 
 @pytest.mark.parametrize("which", ["gate_up", "down"])
-def test_moe_wgrad_full_size_sampled_rows(moe_backward, which):
+def test_moe_wgrad_full_size_row_per_tile(moe_backward, which):
     # dW_e = dY_e^T X_e over each expert's tokens; X is the expert GEMM's input
     m, gu, dn, dgu, dd = moe_backward
     dy = dgu if which == "gate_up" else dd
@@ -233,7 +234,7 @@ def test_moe_wgrad_full_size_sampled_rows(moe_backward, which):
     bt, sbt = oracle.quant_1x128(np.ascontiguousarray(xin.T))
     off = m.offsets.astype(np.int64)
     c = host(_run_wgrad(at, sat, bt, sbt, off))
-    rows = synthetic.sample_rows(at.shape[0], 6, 408)
+    rows = synthetic.rows_per_tile(at.shape[0], 408)
     co = oracle.grouped_gemm_wgrad(at, sat, bt, sbt, off, rows=rows)
     _, R = oracle.grouped_gemm_wgrad(at, sat, bt, sbt, off, rows=rows, f64=True)
     for e in range(c.shape[0]):

@@ -140,6 +140,7 @@ def test_grouped_validation():
     assert call(a7=1) == fq.ERR_SHAPE
     assert call(a3=200, a5=256, a7=2) == fq.ERR_ALIGN      # K % 16 != 0
     assert call(a8=A16 + 2) == fq.ERR_ALIGN
+    assert call(a0=1025, a1=1025 * 128) == fq.ERR_UNSUPPORTED   # the offsets live in LDS: G <= 1024
 
 
 def test_gemm_e4m3_validation():
@@ -188,6 +189,7 @@ def test_grouped_dgrad_validation():
     assert call(a12=200) == fq.ERR_SHAPE                   # ldc < K
     assert call(a3=200, a12=256) == fq.ERR_ALIGN           # K % 16 != 0 (weight row stride)
     assert call(a8=A16 + 2) == fq.ERR_ALIGN
+    assert call(a0=1025, a1=1025 * 128) == fq.ERR_UNSUPPORTED
 
 
 def test_grouped_wgrad_validation():
@@ -209,6 +211,7 @@ def test_grouped_wgrad_validation():
     assert call(a14=200) == fq.ERR_SHAPE                   # ldc < K
     assert call(a9=520) == fq.ERR_ALIGN                    # ldb % 16 != 0
     assert call(a13=A16 + 4) == fq.ERR_ALIGN
+    assert call(a0=1025, a1=1025 * 128, a5=1025 * 128, a9=1025 * 128, a7=1025, a11=1025) == fq.ERR_UNSUPPORTED
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="a GPU is present: valid fake pointers would launch")
