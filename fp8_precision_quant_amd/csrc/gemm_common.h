@@ -60,6 +60,10 @@ __device__ __forceinline__ uint4 mask_bytes(uint4 v, int valid)
 // caller then uses the general kernel).
 // `out` is OUT_F32, OUT_BF16 or OUT_E4M3 (codes in c, scales in cs).
 bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, int out, hipStream_t st);
+// The four-wave kernel (gemm_w4.hip) for dense calls with B stored [N][K]
+// and K a multiple of 128 (fp32, bf16 or E4M3 output); false if it does not
+// cover the call.
+bool launch_gemm_w4(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, int out, hipStream_t st);
 // Grouped (MoE) launch of the same kernel: A row tiles select their expert
 // through the device group offsets (B per expert as [N][K] for the forward,
 // read as [K][N] for dgrad); false if the call is not covered.

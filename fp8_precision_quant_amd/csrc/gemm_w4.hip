@@ -1,0 +1,592 @@
+// Block-scaled FP8 GEMM on gfx950, four-wave form: one wave per SIMD.
+//
+//   C[m][n] = sum_kb SA(m,kb) * SB(n,kb) * sum_{k in chunk kb} dec(A[m][k]) * dec(B[n][k])
+//
+// (FP8 Linear with an FP32 accumulator: Ling 2.0 FP8 blog, "where does the
+// worry come from" and "where is error introduced"; per-tile activation and
+// 128x128 weight-block scales: same blog, "fine-grained quantization", and
+// "FP8-RL" article, 一; the weight read as stored for dgrad: "FP8 on-demand
+// transpose weight".)
+//
+// For B stored [N][K] (forward and weight gradient).  The same 128 x 256 x 128
+// tile, LDS layout and direct global -> LDS loads as gemm_nk.hip, with a
+// different division of work:
+//  * four waves per workgroup, one per SIMD, each owning all 128 rows of 64
+//    columns for every K chunk, so no partial tiles are exchanged;
+//  * one wave per SIMD may hold 512 registers: the operand fragments of two
+//    chunks live in fixed accumulation registers a0..a191 (the chunk being
+//    multiplied and the next one, read from LDS while the current one runs),
+//    the fp32 accumulators, chunk partials and scales in ordinary registers;
+//  * each chunk is 32 steps; a step issues one MFMA, one or two LDS reads of
+//    the next chunk or one direct load of the chunk three ahead, and the
+//    scale FMAs of the block whose MFMA was issued three steps earlier (so
+//    the FMAs never wait on their own MFMA and need no hazard padding);
+//  * one barrier per chunk: before it every wave has its own loads of the
+//    next chunk in LDS and has finished reading the current one, whose stage
+//    then takes the chunk three ahead.  The loads run on across tiles, so the
+//    next tile's first chunks arrive while the current tile is stored.
+// Fragment registers are named in the instructions (the compiler cannot be
+// made to place a fragment's two 16-byte halves in adjacent registers), so
+// every fragment read declares them clobbered and the compiler allocates no
+// accumulation registers of its own in this kernel.
+#include <type_traits>
+
+#include "fp8q_device.h"
+#include "fp8q_internal.h"
+#include "gemm_common.h"
+#include "gemm_lds.h"
+
+namespace fp8q {
+
+namespace {
+
+constexpr int kW4Threads = 256;
+
+// fragment F (0..23) lives in a[8F .. 8F+7]: set s, A fragment i -> F = 12 s + i;
+// B fragment j -> F = 12 s + 8 + j.  Columns: F, low and high 16-byte halves.
+#define W4_FRAGS(X) \
+    X(0, "a[0:3]", "a[4:7]") \
+    X(1, "a[8:11]", "a[12:15]") \
+    X(2, "a[16:19]", "a[20:23]") \
+    X(3, "a[24:27]", "a[28:31]") \
+    X(4, "a[32:35]", "a[36:39]") \
+    X(5, "a[40:43]", "a[44:47]") \
+    X(6, "a[48:51]", "a[52:55]") \
+    X(7, "a[56:59]", "a[60:63]") \
+    X(8, "a[64:67]", "a[68:71]") \
+    X(9, "a[72:75]", "a[76:79]") \
+    X(10, "a[80:83]", "a[84:87]") \
+    X(11, "a[88:91]", "a[92:95]") \
+    X(12, "a[96:99]", "a[100:103]") \
+    X(13, "a[104:107]", "a[108:111]") \
+    X(14, "a[112:115]", "a[116:119]") \
+    X(15, "a[120:123]", "a[124:127]") \
+    X(16, "a[128:131]", "a[132:135]") \
+    X(17, "a[136:139]", "a[140:143]") \
+    X(18, "a[144:147]", "a[148:151]") \
+    X(19, "a[152:155]", "a[156:159]") \
+    X(20, "a[160:163]", "a[164:167]") \
+    X(21, "a[168:171]", "a[172:175]") \
+    X(22, "a[176:179]", "a[180:183]") \
+    X(23, "a[184:187]", "a[188:191]")
+
+#define W4_AGPRS "a0", "a1", "a2", "a3", "a4", "a5", "a6", "a7", "a8", "a9", "a10", "a11", "a12", "a13", "a14", "a15", "a16", "a17", "a18", "a19", "a20", "a21", "a22", "a23", "a24", "a25", "a26", "a27", "a28", "a29", "a30", "a31", "a32", "a33", "a34", "a35", "a36", "a37", "a38", "a39", "a40", "a41", "a42", "a43", "a44", "a45", "a46", "a47", "a48", "a49", "a50", "a51", "a52", "a53", "a54", "a55", "a56", "a57", "a58", "a59", "a60", "a61", "a62", "a63", "a64", "a65", "a66", "a67", "a68", "a69", "a70", "a71", "a72", "a73", "a74", "a75", "a76", "a77", "a78", "a79", "a80", "a81", "a82", "a83", "a84", "a85", "a86", "a87", "a88", "a89", "a90", "a91", "a92", "a93", "a94", "a95", "a96", "a97", "a98", "a99", "a100", "a101", "a102", "a103", "a104", "a105", "a106", "a107", "a108", "a109", "a110", "a111", "a112", "a113", "a114", "a115", "a116", "a117", "a118", "a119", "a120", "a121", "a122", "a123", "a124", "a125", "a126", "a127", "a128", "a129", "a130", "a131", "a132", "a133", "a134", "a135", "a136", "a137", "a138", "a139", "a140", "a141", "a142", "a143", "a144", "a145", "a146", "a147", "a148", "a149", "a150", "a151", "a152", "a153", "a154", "a155", "a156", "a157", "a158", "a159", "a160", "a161", "a162", "a163", "a164", "a165", "a166", "a167", "a168", "a169", "a170", "a171", "a172", "a173", "a174", "a175", "a176", "a177", "a178", "a179", "a180", "a181", "a182", "a183", "a184", "a185", "a186", "a187", "a188", "a189", "a190", "a191"
+
+// A fragments (multiplicand rows) and B fragments by number, for the MFMA
+#define W4_A_LIST(X, B) \
+    X(B, 0, "a[0:7]") \
+    X(B, 1, "a[8:15]") \
+    X(B, 2, "a[16:23]") \
+    X(B, 3, "a[24:31]") \
+    X(B, 4, "a[32:39]") \
+    X(B, 5, "a[40:47]") \
+    X(B, 6, "a[48:55]") \
+    X(B, 7, "a[56:63]") \
+    X(B, 12, "a[96:103]") \
+    X(B, 13, "a[104:111]") \
+    X(B, 14, "a[112:119]") \
+    X(B, 15, "a[120:127]") \
+    X(B, 16, "a[128:135]") \
+    X(B, 17, "a[136:143]") \
+    X(B, 18, "a[144:151]") \
+    X(B, 19, "a[152:159]")
+#define W4_B_LIST(X) \
+    X(8, "a[64:71]") \
+    X(9, "a[72:79]") \
+    X(10, "a[80:87]") \
+    X(11, "a[88:95]") \
+    X(20, "a[160:167]") \
+    X(21, "a[168:175]") \
+    X(22, "a[176:183]") \
+    X(23, "a[184:191]")
+
+// 16-byte LDS read into half H (0 low, 1 high) of fragment F
+template <int F, int H, int OFF>
+__device__ __forceinline__ void w4_read_half(uint32_t addr)
+{
+#define X(FI, LO, HI) \
+    if constexpr (F == FI) { \
+        if constexpr (H == 0) asm volatile("ds_read_b128 " LO ", %0 offset:%1" ::"v"(addr), "i"(OFF) : "memory", W4_AGPRS); \
+        else asm volatile("ds_read_b128 " HI ", %0 offset:%1" ::"v"(addr), "i"(OFF) : "memory", W4_AGPRS); \
+    }
+    W4_FRAGS(X)
+#undef X
+}
+
+// the chunk's fp32 partial of one 16 x 16 block: fragment FB (B rows) times FA (A rows)
+template <int FB, int FA>
+__device__ __forceinline__ void w4_mfma(v4f& d)
+{
+#define W4_MF_A(BFULL, FAI, AFULL) \
+    if constexpr (FA == FAI) asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, " BFULL ", " AFULL ", 0" : "=v"(d) : : "memory");
+#define W4_MF_B(FBI, BFULL) \
+    if constexpr (FB == FBI) { W4_A_LIST(W4_MF_A, BFULL) }
+    W4_B_LIST(W4_MF_B)
+#undef W4_MF_B
+#undef W4_MF_A
+}
+
+__device__ __forceinline__ void w4_fmac(float& acc, float p, float s)
+{
+    asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(acc) : "v"(p), "v"(s) : "memory");
+}
+
+__device__ __forceinline__ void w4_mul(float& d, float a, float b)
+{
+    asm volatile("v_mul_f32_e32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b) : "memory");
+}
+
+// one lane's fp32 scale from LDS (a load: its result is used only after the
+// chunk's closing wait, which names it)
+template <int OFF>
+__device__ __forceinline__ float w4_ds32(uint32_t addr)
+{
+    float v;
+    asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+    return v;
+}
+
+template <int OFF>
+__device__ __forceinline__ v4f w4_ds128(uint32_t addr)
+{
+    v4f v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+    return v;
+}
+
+}  // namespace
+
+namespace {
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void w4_for(F&& f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        w4_for<I + 1, N>(f);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void w4_wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// the scales of one chunk as a lane uses them
+template <int SB_MODE>
+struct W4Scales {
+    float sa[PMI];                            // SA of the lane's row in 16-row block i
+    float sb;                                 // SB of the wave's 128-column block
+    v4f sc[SB_MODE == SB_ROW ? NNI : 1];      // SB of the lane's 4 columns in 16-column block j
+    float comb[PMI];                          // SA * SB (uniform B scale)
+};
+
+}  // namespace
+
+template <int SA_MODE, int SB_MODE, int OUT>
+__global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4_kernel(GemmArgs p)
+{
+    static_assert(OUT != OUT_E4M3 || SB_MODE != SB_ROW, "quantize-on-store: uniform B scales");
+    // direct loads per chunk and wave: 4 of A, 8 of B, one of A's and one of
+    // B's scales where they are per row / per block
+    constexpr int ND = 12 + (SA_MODE == SA_ROW ? 1 : 0) + (SB_MODE != SB_TENSOR ? 1 : 0);
+    __shared__ __attribute__((aligned(16))) uint8_t Stg[kStages][kStageBytes];
+    __shared__ __attribute__((aligned(16))) float SAs[kStages][TBM];
+    __shared__ __attribute__((aligned(16))) float SBs[kStages][SB_MODE == SB_ROW ? TBN : 4];
+    // quantize-on-store: each wave's row maxima over its 64 columns
+    __shared__ float RowMax[OUT == OUT_E4M3 ? kW4Threads / 64 : 1][OUT == OUT_E4M3 ? TBM : 1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);   // columns [64 wq, 64 wq + 64) of the tile
+
+    // Persistent workgroups dealt to the 8 XCDs round-robin; XCD x owns a
+    // contiguous range of tile ids, walked by its workgroups in lockstep in
+    // groups of kGroupM M-tiles (neighbouring workgroups share A and B panels
+    // in that XCD's L2).
+    const int T = p.tiles_m * p.tiles_n;
+    const int xcd = blockIdx.x & 7;
+    const int local = blockIdx.x >> 3;
+    const int G = gridDim.x;
+    const int nwg = (G >> 3) + (xcd < (G & 7) ? 1 : 0);
+    const int range_start = xcd * (T >> 3) + min(xcd, T & 7);
+    const int range_len = (T >> 3) + (xcd < (T & 7) ? 1 : 0);
+    if (local >= range_len) return;
+    const int span = kGroupM * p.tiles_n;
+    auto tile_origin = [&](int ordinal, int64_t& tm0, int64_t& tn0) __attribute__((always_inline)) {
+        const int pid = range_start + local + ordinal * nwg;
+        const int group = pid / span;
+        const int first_m = group * kGroupM;
+        const int gsz = min(p.tiles_m - first_m, kGroupM);
+        const int idx = pid - group * span;
+        tm0 = (int64_t)(first_m + idx % gsz) * TBM;
+        tn0 = (int64_t)(idx / gsz) * TBN;
+    };
+    const int my_tiles = (range_len - local + nwg - 1) / nwg;
+    const int KB = p.KB;
+    const int total = my_tiles * KB;       // chunks of this workgroup, tile after tile
+
+    // Buffer resources bound every load to its operand; rows past M or N
+    // start past the bound and read as zero (they feed outputs not stored).
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t nblocks = (N + 127) / 128;
+    const __amdgpu_buffer_rsrc_t ra = rsrc(p.a, (M - 1) * p.lda + K);
+    const __amdgpu_buffer_rsrc_t rb = rsrc(p.b, (N - 1) * p.ldb + K);
+    const __amdgpu_buffer_rsrc_t rsa = rsrc(p.sa, SA_MODE == SA_ROW ? ((M - 1) * p.ldsa + KB) * 4 : 4);
+    const __amdgpu_buffer_rsrc_t rsb =
+        rsrc(p.sb, SB_MODE == SB_ROW     ? ((N - 1) * p.ldsb + KB) * 4
+                   : SB_MODE == SB_BLOCK ? ((nblocks - 1) * p.ldsb + KB) * 4
+                                         : 4);
+    const float sa_t = SA_MODE == SA_TENSOR ? p.sa[0] : 0.0f;
+    const float sb_t = SB_MODE == SB_TENSOR ? p.sb[0] : 0.0f;
+
+    // ---- loads (the load cursor runs three chunks ahead of the MFMAs) ----
+    // This wave loads A rows [32 wq, 32 wq + 32) (4 loads of 8 rows), B rows
+    // [64 wq, 64 wq + 64) (8 loads of 8 rows), A's row scales of rows
+    // [32 wq, 32 wq + 32), and its own B scales.  Load t differs from
+    // load 0 by t row steps (scalar offset) and, for odd t, by the swizzle key.
+    int ld_ord = 0, ld_k = 0;
+    int64_t lm0, ln0;
+    tile_origin(0, lm0, ln0);
+    uint32_t va0, va1, vb0, vb1, vsa = 0, vsb = 0;
+    auto load_offsets = [&]() __attribute__((always_inline)) {
+        const int l = lane;
+        const int64_t arow = lm0 + 32 * wq + (l >> 3);
+        va0 = (uint32_t)(arow * p.lda) + 16u * (uint32_t)((l & 7) ^ (l >> 3));
+        va1 = (uint32_t)(arow * p.lda) + 16u * (uint32_t)((l & 7) ^ (l >> 3) ^ 1);
+        const int64_t brow = ln0 + 64 * wq + (l >> 3);
+        vb0 = (uint32_t)(brow * p.ldb) + 16u * (uint32_t)((l & 7) ^ (l >> 3));
+        vb1 = (uint32_t)(brow * p.ldb) + 16u * (uint32_t)((l & 7) ^ (l >> 3) ^ 1);
+        if (SA_MODE == SA_ROW) vsa = (uint32_t)((lm0 + 32 * wq + l) * p.ldsa * 4);
+        if (SB_MODE == SB_ROW) vsb = (uint32_t)((ln0 + 64 * wq + l) * p.ldsb * 4);
+        if (SB_MODE == SB_BLOCK) vsb = (uint32_t)((ln0 / 128 + (wq >> 1)) * p.ldsb * 4);
+    };
+    load_offsets();
+    // load d (0 .. ND-1) of the cursor's chunk into stage st
+    auto load_item = [&](auto dt, int st) __attribute__((always_inline)) {
+        constexpr int d = decltype(dt)::value;
+        const uint32_t kg = (uint32_t)ld_k;
+        if constexpr (d < 4) {
+            dma16_at(ra, lds_addr(&Stg[st][0]) + (uint32_t)((32 * wq + 8 * d) * TBK), (d & 1) ? va1 : va0,
+                     kg * TBK + (uint32_t)(8 * d) * (uint32_t)p.lda);
+        } else if constexpr (d < 12) {
+            constexpr int t = d - 4;
+            dma16_at(rb, lds_addr(&Stg[st][kAStage]) + (uint32_t)((64 * wq + 8 * t) * TBK), (t & 1) ? vb1 : vb0,
+                     kg * TBK + 8u * t * (uint32_t)p.ldb);
+        } else if constexpr (SA_MODE == SA_ROW && d == 12) {
+            if (lane < 32) dma4(rsa, &SAs[st][32 * wq], vsa, kg * 4);
+        } else {
+            if constexpr (SB_MODE == SB_ROW) dma4(rsb, &SBs[st][64 * wq], vsb, kg * 4);
+            if constexpr (SB_MODE == SB_BLOCK) {
+                if (lane == 0) dma4(rsb, &SBs[st][wq], vsb, kg * 4);
+            }
+        }
+    };
+    // (past the last tile the cursor stays on it: the loads it then issues
+    // read valid memory into a free stage and are never used, which keeps
+    // the loads per chunk, and so the wait counts, the same for every chunk)
+    auto load_advance = [&]() __attribute__((always_inline)) {
+        if (++ld_k == KB) {
+            ld_k = 0;
+            if (ld_ord + 1 < my_tiles) {
+                ++ld_ord;
+                tile_origin(ld_ord, lm0, ln0);
+                load_offsets();
+            }
+        }
+    };
+
+    // ---- LDS reads of a chunk into fragment set NS (fixed registers) ----
+    const int lrow = lane & 15, kgrp = lane >> 4;
+    const uint32_t stg0 = lds_addr(&Stg[0][0]);
+    const uint32_t a_rel0 = (uint32_t)sw(lrow, 2 * kgrp), a_rel1 = (uint32_t)sw(lrow, 2 * kgrp + 1);
+    const uint32_t b_rel0 = (uint32_t)(kAStage + sw(64 * wq + lrow, 2 * kgrp));
+    const uint32_t b_rel1 = (uint32_t)(kAStage + sw(64 * wq + lrow, 2 * kgrp + 1));
+    const uint32_t sa_rel = lds_addr(&SAs[0][0]) + (uint32_t)lrow * 4;
+    const uint32_t sb_rel = SB_MODE == SB_ROW ? lds_addr(&SBs[0][0]) + (uint32_t)(64 * wq + 4 * kgrp) * 4
+                                              : lds_addr(&SBs[0][0]) + (uint32_t)wq * 4;
+
+    W4Scales<SB_MODE> scl[2];
+    // read item k (0 .. 31) of the chunk in stage st into fragment set NS and
+    // scale set NS: 0-1 B0, 2-17 A0..A7 (two halves each), 18-23 B1..B3,
+    // 24-31 the scales.
+    auto read_item = [&](auto kt, auto nst, int st) __attribute__((always_inline)) {
+        constexpr int k = decltype(kt)::value;
+        constexpr int NS = decltype(nst)::value;
+        const uint32_t base = stg0 + (uint32_t)st * kStageBytes;
+        if constexpr (k >= 2 && k < 18) {
+            constexpr int i = (k - 2) / 2, h = (k - 2) % 2;
+            w4_read_half<12 * NS + i, h, i * 16 * TBK>(base + (h ? a_rel1 : a_rel0));
+        } else if constexpr (k < 24) {
+            constexpr int j = k < 2 ? 0 : 1 + (k - 18) / 2;
+            constexpr int h = k < 2 ? k : (k - 18) % 2;
+            constexpr int F = 12 * NS + 8 + j;
+            w4_read_half<F, h, j * 16 * TBK>(base + (h ? b_rel1 : b_rel0));
+        } else {
+            constexpr int i = k - 24;
+            if constexpr (SA_MODE == SA_ROW) scl[NS].sa[i] = w4_ds32<i * 64>(sa_rel + (uint32_t)(st * TBM * 4));
+            if constexpr (SB_MODE == SB_BLOCK && i == 0) scl[NS].sb = w4_ds32<0>(sb_rel + (uint32_t)(st * 16));
+            if constexpr (SB_MODE == SB_ROW && (i & 1) == 0)
+                scl[NS].sc[i / 2] = w4_ds128<(i / 2) * 64>(sb_rel + (uint32_t)(st * TBN * 4));
+        }
+    };
+    // the closing wait of a chunk's reads; it names the scale registers so
+    // that nothing reads them earlier
+    auto reads_done = [&](auto nst) __attribute__((always_inline)) {
+        constexpr int NS = decltype(nst)::value;
+        W4Scales<SB_MODE>& s = scl[NS];
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(s.sa[0]), "+v"(s.sa[1]), "+v"(s.sa[2]), "+v"(s.sa[3]), "+v"(s.sa[4]),
+                       "+v"(s.sa[5]), "+v"(s.sa[6]), "+v"(s.sa[7]), "+v"(s.sb)
+                     :
+                     : "memory");
+        if constexpr (SB_MODE == SB_ROW)
+            asm volatile("" : "+v"(s.sc[0]), "+v"(s.sc[1]), "+v"(s.sc[2]), "+v"(s.sc[3]));
+    };
+
+    v4f acc[PMI][NNI];
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < PMI; ++i)
+#pragma unroll
+        for (int j = 0; j < NNI; ++j) acc[i][j] = zero;
+    v4f P[4] = {zero, zero, zero, zero};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int i = 0; i < PMI; ++i) scl[s].sa[i] = scl[s].comb[i] = 0.0f;
+        scl[s].sb = 0.0f;
+#pragma unroll
+        for (int j = 0; j < (SB_MODE == SB_ROW ? NNI : 1); ++j) scl[s].sc[j] = zero;
+    }
+
+    // scale FMAs of 16 x 16 block v (MFMA order: j = v / 8, i = v % 8) from
+    // partial slot v & 3 with the scales of set S
+    auto block_fma = [&](auto vt, auto st_) __attribute__((always_inline)) {
+        constexpr int v = decltype(vt)::value;
+        constexpr int S = decltype(st_)::value;
+        constexpr int i = v % PMI, j = v / PMI;
+        const v4f pp = P[v & 3];
+        if constexpr (SB_MODE == SB_ROW) {
+            const float ra = SA_MODE == SA_ROW ? scl[S].sa[i] : sa_t;
+            float t[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) w4_mul(t[r], ra, scl[S].sc[j][r]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float a = acc[i][j][r];
+                w4_fmac(a, pp[r], t[r]);
+                acc[i][j][r] = a;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float a = acc[i][j][r];
+                w4_fmac(a, pp[r], scl[S].comb[i]);
+                acc[i][j][r] = a;
+            }
+        }
+    };
+
+    // ---- output of a finished tile ----
+    int c_ord = 0;
+    int64_t cm0, cn0;
+    tile_origin(0, cm0, cn0);
+    auto store_tile = [&]() __attribute__((always_inline)) {
+        if constexpr (OUT == OUT_E4M3) {
+            // The output's 1x128 tiles along N: a tile is the 64 columns of
+            // this wave and those of wave wq ^ 1 (same rows).  Columns past N
+            // are left out of the amax.
+            float mx[PMI];
+            const int64_t ncol0 = cn0 + 64 * wq + 4 * kgrp;
+#pragma unroll
+            for (int i = 0; i < PMI; ++i) {
+                float v = 0.0f;
+#pragma unroll
+                for (int j = 0; j < NNI; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (ncol0 + 16 * j + r < N) v = fmaxf(v, fabsf(acc[i][j][r]));
+                v = fmaxf(v, __shfl_xor(v, 16));
+                mx[i] = fmaxf(v, __shfl_xor(v, 32));
+                if (kgrp == 0) RowMax[wq][16 * i + lrow] = mx[i];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < PMI; ++i) {
+                const float other = RowMax[wq ^ 1][16 * i + lrow];
+                const TileScale ts = make_scale(fmaxf(mx[i], other));
+                uint32_t code[NNI];
+                float v[8];
+#pragma unroll
+                for (int jp = 0; jp < NNI / 2; ++jp) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        v[r] = acc[i][2 * jp][r];
+                        v[4 + r] = acc[i][2 * jp + 1][r];
+                    }
+                    quant8(v, ts, code[2 * jp], code[2 * jp + 1]);
+                }
+                const int64_t m = cm0 + 16 * i + lrow;
+                if (m >= M) continue;
+                uint8_t* qrow = reinterpret_cast<uint8_t*>(p.c) + m * p.ldc;
+#pragma unroll
+                for (int j = 0; j < NNI; ++j) {
+                    const int64_t n = ncol0 + 16 * j;
+                    if (n + 3 < N) {
+                        *reinterpret_cast<uint32_t*>(qrow + n) = code[j];
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (n + r < N) qrow[n + r] = (uint8_t)(code[j] >> (8 * r));
+                    }
+                }
+                const int64_t n_tile = cn0 + 64 * wq;
+                if (kgrp == 0 && (wq & 1) == 0 && n_tile < N) p.cs[m * p.ldcs + n_tile / 128] = ts.s;
+            }
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < PMI; ++i) {
+            const int64_t m = cm0 + 16 * i + lrow;
+            if (m >= M) continue;
+#pragma unroll
+            for (int j = 0; j < NNI; ++j) {
+                const int64_t n = cn0 + 64 * wq + 16 * j + 4 * kgrp;
+                const v4f v = acc[i][j];
+                if (n + 3 < N) {
+                    if (OUT == OUT_BF16) {
+                        const uint32_t lo = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
+                        const uint32_t hi = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+                        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.c) + m * p.ldc + n) = make_uint2(lo, hi);
+                    } else {
+                        *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.c) + m * p.ldc + n) = v;
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (n + r < N) {
+                            if (OUT == OUT_BF16)
+                                reinterpret_cast<uint16_t*>(p.c)[m * p.ldc + n + r] = (uint16_t)bf16_rne(v[r]);
+                            else
+                                reinterpret_cast<float*>(p.c)[m * p.ldc + n + r] = v[r];
+                        }
+                    }
+                }
+            }
+        }
+    };
+
+    // ---- prologue: chunks 0..2 to LDS, chunk 0 to registers ----
+    for (int c = 0; c < 3; ++c) {
+        w4_for<0, ND>([&](auto dt) __attribute__((always_inline)) { load_item(dt, c); });
+        load_advance();
+    }
+    w4_wait_vm<2 * ND>();
+    __builtin_amdgcn_s_barrier();
+    w4_for<0, 32>([&](auto kt) __attribute__((always_inline)) { read_item(kt, std::integral_constant<int, 0>{}, 0); });
+    reads_done(std::integral_constant<int, 0>{});
+
+    // ---- the chunk stream ----
+    int g = 0, ck = 0;
+    int st_w = 0;          // stage of chunk g (takes chunk g + 3)
+    auto iteration = [&](auto s_tag) __attribute__((always_inline)) {
+        constexpr int S = decltype(s_tag)::value;
+        constexpr int NS = 1 - S;
+        // own loads of chunk g + 1 have landed; after the barrier every
+        // wave's have, and every wave is done reading chunk g's stage
+        w4_wait_vm<ND>();
+        __builtin_amdgcn_s_barrier();
+        if constexpr (SB_MODE != SB_ROW) {
+            const float sbv = SB_MODE == SB_BLOCK ? scl[S].sb : SB_MODE == SB_TENSOR ? sb_t : 1.0f;
+#pragma unroll
+            for (int i = 0; i < PMI; ++i) scl[S].comb[i] = (SA_MODE == SA_ROW ? scl[S].sa[i] : sa_t) * sbv;
+            // formed here, once per chunk, not next to each use
+            asm volatile("" : "+v"(scl[S].comb[0]), "+v"(scl[S].comb[1]), "+v"(scl[S].comb[2]), "+v"(scl[S].comb[3]),
+                              "+v"(scl[S].comb[4]), "+v"(scl[S].comb[5]), "+v"(scl[S].comb[6]), "+v"(scl[S].comb[7]));
+        }
+        const int st_r = st_w == 2 ? 0 : st_w + 1;
+        w4_for<0, 32>([&](auto ut) __attribute__((always_inline)) {
+            constexpr int u = decltype(ut)::value;
+            w4_mfma<12 * S + 8 + u / PMI, 12 * S + u % PMI>(P[u & 3]);
+            read_item(ut, std::integral_constant<int, NS>{}, st_r);
+            if constexpr (u >= 4 && (u - 4) % 2 == 0 && (u - 4) / 2 < ND)
+                load_item(std::integral_constant<int, (u - 4) / 2>{}, st_w);
+            // blocks 29..31 of the previous chunk (zero partials after a
+            // tile's last chunk, whose blocks were scaled before its output)
+            if constexpr (u >= 3) block_fma(std::integral_constant<int, u - 3>{}, std::integral_constant<int, S>{});
+            else block_fma(std::integral_constant<int, 29 + u>{}, std::integral_constant<int, NS>{});
+        });
+        load_advance();
+        reads_done(std::integral_constant<int, NS>{});
+        if (ck == KB - 1) {
+            // last chunk of the tile: blocks 29..31 (their MFMAs are more
+            // than 12 instructions back after this padding), then the output
+            asm volatile("s_nop 7" ::: "memory");
+            block_fma(std::integral_constant<int, 29>{}, std::integral_constant<int, S>{});
+            block_fma(std::integral_constant<int, 30>{}, std::integral_constant<int, S>{});
+            block_fma(std::integral_constant<int, 31>{}, std::integral_constant<int, S>{});
+            P[1] = zero;
+            P[2] = zero;
+            P[3] = zero;
+            store_tile();
+#pragma unroll
+            for (int i = 0; i < PMI; ++i)
+#pragma unroll
+                for (int j = 0; j < NNI; ++j) acc[i][j] = zero;
+            if (++c_ord < my_tiles) tile_origin(c_ord, cm0, cn0);
+            ck = 0;
+        } else {
+            ++ck;
+        }
+        st_w = st_r;
+        ++g;
+    };
+    for (;;) {
+        iteration(std::integral_constant<int, 0>{});
+        if (g == total) break;
+        iteration(std::integral_constant<int, 1>{});
+        if (g == total) break;
+    }
+    w4_wait_vm<0>();
+}
+
+template <int SA_MODE, int SB_MODE>
+static void w4_launch_out(const GemmArgs& g, int out, hipStream_t st)
+{
+    GemmArgs a = g;
+    a.tiles_m = (int)((g.M + TBM - 1) / TBM);
+    a.tiles_n = (int)((g.N + TBN - 1) / TBN);
+    const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+    dim3 grid((uint32_t)(tiles < g.num_cus ? tiles : g.num_cus));
+    if (out == OUT_BF16)
+        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_BF16>), grid, dim3(kW4Threads), 0, st, a);
+    else if (out == OUT_F32)
+        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_F32>), grid, dim3(kW4Threads), 0, st, a);
+    else if constexpr (SB_MODE != SB_ROW)
+        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_E4M3>), grid, dim3(kW4Threads), 0, st, a);
+}
+
+// [N][K] B only.  B read as stored ([K][N], data gradient) takes twice as
+// many fragment reads (transposing 8-byte ones); with one wave per SIMD
+// issuing every read, load, MFMA and FMA itself, that form measured 4%
+// slower than gemm_nk_kernel, whose two waves per SIMD share the issue work.
+bool launch_gemm_w4(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, int out, hipStream_t st)
+{
+    if (g.K <= 0 || g.K % 128 != 0 || b_kn) return false;
+    if (out == OUT_E4M3 && sb_mode == SB_ROW) return false;
+    if (sa_mode == SA_ROW) {
+        if (sb_mode == SB_BLOCK) w4_launch_out<SA_ROW, SB_BLOCK>(g, out, st);
+        else if (sb_mode == SB_ROW) w4_launch_out<SA_ROW, SB_ROW>(g, out, st);
+        else w4_launch_out<SA_ROW, SB_TENSOR>(g, out, st);
+    } else {
+        if (sb_mode == SB_BLOCK) w4_launch_out<SA_TENSOR, SB_BLOCK>(g, out, st);
+        else if (sb_mode == SB_ROW) w4_launch_out<SA_TENSOR, SB_ROW>(g, out, st);
+        else w4_launch_out<SA_TENSOR, SB_TENSOR>(g, out, st);
+    }
+    return true;
+}
+
+}  // namespace fp8q

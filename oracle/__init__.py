@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
             L.orc_f32_to_bf16.argtypes = [p, i64, p]
             L.orc_underflow_count.argtypes = [p, p, i64, p, p]
             L.orc_num_threads.restype = ctypes.c_int
+            L.orc_set_num_threads.argtypes = [ctypes.c_int]
             _lib = L
     return _lib
 
@@ -84,6 +85,11 @@ def lib() -> ctypes.CDLL:
 def num_threads() -> int:
     """Threads the oracle's parallel loops use."""
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the oracle's parallel loops (timing only)."""
+    lib().orc_set_num_threads(int(n))
 
 
 def _ptr(a: np.ndarray) -> int:

@@ -42,6 +42,17 @@
 #include <omp.h>
 #endif
 
+/* Sets the number of threads the parallel loops below run on (timing only:
+   no result depends on it). */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Threads the parallel loops below run on (reported with CPU timings). */
 int orc_num_threads(void)
 {
