@@ -19,7 +19,10 @@ finds the previous step's data in the last-level cache.  `value` is the GEMM
 work of the step (3 x 2*M*N*K) divided by the GPU time of the whole step,
 quantizers included (K steps between two events, nothing else in between).
 A second pass over K steps brackets each launch with events for the
-per-kernel breakdown.  The roofline entry covers the kernel that takes the
+per-kernel breakdown.  Timing starts after W warmup steps (default 50, about
+50 ms): after an idle gap the clock first drops under the sudden dense load
+and recovers over some tens of milliseconds, so a few warmup steps would
+time that transient rather than the steady state.  The roofline entry covers the kernel that takes the
 most time in the step.
 
 Also reported, each on its own workload (none is part of `value`):
@@ -74,7 +77,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-moe", action="store_true", help="skip the grouped MoE GEMM timing")
     p.add_argument("--no-extras", action="store_true",
@@ -146,12 +149,28 @@ def copy_ceiling_gbs(dev):
     return round(2 * n / (ms * 1e-3) / 1e9, 1)
 
 
+def settle(fn_list, ms=60.0):
+    """Runs the calls back to back for about `ms` of wall time before a timed
+    region.  After an idle gap the first few milliseconds of dense work run
+    at a clock the power management then lowers and raises again over tens
+    of milliseconds; timing starts past that transient."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            fn_list[i % len(fn_list)]()
+            i += 1
+        torch.cuda.synchronize()
+
+
 def time_launches(fn_list, reps, stream):
     """Average GPU time (us) of one call of each fn: `reps` calls between an
-    event pair, fn_list[i % len] in turn (rotating buffer sets)."""
+    event pair, fn_list[i % len] in turn (rotating buffer sets), after
+    `settle`."""
     import torch
-    for f in fn_list:
-        f()
+    settle(fn_list)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -515,6 +534,11 @@ def adam_step(fq, b, args, stream):
     p_w = b.w.float().reshape(-1).contiguous()
     g_w = b.dW.reshape(-1)
     st8 = fq.fp8_adam_state(n_w, b.x.device)
+    # warmup on a copy of the state (the timed steps continue from step 1)
+    warm = fq.fp8_adam_state(n_w, b.x.device)
+    p_warm = p_w.clone()
+    settle([lambda: fq.fp8_adam_step(p_warm, g_w, warm, lr=1e-4, weight_decay=0.1, step=1)])
+    del warm, p_warm
     for t in range(1, args.warmup + 1):
         fq.fp8_adam_step(p_w, g_w, st8, lr=1e-4, weight_decay=0.1, step=t)
     torch.cuda.synchronize()

@@ -25,7 +25,7 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]
 
-SOURCES = ["api.hip", "quant.hip", "quant_transpose.hip", "gemm.hip", "gemm_nk.hip", "gemm_w4.hip", "adam.hip"]
+SOURCES = ["api.hip", "check.hip", "quant.hip", "quant_transpose.hip", "gemm.hip", "gemm_nk.hip", "gemm_w4.hip", "adam.hip"]
 
 
 def _compile(src: str, obj: str) -> None:

@@ -1,8 +1,8 @@
 // C ABI of libfp8q: argument validation, device check, dispatch.
 //
 // Every entry point validates all of its arguments on the host before it
-// enqueues anything, never allocates or synchronizes, and reports a pending
-// launch error as FP8Q_ERR_LAUNCH.  Operation semantics are documented in
+// enqueues anything, never allocates or synchronizes (except in the debug
+// mode FP8Q_CHECK=1), and reports a pending launch error as FP8Q_ERR_LAUNCH.  Operation semantics are documented in
 // include/fp8q.h.
 #include <atomic>
 #include <cmath>
@@ -13,7 +13,6 @@
 namespace {
 
 constexpr int64_t kTile = 128;
-constexpr int64_t kMaxGridY = 65535;
 constexpr int64_t kMaxIndex = (int64_t)1 << 31;
 // grouped GEMMs keep the group offsets in LDS
 constexpr int64_t kMaxGroups = 1024;
@@ -51,9 +50,23 @@ int check_device()
     return st == 1 ? FP8Q_OK : FP8Q_ERR_DEVICE;
 }
 
-int launch_status()
+// A pending launch error; with FP8Q_CHECK=1 the stream is also synchronized
+// so that an error of the work itself is reported by the call that enqueued it.
+int launch_status(void* stream)
 {
-    return hipGetLastError() == hipSuccess ? FP8Q_OK : FP8Q_ERR_LAUNCH;
+    if (hipGetLastError() != hipSuccess) return FP8Q_ERR_LAUNCH;
+    if (fp8q::debug_checks_enabled() && hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) {
+        (void)hipGetLastError();
+        return FP8Q_ERR_LAUNCH;
+    }
+    return FP8Q_OK;
+}
+
+// FP8Q_CHECK=1: the group offsets are checked on the device first.
+int offsets_status(const int32_t* offsets, int64_t G, int64_t M_pad, void* stream)
+{
+    if (!fp8q::debug_checks_enabled()) return FP8Q_OK;
+    return fp8q::check_group_offsets(offsets, G, M_pad, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace
@@ -96,7 +109,7 @@ int fp8_quant_blockwise(const void* x, int x_dtype, int64_t rows, int64_t cols, 
     if (st != FP8Q_OK) return st;
     fp8q::launch_quant_blockwise(x, x_dtype, rows, cols, ldx, kind, q, ldq, s, lds,
                                  static_cast<hipStream_t>(stream));
-    return launch_status();
+    return launch_status(stream);
 }
 
 int fp8_quant_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
@@ -116,7 +129,7 @@ int fp8_quant_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols, 
     if (ldx < cols) return FP8Q_ERR_SHAPE;
     if (want_row && (ldq_row < cols || lds_row < cdiv(cols, kTile))) return FP8Q_ERR_SHAPE;
     if (want_col && (ldq_colT < rows || lds_colT < cdiv(rows, kTile))) return FP8Q_ERR_SHAPE;
-    if (cdiv(rows, kTile) > kMaxGridY || cdiv(rows, kTile) * cdiv(cols, kTile) >= kMaxIndex) return FP8Q_ERR_SHAPE;
+    if (cdiv(rows, kTile) * cdiv(cols, kTile) >= kMaxIndex) return FP8Q_ERR_SHAPE;
     if (!aligned16(x) || (ldx * elem_size(x_dtype)) % 16) return FP8Q_ERR_ALIGN;
     if (want_row && (!aligned16(q_row) || ldq_row % 16)) return FP8Q_ERR_ALIGN;
     if (want_col && (!aligned16(q_colT) || ldq_colT % 16)) return FP8Q_ERR_ALIGN;
@@ -125,7 +138,7 @@ int fp8_quant_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols, 
     fp8q::launch_quant_transpose(x, x_dtype, rows, cols, ldx, want_row ? q_row : nullptr, ldq_row,
                                  s_row, lds_row, want_col ? q_colT : nullptr, ldq_colT, s_colT,
                                  lds_colT, static_cast<hipStream_t>(stream));
-    return launch_status();
+    return launch_status(stream);
 }
 
 int fp8_quant_blockwise_e8m0(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
@@ -146,7 +159,7 @@ int fp8_quant_blockwise_e8m0(const void* x, int x_dtype, int64_t rows, int64_t c
     if (st != FP8Q_OK) return st;
     fp8q::launch_quant_blockwise_e8m0(x, x_dtype, rows, cols, ldx, kind, q, ldq, e, lde,
                                       static_cast<hipStream_t>(stream));
-    return launch_status();
+    return launch_status(stream);
 }
 
 int fp8_quant_transpose_e8m0(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
@@ -166,7 +179,7 @@ int fp8_quant_transpose_e8m0(const void* x, int x_dtype, int64_t rows, int64_t c
     if (ldx < cols) return FP8Q_ERR_SHAPE;
     if (want_row && (ldq_row < cols || lde_row < cdiv(cols, kTile))) return FP8Q_ERR_SHAPE;
     if (want_col && (ldq_colT < rows || lde_colT < cdiv(rows, kTile))) return FP8Q_ERR_SHAPE;
-    if (cdiv(rows, kTile) > kMaxGridY || cdiv(rows, kTile) * cdiv(cols, kTile) >= kMaxIndex) return FP8Q_ERR_SHAPE;
+    if (cdiv(rows, kTile) * cdiv(cols, kTile) >= kMaxIndex) return FP8Q_ERR_SHAPE;
     if (!aligned16(x) || (ldx * elem_size(x_dtype)) % 16) return FP8Q_ERR_ALIGN;
     if (want_row && (!aligned16(q_row) || ldq_row % 16)) return FP8Q_ERR_ALIGN;
     if (want_col && (!aligned16(q_colT) || ldq_colT % 16)) return FP8Q_ERR_ALIGN;
@@ -175,7 +188,7 @@ int fp8_quant_transpose_e8m0(const void* x, int x_dtype, int64_t rows, int64_t c
     fp8q::launch_quant_transpose_e8m0(x, x_dtype, rows, cols, ldx, want_row ? q_row : nullptr, ldq_row,
                                       e_row, lde_row, want_col ? q_colT : nullptr, ldq_colT, e_colT,
                                       lde_colT, static_cast<hipStream_t>(stream));
-    return launch_status();
+    return launch_status(stream);
 }
 
 int fp8_gemm_e8m0(int64_t M, int64_t N, int64_t K,
@@ -211,7 +224,7 @@ int fp8_gemm_e8m0(int64_t M, int64_t N, int64_t K,
     if (!fp8q::launch_gemm_e8m0(M, N, K, a, lda, ea, ldea, b, ldb, b_layout, eb, ldeb, eb_kind, c, ldc,
                                 c_dtype, static_cast<hipStream_t>(stream)))
         return FP8Q_ERR_UNSUPPORTED;
-    return launch_status();
+    return launch_status(stream);
 }
 
 int fp8_adam_step(int64_t n, float* p, const void* g, int g_dtype, uint8_t* mq, float* ms,
@@ -242,7 +255,7 @@ int fp8_adam_step(int64_t n, float* p, const void* g, int g_dtype, uint8_t* mq, 
     a.bc2_sqrt = (float)std::sqrt(1.0 - std::pow(beta2, (double)step));
     a.eps = (float)eps;
     fp8q::launch_adam_fp8(n, p, g, g_dtype, mq, ms, vq, vs, a, static_cast<hipStream_t>(stream));
-    return launch_status();
+    return launch_status(stream);
 }
 
 // Validation of the operands of a dense GEMM (everything but the output).
@@ -295,7 +308,7 @@ int fp8_gemm_blockscaled_e4m3(int64_t M, int64_t N, int64_t K,
     if (!fp8q::launch_gemm_e4m3(M, N, K, a, lda, sa, ldsa, sa_kind, b, ldb, b_layout, sb, ldsb, sb_kind,
                                 q, ldq, s, lds, static_cast<hipStream_t>(stream)))
         return FP8Q_ERR_UNSUPPORTED;
-    return launch_status();
+    return launch_status(stream);
 }
 
 int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K,
@@ -330,7 +343,7 @@ int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K,
     if (!fp8q::launch_gemm(M, N, K, a, lda, sa, ldsa, sa_kind, b, ldb, b_layout, sb, ldsb, sb_kind, c,
                            ldc, c_dtype, static_cast<hipStream_t>(stream)))
         return FP8Q_ERR_UNSUPPORTED;
-    return launch_status();
+    return launch_status(stream);
 }
 
 int fp8_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K,
@@ -353,10 +366,12 @@ int fp8_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K,
     if (reinterpret_cast<uintptr_t>(group_offsets) & 3u) return FP8Q_ERR_ALIGN;
     int st = check_device();
     if (st != FP8Q_OK) return st;
+    st = offsets_status(group_offsets, G, M_pad, stream);
+    if (st != FP8Q_OK) return st;
     if (!fp8q::launch_grouped_gemm(G, M_pad, N, K, a, lda, sa, ldsa, group_offsets, b, sb, c, ldc,
                                    c_dtype, static_cast<hipStream_t>(stream)))
         return FP8Q_ERR_UNSUPPORTED;
-    return launch_status();
+    return launch_status(stream);
 }
 
 int fp8_grouped_gemm_dgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K,
@@ -378,10 +393,12 @@ int fp8_grouped_gemm_dgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K,
     if (reinterpret_cast<uintptr_t>(group_offsets) & 3u) return FP8Q_ERR_ALIGN;
     int st = check_device();
     if (st != FP8Q_OK) return st;
+    st = offsets_status(group_offsets, G, M_pad, stream);
+    if (st != FP8Q_OK) return st;
     if (!fp8q::launch_grouped_gemm_dgrad(G, M_pad, N, K, a, lda, sa, ldsa, group_offsets, w, sw, c, ldc,
                                          c_dtype, static_cast<hipStream_t>(stream)))
         return FP8Q_ERR_UNSUPPORTED;
-    return launch_status();
+    return launch_status(stream);
 }
 
 int fp8_grouped_gemm_wgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K,
@@ -403,10 +420,12 @@ int fp8_grouped_gemm_wgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K,
     if (reinterpret_cast<uintptr_t>(group_offsets) & 3u) return FP8Q_ERR_ALIGN;
     int st = check_device();
     if (st != FP8Q_OK) return st;
+    st = offsets_status(group_offsets, G, M_pad, stream);
+    if (st != FP8Q_OK) return st;
     if (!fp8q::launch_grouped_gemm_wgrad(G, M_pad, N, K, a, lda, sa, ldsa, b, ldb, sb, ldsb, group_offsets,
                                          c, ldc, static_cast<hipStream_t>(stream)))
         return FP8Q_ERR_UNSUPPORTED;
-    return launch_status();
+    return launch_status(stream);
 }
 
 }  // extern "C"

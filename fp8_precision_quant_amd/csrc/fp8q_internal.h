@@ -13,6 +13,12 @@ namespace fp8q {
 // compute units of the current device (cached per device)
 int device_cu_count();
 
+// FP8Q_CHECK=1 in the environment (read at every call)
+bool debug_checks_enabled();
+// Checks the group-offset contract on the device (synchronizes `st`):
+// FP8Q_OK, FP8Q_ERR_SHAPE if violated, FP8Q_ERR_LAUNCH / _DEVICE on a HIP error.
+int check_group_offsets(const int32_t* offsets, int64_t G, int64_t M_pad, hipStream_t st);
+
 void launch_quant_blockwise(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
                             int kind, uint8_t* q, int64_t ldq, float* s, int64_t lds,
                             hipStream_t st);

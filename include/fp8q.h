@@ -60,6 +60,12 @@
  *    launch error is reported as FP8Q_ERR_LAUNCH.
  *  - Calls are stateless and thread-safe (the only state is a per-device
  *    architecture check cached at first use).
+ *  - Debug mode: with the environment variable FP8Q_CHECK=1 (read at every
+ *    call) each call synchronizes its stream after enqueueing and reports an
+ *    error of the work as FP8Q_ERR_LAUNCH, and the grouped GEMMs first check
+ *    the group-offset contract on the device (one small kernel and a
+ *    synchronization; a violation returns FP8Q_ERR_SHAPE and enqueues no
+ *    GEMM).  Without it the offsets are the caller's responsibility.
  */
 #ifndef FP8Q_H
 #define FP8Q_H
@@ -188,7 +194,7 @@ int fp8_gemm_blockscaled_e4m3(int64_t M, int64_t N, int64_t K,
  * B[e][n][:] (128x128 block scales).
  *  a, lda, sa, ldsa : A codes [M_pad][K] (contiguous groups), scales
  *                     sa[m*ldsa + kb].
- *  group_offsets    : DEVICE int32[G+1]; off[0] = 0, off[G] = M_pad,
+ *  group_offsets    : DEVICE int32[G+1]; off[0] = 0, off[G] <= M_pad,
  *                     non-decreasing, every off[e] a multiple of 128 (the
  *                     caller pads each group with zero rows; zero codes with
  *                     s = 0 give zero output rows).  This device-side
