@@ -67,8 +67,8 @@ M, N, K = 4096, 14336, 4096     # tokens, out features (14336), in features
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_mlp_fwd_bwd_step.txt")
 CSRC = os.path.join(ROOT, "fp8_precision_quant_amd", "csrc")
 KERNEL_SOURCES = {
-    "quant": ["quant.hip", "fp8q_device.h"],
-    "quant_transpose": ["quant_transpose.hip", "fp8q_device.h"],
+    "quant": ["quant.hip", "quant_io.h", "fp8q_device.h"],
+    "quant_transpose": ["quant_transpose.hip", "quant_io.h", "fp8q_device.h"],
     "gemm": ["gemm_nk.hip", "gemm_w4.hip", "gemm_lds.h", "gemm.hip", "gemm_common.h", "fp8q_device.h"],
 }
 

@@ -22,6 +22,8 @@ constexpr int kGroupM = 16;
 constexpr int kAStage = TBM * TBK;   // bytes
 constexpr int kBStage = TBN * TBK;
 constexpr int kStageBytes = kAStage + kBStage; // A at 0, B at kAStage
+// groups whose offsets fit in LDS (grouped launches with more are unsupported)
+constexpr int kMaxLdsGroups = 1024;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 

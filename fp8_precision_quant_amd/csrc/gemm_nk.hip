@@ -46,8 +46,6 @@ constexpr int kThreads = 512;
 
 }  // namespace
 
-// groups whose offsets fit in LDS (grouped launches with more fall back)
-constexpr int kMaxLdsGroups = 1024;
 
 // ---------------------------------------------------------------------------
 // The kernel.  Each wave owns all 128 rows of its 64 columns (32 MFMAs per

@@ -185,9 +185,15 @@ struct W4Scales {
 
 }  // namespace
 
-template <int SA_MODE, int SB_MODE, int OUT>
+// GROUPED: the MoE forward over padded groups of rows.  Row tile m0 belongs
+// to group e with off[e] <= m0 < off[e+1] (offsets held in LDS), whose
+// expert's B and block scales it multiplies; rows at or past off[G] are not
+// stored.
+template <int SA_MODE, int SB_MODE, int OUT, bool GROUPED>
 __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4_kernel(GemmArgs p)
 {
+    static_assert(!GROUPED || (SA_MODE == SA_ROW && SB_MODE == SB_BLOCK && OUT != OUT_E4M3),
+                  "grouped: row-scaled A, block-scaled B, fp32 or bf16 out");
     static_assert(OUT != OUT_E4M3 || SB_MODE != SB_ROW, "quantize-on-store: uniform B scales");
     // direct loads per chunk and wave: 4 of A, 8 of B, one of A's and one of
     // B's scales where they are per row / per block
@@ -197,6 +203,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     __shared__ __attribute__((aligned(16))) float SBs[kStages][SB_MODE == SB_ROW ? TBN : 4];
     // quantize-on-store: each wave's row maxima over its 64 columns
     __shared__ float RowMax[OUT == OUT_E4M3 ? kW4Threads / 64 : 1][OUT == OUT_E4M3 ? TBM : 1];
+    __shared__ int32_t goff[GROUPED ? kMaxLdsGroups + 1 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -225,6 +232,19 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         tn0 = (int64_t)(idx / gsz) * TBN;
     };
     const int my_tiles = (range_len - local + nwg - 1) / nwg;
+    if (GROUPED) {
+        for (int i = tid; i <= p.G; i += kW4Threads) goff[i] = p.offsets[i];
+        __syncthreads();
+    }
+    // group of row tile m0 (wave-uniform): the last e with off[e] <= m0
+    auto group_of = [&](int64_t m0) __attribute__((always_inline)) {
+        int lo = 0, hi = p.G - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((int64_t)goff[mid] <= m0) lo = mid; else hi = mid - 1;
+        }
+        return __builtin_amdgcn_readfirstlane(lo);
+    };
     const int KB = p.KB;
     const int total = my_tiles * KB;       // chunks of this workgroup, tile after tile
 
@@ -233,9 +253,9 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     const int64_t M = p.M, N = p.N, K = p.K;
     const int64_t nblocks = (N + 127) / 128;
     const __amdgpu_buffer_rsrc_t ra = rsrc(p.a, (M - 1) * p.lda + K);
-    const __amdgpu_buffer_rsrc_t rb = rsrc(p.b, (N - 1) * p.ldb + K);
+    __amdgpu_buffer_rsrc_t rb = rsrc(p.b, (N - 1) * p.ldb + K);
     const __amdgpu_buffer_rsrc_t rsa = rsrc(p.sa, SA_MODE == SA_ROW ? ((M - 1) * p.ldsa + KB) * 4 : 4);
-    const __amdgpu_buffer_rsrc_t rsb =
+    __amdgpu_buffer_rsrc_t rsb =
         rsrc(p.sb, SB_MODE == SB_ROW     ? ((N - 1) * p.ldsb + KB) * 4
                    : SB_MODE == SB_BLOCK ? ((nblocks - 1) * p.ldsb + KB) * 4
                                          : 4);
@@ -262,6 +282,12 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         if (SA_MODE == SA_ROW) vsa = (uint32_t)((lm0 + 32 * wq + l) * p.ldsa * 4);
         if (SB_MODE == SB_ROW) vsb = (uint32_t)((ln0 + 64 * wq + l) * p.ldsb * 4);
         if (SB_MODE == SB_BLOCK) vsb = (uint32_t)((ln0 / 128 + (wq >> 1)) * p.ldsb * 4);
+        if (GROUPED) {
+            // the expert of the load cursor's tile: its B and block scales
+            const int e = group_of(lm0);
+            rb = rsrc(p.b + (int64_t)e * p.b_group_stride, (N - 1) * p.ldb + K);
+            rsb = rsrc(p.sb + (int64_t)e * p.sb_group_stride, p.sb_group_stride * 4);
+        }
     };
     load_offsets();
     // load d (0 .. ND-1) of the cursor's chunk into stage st
@@ -394,6 +420,8 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     int c_ord = 0;
     int64_t cm0, cn0;
     tile_origin(0, cm0, cn0);
+    // rows stored: [0, M), or [0, off[G]) for groups of rows
+    const int64_t m_end = GROUPED ? min(M, (int64_t)__builtin_amdgcn_readfirstlane(goff[p.G])) : M;
     auto store_tile = [&]() __attribute__((always_inline)) {
         if constexpr (OUT == OUT_E4M3) {
             // The output's 1x128 tiles along N: a tile is the 64 columns of
@@ -430,7 +458,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
                     quant8(v, ts, code[2 * jp], code[2 * jp + 1]);
                 }
                 const int64_t m = cm0 + 16 * i + lrow;
-                if (m >= M) continue;
+                if (m >= m_end) continue;
                 uint8_t* qrow = reinterpret_cast<uint8_t*>(p.c) + m * p.ldc;
 #pragma unroll
                 for (int j = 0; j < NNI; ++j) {
@@ -451,7 +479,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 #pragma unroll
         for (int i = 0; i < PMI; ++i) {
             const int64_t m = cm0 + 16 * i + lrow;
-            if (m >= M) continue;
+            if (m >= m_end) continue;
 #pragma unroll
             for (int j = 0; j < NNI; ++j) {
                 const int64_t n = cn0 + 64 * wq + 16 * j + 4 * kgrp;
@@ -553,7 +581,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     w4_wait_vm<0>();
 }
 
-template <int SA_MODE, int SB_MODE>
+template <int SA_MODE, int SB_MODE, bool GROUPED = false>
 static void w4_launch_out(const GemmArgs& g, int out, hipStream_t st)
 {
     GemmArgs a = g;
@@ -562,11 +590,11 @@ static void w4_launch_out(const GemmArgs& g, int out, hipStream_t st)
     const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
     dim3 grid((uint32_t)(tiles < g.num_cus ? tiles : g.num_cus));
     if (out == OUT_BF16)
-        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_BF16>), grid, dim3(kW4Threads), 0, st, a);
+        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_BF16, GROUPED>), grid, dim3(kW4Threads), 0, st, a);
     else if (out == OUT_F32)
-        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_F32>), grid, dim3(kW4Threads), 0, st, a);
-    else if constexpr (SB_MODE != SB_ROW)
-        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_E4M3>), grid, dim3(kW4Threads), 0, st, a);
+        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_F32, GROUPED>), grid, dim3(kW4Threads), 0, st, a);
+    else if constexpr (SB_MODE != SB_ROW && !GROUPED)
+        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_E4M3, GROUPED>), grid, dim3(kW4Threads), 0, st, a);
 }
 
 // [N][K] B only.  B read as stored ([K][N], data gradient) takes twice as
@@ -586,6 +614,20 @@ bool launch_gemm_w4(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, int 
         else if (sb_mode == SB_ROW) w4_launch_out<SA_TENSOR, SB_ROW>(g, out, st);
         else w4_launch_out<SA_TENSOR, SB_TENSOR>(g, out, st);
     }
+    return true;
+}
+
+// The MoE forward (groups of rows, expert B stored [N][K]) with K a multiple
+// of 128; false if it does not cover the call.  Every operand must span less
+// than 2 GiB (32-bit buffer offsets; A's loads run up to a tile past M).
+bool launch_grouped_gemm_w4(const GemmArgs& g, bool out_bf16, hipStream_t st)
+{
+    const int64_t lim = (int64_t)1 << 31;
+    if (g.K <= 0 || g.K % 128 != 0 || g.G < 1 || g.G > kMaxLdsGroups) return false;
+    if ((g.M + TBM) * g.lda >= lim || g.N * g.ldb >= lim || (g.M + TBM) * g.ldsa * 4 >= lim ||
+        g.sb_group_stride * 4 >= lim)
+        return false;
+    w4_launch_out<SA_ROW, SB_BLOCK, true>(g, out_bf16 ? OUT_BF16 : OUT_F32, st);
     return true;
 }
 

@@ -42,18 +42,22 @@ def _run(a, sa, off, b, sb, out=torch.float32, c=None):
     return c
 
 
-def test_small_groups_with_empty_and_ragged():
+# K = 400 takes the kernel that masks a partial last chunk; K = 384 (whole
+# chunks) the four-wave kernel
+@pytest.mark.parametrize("K", [400, 384])
+def test_small_groups_with_empty_and_ragged(K):
     counts = [100, 0, 260, 1, 0, 128]
-    G, N, K = len(counts), 300, 400
+    G, N = len(counts), 300
+    KB = -(-K // 128)
     off = np.concatenate([[0], np.cumsum([-(-c // 128) * 128 for c in counts])])
     M = int(off[-1])
     A = np.zeros((M, K), np.uint8)
-    sa = np.zeros((M, 4), np.float32)
+    sa = np.zeros((M, KB), np.float32)
     for e, cnt in enumerate(counts):
         A[off[e]:off[e] + cnt] = _codes((cnt, K), 10 + e)
-        sa[off[e]:off[e] + cnt] = _scales((cnt, 4), 20 + e)
+        sa[off[e]:off[e] + cnt] = _scales((cnt, KB), 20 + e)
     B = _codes((G, N, K), 30)
-    sb = _scales((G, 3, 4), 31)
+    sb = _scales((G, 3, KB), 31)
     c = host(_run(A, sa, off, B, sb))
     co = oracle.grouped_gemm(A, sa, off, B, sb)
     _, R = oracle.grouped_gemm(A, sa, off, B, sb, f64=True)
