@@ -228,7 +228,7 @@ bool launch_grouped_gemm_wgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K, c
     g.G = (int)G;
     g.c_group_stride = N * ldc;
     g.num_cus = device_cu_count();
-    return launch_grouped_wgrad_nk(g, st);
+    return launch_grouped_wgrad_w4(g, st);
 }
 
 }  // namespace fp8q

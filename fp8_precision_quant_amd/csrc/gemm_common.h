@@ -67,6 +67,8 @@ bool launch_gemm_w4(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, int 
 // The four-wave kernel over groups of rows (MoE forward, K % 128 == 0);
 // false if it does not cover the call.
 bool launch_grouped_gemm_w4(const GemmArgs& g, bool out_bf16, hipStream_t st);
+// ... and over groups of K (MoE weight gradient); false if not covered.
+bool launch_grouped_wgrad_w4(const GemmArgs& g, hipStream_t st);
 // Grouped (MoE) launch of the same kernel: A row tiles select their expert
 // through the device group offsets (B per expert as [N][K] for the forward,
 // read as [K][N] for dgrad); false if the call is not covered.
@@ -75,8 +77,5 @@ bool launch_grouped_gemm_nk(const GemmArgs& g, bool out_bf16, bool b_kn, hipStre
 // (row-scaled A; block-scaled B as [N][K] or [K][N], or row-scaled [N][K]
 // B), whose row strides are multiples of 4; false if the call is not covered.
 bool launch_gemm_nk_e8m0(const GemmArgs& g, int sb_mode, bool b_kn, bool out_bf16, hipStream_t st);
-// Grouped weight gradient: for each group, the product over the group's
-// token chunks only, into the group's own fp32 output block.
-bool launch_grouped_wgrad_nk(const GemmArgs& g, hipStream_t st);
 
 }  // namespace fp8q

@@ -95,9 +95,8 @@ __device__ __forceinline__ v4f col_scales(uint32_t a, int j)
 }
 
 // GMODE: 0 dense; 1 groups of A rows (MoE forward and dgrad: the row tile's
-// group selects the expert's B and B scales); 2 groups of K (MoE weight
-// gradient: tile rows index the virtual matrix [G][M], the group's token
-// chunks are the K loop and each group has its own output block).
+// group selects the expert's B and B scales).  (The MoE weight gradient,
+// groups of K, runs on gemm_w4.hip.)
 // P2: power-of-two scales given as E8M0 bytes (p.sa / p.sb point at bytes),
 // applied by the scaled MFMA itself: the chunk's product is accumulated in
 // place, with no partial sum and no scale FMA.  A scale grid's rows are read
@@ -109,9 +108,8 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     static_assert(!(B_KN && SB_MODE == SB_ROW), "row-scaled B is [N][K] only");
     static_assert(!P2 || (GMODE == 0 && SA_MODE == SA_ROW && SB_MODE != SB_TENSOR && OUT != OUT_E4M3),
                   "power-of-two scales: dense, row-scaled A, block- or row-scaled B, fp32/bf16 out");
+    static_assert(GMODE == 0 || GMODE == 1, "dense or groups of rows");
     __shared__ int32_t goff[GMODE != 0 ? kMaxLdsGroups + 1 : 1];
-    // groups of K: this XCD's groups, largest first
-    __shared__ int32_t xlist[GMODE == 2 ? kMaxLdsGroups / 8 + 1 : 1];
     __shared__ __attribute__((aligned(16))) uint8_t Stg[kStages][kStageBytes];
     __shared__ __attribute__((aligned(16))) float SAs[kStages][TBM];
     // B scales of a chunk: its two 128-column blocks (block-scaled B), or its
@@ -138,23 +136,8 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     const int range_start = xcd * (T >> 3) + min(xcd, T & 7);
     const int range_len = (T >> 3) + (xcd < (T & 7) ? 1 : 0);
     const int span = kGroupM * p.tiles_n;
-    // Groups of K have very uneven K loops (the tokens routed to each
-    // expert), so there the groups are ranked by size and dealt to the XCDs
-    // in snake order (ranks 0..7 to XCDs 0..7, ranks 8..15 to XCDs 7..0,
-    // ...); each XCD's workgroups walk its groups' tiles largest group first.
-    // A group's tiles stay on one XCD, so its operands share one L2.
-    const int tiles_g = (int)((p.M + TBM - 1) / TBM);    // row tiles per group
-    const int tpg = tiles_g * p.tiles_n;                  // tiles per group
-    const int nx = GMODE == 2 ? (p.G >> 3) + (((p.G >> 3) & 1) ? (7 - xcd < (p.G & 7)) : (xcd < (p.G & 7))) : 0;
-    const int tiles_here = GMODE == 2 ? nx * tpg : range_len;
+    const int tiles_here = range_len;
     auto tile_origin = [&](int i, int64_t& tm0, int64_t& tn0) {
-        if (GMODE == 2) {
-            const int e = xlist[i / tpg];
-            const int rem = i % tpg;
-            tm0 = (int64_t)(e * tiles_g + rem % tiles_g) * TBM;
-            tn0 = (int64_t)(rem / tiles_g) * TBN;
-            return;
-        }
         const int pid = range_start + i;
         const int group = pid / span;
         const int first_m = group * kGroupM;
@@ -169,28 +152,12 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
         for (int i = tid; i <= p.G; i += kThreads) goff[i] = p.offsets[i];
         __syncthreads();
     }
-    if (GMODE == 2) {
-        for (int e = tid; e < p.G; e += kThreads) {
-            const int size = goff[e + 1] - goff[e];
-            int rank = 0;
-            for (int f = 0; f < p.G; ++f) {
-                const int sf = goff[f + 1] - goff[f];
-                rank += (sf > size || (sf == size && f < e)) ? 1 : 0;
-            }
-            const int x = ((rank >> 3) & 1) ? 7 - (rank & 7) : (rank & 7);
-            if (x == xcd) xlist[rank >> 3] = e;
-        }
-        __syncthreads();
-    }
     int64_t m0, n0;
     tile_origin(ti, m0, n0);
 
     const int64_t M = p.M, N = p.N, K = p.K;
-    const int KBg = p.KB;                 // chunks of the whole K extent
-    const int k_tail = (int)(K - (int64_t)(KBg - 1) * TBK);
-    int KB = KBg;                         // chunks of this tile's K loop
-    int kb_base = 0;                      // its first chunk
-    int64_t c_off = 0;                    // its output block (elements)
+    const int KB = p.KB;                  // chunks of the K loop
+    const int k_tail = (int)(K - (int64_t)(KB - 1) * TBK);
 
     const int64_t ext_a = (M - 1) * p.lda + ((K + 15) & ~(int64_t)15);
     const int64_t ext_b = B_KN ? (K - 1) * p.ldb + ((N + 15) & ~(int64_t)15)
@@ -201,11 +168,9 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     bool tile_live = true;
     // groups of rows: the tile's group e (off[e] <= m0 < off[e+1]) selects
     // expert e's B and block scales; tiles at or past off[G] are computed
-    // from group G-1 but not stored.  Groups of K: virtual row tile
-    // e * ceil(M/128) + t is row tile t of group e, whose K loop runs over
-    // the chunks [off[e], off[e+1]) / 128 (none for an empty group).
-    // (values read from LDS are made wave-uniform explicitly, so that the
-    // loop bounds and addresses derived from them stay scalar)
+    // from group G-1 but not stored.  (values read from LDS are made
+    // wave-uniform explicitly, so that addresses derived from them stay
+    // scalar)
     auto set_group = [&](int64_t& tm0) {
         if (GMODE == 1) {
             int lo = 0, hi = p.G - 1;
@@ -216,13 +181,6 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
             grp_e = __builtin_amdgcn_readfirstlane(lo);
             tile_live = tm0 < (int64_t)__builtin_amdgcn_readfirstlane(goff[p.G]);
             rb = rsrc(p.b + (int64_t)grp_e * p.b_group_stride, ext_b);
-        } else if (GMODE == 2) {
-            const int vt = (int)(tm0 / TBM);
-            grp_e = __builtin_amdgcn_readfirstlane(vt / tiles_g);
-            tm0 = (int64_t)(vt - grp_e * tiles_g) * TBM;
-            kb_base = __builtin_amdgcn_readfirstlane(goff[grp_e]) / TBK;
-            KB = __builtin_amdgcn_readfirstlane(goff[grp_e + 1]) / TBK - kb_base;
-            c_off = (int64_t)grp_e * p.c_group_stride;
         }
     };
     set_group(m0);
@@ -235,17 +193,17 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
     const bool load_sa = SA_MODE == SA_ROW && wq < 2;
     const bool load_sb = SB_MODE == SB_ROW || (SB_MODE == SB_BLOCK && wq == 2);
     // (E8M0 grids: byte extents, each row's last word included)
-    const int64_t kb_words = (KBg + 3) & ~3, nb_words = (nblocks + 3) & ~3;
+    const int64_t kb_words = (KB + 3) & ~3, nb_words = (nblocks + 3) & ~3;
     const __amdgpu_buffer_rsrc_t rsa = rsrc(p.sa, SA_MODE != SA_ROW ? 4
                                                   : P2 ? (M - 1) * p.ldsa + kb_words
-                                                       : ((M - 1) * p.ldsa + KBg) * 4);
+                                                       : ((M - 1) * p.ldsa + KB) * 4);
     auto sb_rsrc = [&]() {
-        if (SB_MODE == SB_ROW) return rsrc(p.sb, P2 ? (N - 1) * p.ldsb + kb_words : ((N - 1) * p.ldsb + KBg) * 4);
+        if (SB_MODE == SB_ROW) return rsrc(p.sb, P2 ? (N - 1) * p.ldsb + kb_words : ((N - 1) * p.ldsb + KB) * 4);
         if (SB_MODE == SB_BLOCK) {
             const float* sbg = p.sb + (GMODE == 1 ? (int64_t)grp_e * p.sb_group_stride : 0);
-            if (P2) return rsrc(sbg, B_KN ? (int64_t)(KBg - 1) * p.ldsb + nb_words : (nblocks - 1) * p.ldsb + kb_words);
-            if (B_KN) return rsrc(sbg, ((int64_t)(KBg - 1) * p.ldsb + nblocks) * 4);
-            return rsrc(sbg, ((nblocks - 1) * p.ldsb + KBg) * 4);
+            if (P2) return rsrc(sbg, B_KN ? (int64_t)(KB - 1) * p.ldsb + nb_words : (nblocks - 1) * p.ldsb + kb_words);
+            if (B_KN) return rsrc(sbg, ((int64_t)(KB - 1) * p.ldsb + nblocks) * 4);
+            return rsrc(sbg, ((nblocks - 1) * p.ldsb + KB) * 4);
         }
         return rsrc(p.sb, 4);
     };
@@ -297,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
         // here rather than hoisted out of the loop into spilled registers
         uint32_t a_lds = lds_addr(&Stg[st][0]) + (uint32_t)(32 * wq * TBK);
         uint32_t b_lds = lds_addr(&Stg[st][kAStage]) + (uint32_t)(B_KN ? 32 * wq * TBN : 64 * wq * TBK);
-        const uint32_t kg = (uint32_t)(kb_base + kb);   // chunk within the whole K extent
+        const uint32_t kg = (uint32_t)kb;
         uint32_t a_soff = kg * TBK, a_step = 8u * (uint32_t)p.lda;
         uint32_t b_soff = B_KN ? kg * TBK * (uint32_t)p.ldb : kg * TBK;
         uint32_t b_step = (B_KN ? 4u : 8u) * (uint32_t)p.ldb;
@@ -562,8 +520,7 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
                 if (kReadsFirst && c + 2 < KB) issue(c + 2);
                 __builtin_amdgcn_sched_barrier(0);
                 reads_wait(f);
-                // (groups of K are whole 128-token chunks: no partial chunk)
-                if (GMODE != 2 && c == KB - 1 && k_tail < TBK) mask_k_tail(f);
+                if (c == KB - 1 && k_tail < TBK) mask_k_tail(f);
                 if (kPrio == 1) __builtin_amdgcn_s_setprio(0);
                 if (kPrio == 2) __builtin_amdgcn_s_setprio(1);
                 bar();
@@ -697,18 +654,18 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
                         if (OUT == OUT_BF16) {
                             const uint32_t lo = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
                             const uint32_t hi = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-                            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.c) + c_off + m * p.ldc + n) = make_uint2(lo, hi);
+                            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.c) + m * p.ldc + n) = make_uint2(lo, hi);
                         } else {
-                            *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.c) + c_off + m * p.ldc + n) = v;
+                            *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.c) + m * p.ldc + n) = v;
                         }
                     } else {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             if (n + r < N) {
                                 if (OUT == OUT_BF16)
-                                    reinterpret_cast<uint16_t*>(p.c)[c_off + m * p.ldc + n + r] = (uint16_t)bf16_rne(v[r]);
+                                    reinterpret_cast<uint16_t*>(p.c)[m * p.ldc + n + r] = (uint16_t)bf16_rne(v[r]);
                                 else
-                                    reinterpret_cast<float*>(p.c)[c_off + m * p.ldc + n + r] = v[r];
+                                    reinterpret_cast<float*>(p.c)[m * p.ldc + n + r] = v[r];
                             }
                         }
                     }
@@ -732,7 +689,7 @@ template <int SA_MODE, int SB_MODE, bool B_KN, int OUT, int GMODE = 0, bool P2 =
 static void launch_out(const GemmArgs& g, hipStream_t st)
 {
     GemmArgs a = g;
-    a.tiles_m = (int)((g.M + TBM - 1) / TBM) * (GMODE == 2 ? g.G : 1);
+    a.tiles_m = (int)((g.M + TBM - 1) / TBM);
     a.tiles_n = (int)((g.N + TBN - 1) / TBN);
     const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
     dim3 grid((uint32_t)(tiles < g.num_cus ? tiles : g.num_cus));
@@ -757,17 +714,6 @@ bool launch_grouped_gemm_nk(const GemmArgs& g, bool out_bf16, bool b_kn, hipStre
     const int out = out_bf16 ? OUT_BF16 : OUT_F32;
     if (b_kn) launch_tiles<SA_ROW, SB_BLOCK, true, 1>(g, out, st);
     else launch_tiles<SA_ROW, SB_BLOCK, false, 1>(g, out, st);
-    return true;
-}
-
-bool launch_grouped_wgrad_nk(const GemmArgs& g, hipStream_t st)
-{
-    const int64_t lim = (int64_t)1 << 31;
-    if (g.G > kMaxLdsGroups || g.M * g.lda >= lim || (g.N + TBK) * g.ldb >= lim ||
-        g.M * g.ldsa * 4 >= lim || g.N * g.ldsb * 4 >= lim || (int64_t)g.KB * TBK >= lim ||
-        (int64_t)g.G * ((g.M + TBM - 1) / TBM) >= lim)
-        return false;
-    launch_out<SA_ROW, SB_ROW, false, OUT_F32, 2>(g, st);
     return true;
 }
 

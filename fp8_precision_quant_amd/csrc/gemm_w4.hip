@@ -185,15 +185,25 @@ struct W4Scales {
 
 }  // namespace
 
-// GROUPED: the MoE forward over padded groups of rows.  Row tile m0 belongs
-// to group e with off[e] <= m0 < off[e+1] (offsets held in LDS), whose
-// expert's B and block scales it multiplies; rows at or past off[G] are not
-// stored.
-template <int SA_MODE, int SB_MODE, int OUT, bool GROUPED>
+// GMODE 0: one dense product.
+// GMODE 1 (MoE forward, groups of rows): row tile m0 belongs to group e with
+//   off[e] <= m0 < off[e+1] (offsets held in LDS), whose expert's B and block
+//   scales it multiplies; rows at or past off[G] are not stored.
+// GMODE 2 (MoE weight gradient, groups of K): the tiles of output block e
+//   (dW[e] = p.c + e * c_group_stride) contract over the chunks
+//   [off[e], off[e+1]) / 128 of the token axis only.  Non-empty groups are
+//   ranked by size and dealt to the XCDs in snake order (ranks 0..7 to XCDs
+//   0..7, 8..15 to 7..0, ...); each XCD's workgroups walk its groups' tiles,
+//   largest group first, so a group's operands share one L2 and the K loops
+//   balance across XCDs.  Empty groups get dW[e] = 0, their tiles stored by
+//   all workgroups before the chunk stream.
+template <int SA_MODE, int SB_MODE, int OUT, int GMODE>
 __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4_kernel(GemmArgs p)
 {
-    static_assert(!GROUPED || (SA_MODE == SA_ROW && SB_MODE == SB_BLOCK && OUT != OUT_E4M3),
-                  "grouped: row-scaled A, block-scaled B, fp32 or bf16 out");
+    static_assert(GMODE != 1 || (SA_MODE == SA_ROW && SB_MODE == SB_BLOCK && OUT != OUT_E4M3),
+                  "groups of rows: row-scaled A, block-scaled B, fp32 or bf16 out");
+    static_assert(GMODE != 2 || (SA_MODE == SA_ROW && SB_MODE == SB_ROW && OUT == OUT_F32),
+                  "groups of K: row-scaled A and B, fp32 out");
     static_assert(OUT != OUT_E4M3 || SB_MODE != SB_ROW, "quantize-on-store: uniform B scales");
     // direct loads per chunk and wave: 4 of A, 8 of B, one of A's and one of
     // B's scales where they are per row / per block
@@ -203,11 +213,18 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     __shared__ __attribute__((aligned(16))) float SBs[kStages][SB_MODE == SB_ROW ? TBN : 4];
     // quantize-on-store: each wave's row maxima over its 64 columns
     __shared__ float RowMax[OUT == OUT_E4M3 ? kW4Threads / 64 : 1][OUT == OUT_E4M3 ? TBM : 1];
-    __shared__ int32_t goff[GROUPED ? kMaxLdsGroups + 1 : 1];
+    __shared__ int32_t goff[GMODE != 0 ? kMaxLdsGroups + 1 : 1];
+    // groups of K: this XCD's groups, largest first
+    __shared__ int32_t xlist[GMODE == 2 ? kMaxLdsGroups / 8 + 1 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wq = __builtin_amdgcn_readfirstlane(tid >> 6);   // columns [64 wq, 64 wq + 64) of the tile
+
+    if (GMODE != 0) {
+        for (int i = tid; i <= p.G; i += kW4Threads) goff[i] = p.offsets[i];
+        __syncthreads();
+    }
 
     // Persistent workgroups dealt to the 8 XCDs round-robin; XCD x owns a
     // contiguous range of tile ids, walked by its workgroups in lockstep in
@@ -216,26 +233,57 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     const int T = p.tiles_m * p.tiles_n;
     const int xcd = blockIdx.x & 7;
     const int local = blockIdx.x >> 3;
-    const int G = gridDim.x;
-    const int nwg = (G >> 3) + (xcd < (G & 7) ? 1 : 0);
+    const int nwg = (gridDim.x >> 3) + (xcd < (int)(gridDim.x & 7) ? 1 : 0);
     const int range_start = xcd * (T >> 3) + min(xcd, T & 7);
-    const int range_len = (T >> 3) + (xcd < (T & 7) ? 1 : 0);
-    if (local >= range_len) return;
+    int tiles_here = (T >> 3) + (xcd < (T & 7) ? 1 : 0);
     const int span = kGroupM * p.tiles_n;
-    auto tile_origin = [&](int ordinal, int64_t& tm0, int64_t& tn0) __attribute__((always_inline)) {
-        const int pid = range_start + local + ordinal * nwg;
-        const int group = pid / span;
-        const int first_m = group * kGroupM;
-        const int gsz = min(p.tiles_m - first_m, kGroupM);
-        const int idx = pid - group * span;
-        tm0 = (int64_t)(first_m + idx % gsz) * TBM;
-        tn0 = (int64_t)(idx / gsz) * TBN;
-    };
-    const int my_tiles = (range_len - local + nwg - 1) / nwg;
-    if (GROUPED) {
-        for (int i = tid; i <= p.G; i += kW4Threads) goff[i] = p.offsets[i];
+    const int64_t M = p.M, N = p.N, K = p.K;
+    if constexpr (GMODE == 2) {
+        int gn = 0;   // non-empty groups
+        for (int f = 0; f < p.G; ++f) gn += goff[f + 1] > goff[f] ? 1 : 0;
+        for (int e = tid; e < p.G; e += kW4Threads) {
+            const int size = goff[e + 1] - goff[e];
+            if (size == 0) continue;
+            int rank = 0;
+            for (int f = 0; f < p.G; ++f) {
+                const int sf = goff[f + 1] - goff[f];
+                rank += (sf > size || (sf == size && f < e)) ? 1 : 0;
+            }
+            const int x = ((rank >> 3) & 1) ? 7 - (rank & 7) : (rank & 7);
+            if (x == xcd) xlist[rank >> 3] = e;
+        }
         __syncthreads();
+        const int q = gn >> 3, rem = gn & 7;
+        const int nx = q + ((q & 1) ? (xcd >= 8 - rem ? 1 : 0) : (xcd < rem ? 1 : 0));
+        tiles_here = nx * T;
+        // dW[e] = 0 for the empty groups: (empty group, tile) pairs dealt to
+        // all workgroups, 128 x 256 fp32 zeros per tile
+        const int ne = p.G - gn;
+        for (int j = blockIdx.x; j < ne * T; j += gridDim.x) {
+            int e = -1;
+            for (int f = 0, k = j / T; f < p.G; ++f) {
+                if (goff[f + 1] == goff[f] && k-- == 0) {
+                    e = f;
+                    break;
+                }
+            }
+            if (e < 0) break;   // (not reached: j < ne * T)
+            const int t = j % T;
+            const int64_t zm0 = (int64_t)(t % p.tiles_m) * TBM, zn0 = (int64_t)(t / p.tiles_m) * TBN;
+            float* cz = reinterpret_cast<float*>(p.c) + (int64_t)e * p.c_group_stride;
+            for (int i = tid; i < TBM * (TBN / 4); i += kW4Threads) {
+                const int64_t m = zm0 + i / (TBN / 4), n = zn0 + 4 * (i % (TBN / 4));
+                if (m >= M) continue;
+                if (n + 3 < N) {
+                    *reinterpret_cast<v4f*>(cz + m * p.ldc + n) = v4f{0.f, 0.f, 0.f, 0.f};
+                } else {
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N) cz[m * p.ldc + n + r] = 0.0f;
+                }
+            }
+        }
     }
+    if (local >= tiles_here) return;
     // group of row tile m0 (wave-uniform): the last e with off[e] <= m0
     auto group_of = [&](int64_t m0) __attribute__((always_inline)) {
         int lo = 0, hi = p.G - 1;
@@ -245,12 +293,42 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         }
         return __builtin_amdgcn_readfirstlane(lo);
     };
+    // Tile `ordinal` of this workgroup: origin, group, and its chunks
+    // [kb0, kb0 + kbn) of the K axis.
+    struct Tile {
+        int64_t m0, n0;
+        int e, kb0, kbn;
+    };
+    auto tile_at = [&](int ordinal) __attribute__((always_inline)) {
+        Tile t;
+        t.e = 0;
+        t.kb0 = 0;
+        t.kbn = p.KB;
+        if constexpr (GMODE == 2) {
+            const int i = local + ordinal * nwg;
+            t.e = __builtin_amdgcn_readfirstlane(xlist[i / T]);
+            const int r = i % T;
+            t.m0 = (int64_t)(r % p.tiles_m) * TBM;
+            t.n0 = (int64_t)(r / p.tiles_m) * TBN;
+            t.kb0 = __builtin_amdgcn_readfirstlane(goff[t.e]) / TBK;
+            t.kbn = __builtin_amdgcn_readfirstlane(goff[t.e + 1]) / TBK - t.kb0;
+        } else {
+            const int pid = range_start + local + ordinal * nwg;
+            const int group = pid / span;
+            const int first_m = group * kGroupM;
+            const int gsz = min(p.tiles_m - first_m, kGroupM);
+            const int idx = pid - group * span;
+            t.m0 = (int64_t)(first_m + idx % gsz) * TBM;
+            t.n0 = (int64_t)(idx / gsz) * TBN;
+            if constexpr (GMODE == 1) t.e = group_of(t.m0);
+        }
+        return t;
+    };
+    const int my_tiles = (tiles_here - local + nwg - 1) / nwg;
     const int KB = p.KB;
-    const int total = my_tiles * KB;       // chunks of this workgroup, tile after tile
 
     // Buffer resources bound every load to its operand; rows past M or N
     // start past the bound and read as zero (they feed outputs not stored).
-    const int64_t M = p.M, N = p.N, K = p.K;
     const int64_t nblocks = (N + 127) / 128;
     const __amdgpu_buffer_rsrc_t ra = rsrc(p.a, (M - 1) * p.lda + K);
     __amdgpu_buffer_rsrc_t rb = rsrc(p.b, (N - 1) * p.ldb + K);
@@ -268,11 +346,11 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     // [32 wq, 32 wq + 32), and its own B scales.  Load t differs from
     // load 0 by t row steps (scalar offset) and, for odd t, by the swizzle key.
     int ld_ord = 0, ld_k = 0;
-    int64_t lm0, ln0;
-    tile_origin(0, lm0, ln0);
+    Tile lt = tile_at(0);
     uint32_t va0, va1, vb0, vb1, vsa = 0, vsb = 0;
     auto load_offsets = [&]() __attribute__((always_inline)) {
         const int l = lane;
+        const int64_t lm0 = lt.m0, ln0 = lt.n0;
         const int64_t arow = lm0 + 32 * wq + (l >> 3);
         va0 = (uint32_t)(arow * p.lda) + 16u * (uint32_t)((l & 7) ^ (l >> 3));
         va1 = (uint32_t)(arow * p.lda) + 16u * (uint32_t)((l & 7) ^ (l >> 3) ^ 1);
@@ -282,18 +360,17 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         if (SA_MODE == SA_ROW) vsa = (uint32_t)((lm0 + 32 * wq + l) * p.ldsa * 4);
         if (SB_MODE == SB_ROW) vsb = (uint32_t)((ln0 + 64 * wq + l) * p.ldsb * 4);
         if (SB_MODE == SB_BLOCK) vsb = (uint32_t)((ln0 / 128 + (wq >> 1)) * p.ldsb * 4);
-        if (GROUPED) {
+        if (GMODE == 1) {
             // the expert of the load cursor's tile: its B and block scales
-            const int e = group_of(lm0);
-            rb = rsrc(p.b + (int64_t)e * p.b_group_stride, (N - 1) * p.ldb + K);
-            rsb = rsrc(p.sb + (int64_t)e * p.sb_group_stride, p.sb_group_stride * 4);
+            rb = rsrc(p.b + (int64_t)lt.e * p.b_group_stride, (N - 1) * p.ldb + K);
+            rsb = rsrc(p.sb + (int64_t)lt.e * p.sb_group_stride, p.sb_group_stride * 4);
         }
     };
     load_offsets();
     // load d (0 .. ND-1) of the cursor's chunk into stage st
     auto load_item = [&](auto dt, int st) __attribute__((always_inline)) {
         constexpr int d = decltype(dt)::value;
-        const uint32_t kg = (uint32_t)ld_k;
+        const uint32_t kg = (uint32_t)(lt.kb0 + ld_k);
         if constexpr (d < 4) {
             dma16_at(ra, lds_addr(&Stg[st][0]) + (uint32_t)((32 * wq + 8 * d) * TBK), (d & 1) ? va1 : va0,
                      kg * TBK + (uint32_t)(8 * d) * (uint32_t)p.lda);
@@ -314,11 +391,11 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     // read valid memory into a free stage and are never used, which keeps
     // the loads per chunk, and so the wait counts, the same for every chunk)
     auto load_advance = [&]() __attribute__((always_inline)) {
-        if (++ld_k == KB) {
+        if (++ld_k == lt.kbn) {
             ld_k = 0;
             if (ld_ord + 1 < my_tiles) {
                 ++ld_ord;
-                tile_origin(ld_ord, lm0, ln0);
+                lt = tile_at(ld_ord);
                 load_offsets();
             }
         }
@@ -418,11 +495,14 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 
     // ---- output of a finished tile ----
     int c_ord = 0;
-    int64_t cm0, cn0;
-    tile_origin(0, cm0, cn0);
+    Tile ct = tile_at(0);
     // rows stored: [0, M), or [0, off[G]) for groups of rows
-    const int64_t m_end = GROUPED ? min(M, (int64_t)__builtin_amdgcn_readfirstlane(goff[p.G])) : M;
+    const int64_t m_end = GMODE == 1 ? min(M, (int64_t)__builtin_amdgcn_readfirstlane(goff[p.G])) : M;
     auto store_tile = [&]() __attribute__((always_inline)) {
+        const int64_t cm0 = ct.m0, cn0 = ct.n0;
+        // the output block of the tile's group (groups of K)
+        void* const cbase = GMODE == 2 ? (void*)(reinterpret_cast<float*>(p.c) + (int64_t)ct.e * p.c_group_stride)
+                                       : p.c;
         if constexpr (OUT == OUT_E4M3) {
             // The output's 1x128 tiles along N: a tile is the 64 columns of
             // this wave and those of wave wq ^ 1 (same rows).  Columns past N
@@ -459,7 +539,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
                 }
                 const int64_t m = cm0 + 16 * i + lrow;
                 if (m >= m_end) continue;
-                uint8_t* qrow = reinterpret_cast<uint8_t*>(p.c) + m * p.ldc;
+                uint8_t* qrow = reinterpret_cast<uint8_t*>(cbase) + m * p.ldc;
 #pragma unroll
                 for (int j = 0; j < NNI; ++j) {
                     const int64_t n = ncol0 + 16 * j;
@@ -488,18 +568,18 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
                     if (OUT == OUT_BF16) {
                         const uint32_t lo = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
                         const uint32_t hi = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
-                        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.c) + m * p.ldc + n) = make_uint2(lo, hi);
+                        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(cbase) + m * p.ldc + n) = make_uint2(lo, hi);
                     } else {
-                        *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.c) + m * p.ldc + n) = v;
+                        *reinterpret_cast<v4f*>(reinterpret_cast<float*>(cbase) + m * p.ldc + n) = v;
                     }
                 } else {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         if (n + r < N) {
                             if (OUT == OUT_BF16)
-                                reinterpret_cast<uint16_t*>(p.c)[m * p.ldc + n + r] = (uint16_t)bf16_rne(v[r]);
+                                reinterpret_cast<uint16_t*>(cbase)[m * p.ldc + n + r] = (uint16_t)bf16_rne(v[r]);
                             else
-                                reinterpret_cast<float*>(p.c)[m * p.ldc + n + r] = v[r];
+                                reinterpret_cast<float*>(cbase)[m * p.ldc + n + r] = v[r];
                         }
                     }
                 }
@@ -518,7 +598,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     reads_done(std::integral_constant<int, 0>{});
 
     // ---- the chunk stream ----
-    int g = 0, ck = 0;
+    int ck = 0;
     int st_w = 0;          // stage of chunk g (takes chunk g + 3)
     auto iteration = [&](auto s_tag) __attribute__((always_inline)) {
         constexpr int S = decltype(s_tag)::value;
@@ -549,7 +629,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         });
         load_advance();
         reads_done(std::integral_constant<int, NS>{});
-        if (ck == KB - 1) {
+        if (ck == ct.kbn - 1) {
             // last chunk of the tile: blocks 29..31 (their MFMAs are more
             // than 12 instructions back after this padding), then the output
             asm volatile("s_nop 7" ::: "memory");
@@ -564,37 +644,39 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
             for (int i = 0; i < PMI; ++i)
 #pragma unroll
                 for (int j = 0; j < NNI; ++j) acc[i][j] = zero;
-            if (++c_ord < my_tiles) tile_origin(c_ord, cm0, cn0);
+            if (++c_ord < my_tiles) ct = tile_at(c_ord);
             ck = 0;
         } else {
             ++ck;
         }
         st_w = st_r;
-        ++g;
     };
     for (;;) {
         iteration(std::integral_constant<int, 0>{});
-        if (g == total) break;
+        if (c_ord == my_tiles) break;
         iteration(std::integral_constant<int, 1>{});
-        if (g == total) break;
+        if (c_ord == my_tiles) break;
     }
     w4_wait_vm<0>();
 }
 
-template <int SA_MODE, int SB_MODE, bool GROUPED = false>
+template <int SA_MODE, int SB_MODE, int GMODE = 0>
 static void w4_launch_out(const GemmArgs& g, int out, hipStream_t st)
 {
     GemmArgs a = g;
     a.tiles_m = (int)((g.M + TBM - 1) / TBM);
     a.tiles_n = (int)((g.N + TBN - 1) / TBN);
-    const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+    // groups of K: every workgroup derives its tiles from the offsets
+    const int64_t tiles = GMODE == 2 ? g.num_cus : (int64_t)a.tiles_m * a.tiles_n;
     dim3 grid((uint32_t)(tiles < g.num_cus ? tiles : g.num_cus));
-    if (out == OUT_BF16)
-        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_BF16, GROUPED>), grid, dim3(kW4Threads), 0, st, a);
-    else if (out == OUT_F32)
-        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_F32, GROUPED>), grid, dim3(kW4Threads), 0, st, a);
-    else if constexpr (SB_MODE != SB_ROW && !GROUPED)
-        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_E4M3, GROUPED>), grid, dim3(kW4Threads), 0, st, a);
+    if (out == OUT_BF16) {
+        if constexpr (GMODE != 2)
+            hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_BF16, GMODE>), grid, dim3(kW4Threads), 0, st, a);
+    } else if (out == OUT_F32) {
+        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_F32, GMODE>), grid, dim3(kW4Threads), 0, st, a);
+    } else if constexpr (SB_MODE != SB_ROW && GMODE == 0) {
+        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_E4M3, GMODE>), grid, dim3(kW4Threads), 0, st, a);
+    }
 }
 
 // [N][K] B only.  B read as stored ([K][N], data gradient) takes twice as
@@ -627,7 +709,22 @@ bool launch_grouped_gemm_w4(const GemmArgs& g, bool out_bf16, hipStream_t st)
     if ((g.M + TBM) * g.lda >= lim || g.N * g.ldb >= lim || (g.M + TBM) * g.ldsa * 4 >= lim ||
         g.sb_group_stride * 4 >= lim)
         return false;
-    w4_launch_out<SA_ROW, SB_BLOCK, true>(g, out_bf16 ? OUT_BF16 : OUT_F32, st);
+    w4_launch_out<SA_ROW, SB_BLOCK, 1>(g, out_bf16 ? OUT_BF16 : OUT_F32, st);
+    return true;
+}
+
+// The MoE weight gradient (groups of K over the token axis, row-scaled
+// operands, fp32 out); false if it does not cover the call.  The token
+// extent M_pad (the GEMM's K) is a multiple of 128 by contract; with
+// M_pad = 0 every group is empty and the kernel only stores zeros.
+bool launch_grouped_wgrad_w4(const GemmArgs& g, hipStream_t st)
+{
+    const int64_t lim = (int64_t)1 << 31;
+    if (g.K < 0 || g.K % 128 != 0 || g.G < 1 || g.G > kMaxLdsGroups) return false;
+    if ((g.M + TBM) * g.lda >= lim || (g.N + TBN) * g.ldb >= lim || (g.M + TBM) * g.ldsa * 4 >= lim ||
+        (g.N + TBN) * g.ldsb * 4 >= lim || (int64_t)g.G * g.c_group_stride * 4 >= ((int64_t)1 << 62))
+        return false;
+    w4_launch_out<SA_ROW, SB_ROW, 2>(g, OUT_F32, st);
     return true;
 }
 

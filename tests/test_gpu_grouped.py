@@ -204,6 +204,37 @@ def test_wgrad_small_groups_with_empty_and_ragged():
             assert np.all(hb[e, :, :K] == 0)
 
 
+def test_wgrad_one_group_holds_every_token():
+    # a single non-empty group: one XCD computes, every workgroup zero-fills
+    counts = [0, 0, 390, 0]
+    G, N, K = len(counts), 256, 512
+    off = _groups(counts)
+    M = int(off[-1])
+    g = np.random.Generator(np.random.PCG64(151))
+    dy = g.standard_normal((M, N)).astype(np.float32)
+    x = g.standard_normal((M, K)).astype(np.float32)
+    dy[off[2] + counts[2]:] = 0
+    x[off[2] + counts[2]:] = 0
+    at, sat = oracle.quant_1x128(np.ascontiguousarray(dy.T))
+    bt, sbt = oracle.quant_1x128(np.ascontiguousarray(x.T))
+    buf = torch.full((G, N, K), -7.0, dtype=torch.float32, device=DEV)
+    hb = host(_run_wgrad(at, sat, bt, sbt, off, c=buf))
+    co = oracle.grouped_gemm_wgrad(at, sat, bt, sbt, off)
+    _, R = oracle.grouped_gemm_wgrad(at, sat, bt, sbt, off, f64=True)
+    gemm_parity(hb[2], co[2], R[2])
+    for e in (0, 1, 3):
+        assert np.all(hb[e] == 0)
+
+
+def test_wgrad_without_tokens_is_zero():
+    G, N, K = 3, 130, 300
+    off = np.zeros(G + 1, np.int64)
+    at, sat = np.zeros((N, 0), np.uint8), np.zeros((N, 0), np.float32)
+    bt, sbt = np.zeros((K, 0), np.uint8), np.zeros((K, 0), np.float32)
+    buf = torch.full((G, N, K), -7.0, dtype=torch.float32, device=DEV)
+    assert np.all(host(_run_wgrad(at, sat, bt, sbt, off, c=buf)) == 0)
+
+
 @pytest.fixture(scope="module")
 def moe_backward(moe_inputs):
     m, gu, dn = moe_inputs
