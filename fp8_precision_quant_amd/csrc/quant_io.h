@@ -90,6 +90,32 @@ __device__ __forceinline__ void raw_load(const float* row, int64_t c, int64_t co
     r.b = c + 4 < cols ? *reinterpret_cast<const uint4*>(row + c + 4) : make_uint4(0, 0, 0, 0);
 }
 
+// Loads and fp32 values of 8 elements known to lie inside the matrix (no
+// bounds tests: blocks away from the right and bottom edges).
+__device__ __forceinline__ void raw_load_full(const uint16_t* p, Raw8<uint16_t>& r)
+{
+    r.v = *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void raw_load_full(const float* p, Raw8<float>& r)
+{
+    r.a = *reinterpret_cast<const uint4*>(p);
+    r.b = *reinterpret_cast<const uint4*>(p + 4);
+}
+__device__ __forceinline__ void raw_f32_full(const Raw8<uint16_t>& r, float v[8])
+{
+    v[0] = bf16_lo(r.v.x); v[1] = bf16_hi(r.v.x);
+    v[2] = bf16_lo(r.v.y); v[3] = bf16_hi(r.v.y);
+    v[4] = bf16_lo(r.v.z); v[5] = bf16_hi(r.v.z);
+    v[6] = bf16_lo(r.v.w); v[7] = bf16_hi(r.v.w);
+}
+__device__ __forceinline__ void raw_f32_full(const Raw8<float>& r, float v[8])
+{
+    v[0] = __uint_as_float(r.a.x); v[1] = __uint_as_float(r.a.y);
+    v[2] = __uint_as_float(r.a.z); v[3] = __uint_as_float(r.a.w);
+    v[4] = __uint_as_float(r.b.x); v[5] = __uint_as_float(r.b.y);
+    v[6] = __uint_as_float(r.b.z); v[7] = __uint_as_float(r.b.w);
+}
+
 // fp32 values of a raw load; elements at or beyond `cols` become 0.
 __device__ __forceinline__ void raw_f32(const Raw8<uint16_t>& r, int64_t c, int64_t cols, float v[8])
 {

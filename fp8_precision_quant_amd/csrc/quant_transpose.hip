@@ -18,6 +18,8 @@
 // through LDS.  The column codes are produced already in column order (the
 // 4 rows of a thread packed in one dword), staged in LDS as the transposed
 // block and written back as 16-byte row segments of X^T.
+#include <type_traits>
+
 #include "fp8q_device.h"
 #include "fp8q_internal.h"
 #include "quant_io.h"
@@ -93,32 +95,38 @@ __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
     const bool do_row = q_row != nullptr;
     const bool do_col = q_colT != nullptr;
 
-    // block b covers rows [128 rb, +128) and columns [128 cb, +128)
-    auto origin = [&](uint32_t b, int64_t& rb, int64_t& cb) {
-        const uint32_t r = fdiv(b, blocks_per_row);
-        rb = r;
-        cb = b - r * blocks_per_row.d;
-    };
-    // this thread's 4 rows of block b (rows past the end load nothing)
-    auto load = [&](uint32_t b, Raw8<T>* R) {
-        int64_t rb, cb;
-        origin(b, rb, cb);
-#pragma unroll
-        for (int u = 0; u < kQtRows; ++u) {
-            const int64_t r = rb * kTile + kQtRows * g + u;
-            raw_load(x + (r < rows ? r : 0) * ldx, r < rows ? cb * kTile + 8 * l : cols, cols, R[u]);
-        }
-    };
+    // this block: rows [r0, r0 + 128), columns [c0, c0 + 128)
+    const uint32_t b = blockIdx.x;
+    const uint32_t rbu = fdiv(b, blocks_per_row);
+    const int64_t rb = rbu, cb = b - rbu * blocks_per_row.d;
+    const int64_t r0 = rb * kTile, c0 = cb * kTile;
 
-    auto quantize = [&](uint32_t b, const Raw8<T>* R) {
-        int64_t rb, cb;
-        origin(b, rb, cb);
-        const int64_t r0 = rb * kTile, c0 = cb * kTile;
+    // FULL: the block lies inside the matrix, so no element, row or column
+    // needs a bounds test (every block but those on the right and bottom
+    // edges); the same body with the tests covers the edges
+    auto body = [&](auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
         float v[kQtRows][8];
+        {
+            Raw8<T> R[kQtRows];
+            if constexpr (FULL) {
+                const T* xb = x + (r0 + kQtRows * g) * ldx + c0 + 8 * l;
 #pragma unroll
-        for (int u = 0; u < kQtRows; ++u) {
-            const int64_t r = r0 + kQtRows * g + u;
-            raw_f32(R[u], r < rows ? c0 + 8 * l : cols, cols, v[u]);
+                for (int u = 0; u < kQtRows; ++u) raw_load_full(xb + u * ldx, R[u]);
+#pragma unroll
+                for (int u = 0; u < kQtRows; ++u) raw_f32_full(R[u], v[u]);
+            } else {
+#pragma unroll
+                for (int u = 0; u < kQtRows; ++u) {
+                    const int64_t r = r0 + kQtRows * g + u;
+                    raw_load(x + (r < rows ? r : 0) * ldx, r < rows ? c0 + 8 * l : cols, cols, R[u]);
+                }
+#pragma unroll
+                for (int u = 0; u < kQtRows; ++u) {
+                    const int64_t r = r0 + kQtRows * g + u;
+                    raw_f32(R[u], r < rows ? c0 + 8 * l : cols, cols, v[u]);
+                }
+            }
         }
 
         // row maxima (DPP over the 16 lanes of each row), column partial maxima
@@ -150,7 +158,7 @@ __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
             col_s[si] = ts.s;
             col_y[si] = ts.y;
             col_mode[si] = ts.mode;
-            if (do_col && c0 + tid < cols)
+            if (do_col && (FULL || c0 + tid < cols))
                 s_colT[(c0 + tid) * lds_colT + rb] = stored_scale<S>(ts);
         } else if (tid < 2 * kTile) {
             int i = tid - kTile;
@@ -158,21 +166,26 @@ __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
             row_s[i] = ts.s;
             row_y[i] = ts.y;
             row_mode[i] = ts.mode;
-            if (do_row && r0 + i < rows)
+            if (do_row && (FULL || r0 + i < rows))
                 s_row[(r0 + i) * lds_row + cb] = stored_scale<S>(ts);
         }
         __syncthreads();
 
         if (do_row) {
             const int64_t c = c0 + 8 * l;
+            uint8_t* const qb = q_row + (r0 + kQtRows * g) * ldq_row + c;
 #pragma unroll
             for (int u = 0; u < kQtRows; ++u) {
                 int i = kQtRows * g + u;
                 TileScale ts{row_s[i], row_y[i], row_mode[i]};
                 uint32_t lo, hi;
                 quant8_as<S>(v[u], ts, lo, hi);
-                int64_t r = r0 + i;
-                if (r < rows && c < cols) store8(q_row + r * ldq_row, c, cols, lo, hi);
+                if constexpr (FULL) {
+                    *reinterpret_cast<uint2*>(qb + u * ldq_row) = make_uint2(lo, hi);
+                } else {
+                    const int64_t r = r0 + i;
+                    if (r < rows && c < cols) store8(q_row + r * ldq_row, c, cols, lo, hi);
+                }
             }
         }
 
@@ -195,25 +208,23 @@ __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
                 int seg = (tid & 7) * 16;              // byte offset along X's rows
                 int64_t cglob = c0 + cr;
                 int64_t rglob = r0 + seg;
-                if (cglob < cols && rglob < rows) {
-                    uint4 w = *reinterpret_cast<const uint4*>(stage + stage_row(cr) * kStagePitch +
-                                                              16 * ((tid & 7) ^ stage_key(cr)));
-                    uint8_t* dst = q_colT + cglob * ldq_colT + rglob;
-                    if (rglob + 16 <= rows) {
-                        *reinterpret_cast<uint4*>(dst) = w;
-                    } else {
-                        uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-                        for (int k = 0; k < 16 && rglob + k < rows; ++k)
-                            dst[k] = (uint8_t)((wd[k >> 2] >> (8 * (k & 3))) & 0xFF);
-                    }
+                const uint4 w = *reinterpret_cast<const uint4*>(stage + stage_row(cr) * kStagePitch +
+                                                                16 * ((tid & 7) ^ stage_key(cr)));
+                uint8_t* dst = q_colT + cglob * ldq_colT + rglob;
+                if (FULL || (cglob < cols && rglob + 16 <= rows)) {
+                    *reinterpret_cast<uint4*>(dst) = w;
+                } else if (cglob < cols && rglob < rows) {
+                    uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+                    for (int k = 0; k < 16 && rglob + k < rows; ++k)
+                        dst[k] = (uint8_t)((wd[k >> 2] >> (8 * (k & 3))) & 0xFF);
                 }
             }
         }
     };
-
-    Raw8<T> R[kQtRows];
-    load(blockIdx.x, R);
-    quantize(blockIdx.x, R);
+    if (r0 + kTile <= rows && c0 + kTile <= cols)
+        body(std::true_type{});
+    else
+        body(std::false_type{});
 }
 
 template <typename S>
