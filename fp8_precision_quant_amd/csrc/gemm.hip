@@ -185,7 +185,7 @@ bool launch_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K, const u
     g.b_group_stride = N * K;
     g.sb_group_stride = ((N + 127) / 128) * (int64_t)g.KB;
     g.num_cus = device_cu_count();
-    if (launch_grouped_gemm_w4(g, c_dtype == FP8Q_BF16, st)) return true;
+    if (launch_grouped_gemm_w4(g, c_dtype == FP8Q_BF16, false, st)) return true;
     return launch_grouped_gemm_nk(g, c_dtype == FP8Q_BF16, false, st);
 }
 
@@ -208,6 +208,7 @@ bool launch_grouped_gemm_dgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K, c
     g.b_group_stride = N * K;
     g.sb_group_stride = (int64_t)g.KB * g.ldsb;
     g.num_cus = device_cu_count();
+    if (launch_grouped_gemm_w4(g, c_dtype == FP8Q_BF16, true, st)) return true;
     return launch_grouped_gemm_nk(g, c_dtype == FP8Q_BF16, true, st);
 }
 

@@ -64,9 +64,10 @@ bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, int 
 // and K a multiple of 128 (fp32, bf16 or E4M3 output); false if it does not
 // cover the call.
 bool launch_gemm_w4(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, int out, hipStream_t st);
-// The four-wave kernel over groups of rows (MoE forward, K % 128 == 0);
-// false if it does not cover the call.
-bool launch_grouped_gemm_w4(const GemmArgs& g, bool out_bf16, hipStream_t st);
+// The four-wave kernel over groups of rows (MoE forward, B [N][K], and
+// dgrad, B read as stored [K][N]; K % 128 == 0); false if it does not cover
+// the call.
+bool launch_grouped_gemm_w4(const GemmArgs& g, bool out_bf16, bool b_kn, hipStream_t st);
 // ... and over groups of K (MoE weight gradient); false if not covered.
 bool launch_grouped_wgrad_w4(const GemmArgs& g, hipStream_t st);
 // Grouped (MoE) launch of the same kernel: A row tiles select their expert

@@ -70,6 +70,33 @@ constexpr int kW4Threads = 256;
     X(22, "a[176:179]", "a[180:183]") \
     X(23, "a[184:187]", "a[188:191]")
 
+// the four 8-byte quarters of fragment F (transposing reads of B read as stored)
+#define W4_QUARTERS(X) \
+    X(0, "a[0:1]", "a[2:3]", "a[4:5]", "a[6:7]") \
+    X(1, "a[8:9]", "a[10:11]", "a[12:13]", "a[14:15]") \
+    X(2, "a[16:17]", "a[18:19]", "a[20:21]", "a[22:23]") \
+    X(3, "a[24:25]", "a[26:27]", "a[28:29]", "a[30:31]") \
+    X(4, "a[32:33]", "a[34:35]", "a[36:37]", "a[38:39]") \
+    X(5, "a[40:41]", "a[42:43]", "a[44:45]", "a[46:47]") \
+    X(6, "a[48:49]", "a[50:51]", "a[52:53]", "a[54:55]") \
+    X(7, "a[56:57]", "a[58:59]", "a[60:61]", "a[62:63]") \
+    X(8, "a[64:65]", "a[66:67]", "a[68:69]", "a[70:71]") \
+    X(9, "a[72:73]", "a[74:75]", "a[76:77]", "a[78:79]") \
+    X(10, "a[80:81]", "a[82:83]", "a[84:85]", "a[86:87]") \
+    X(11, "a[88:89]", "a[90:91]", "a[92:93]", "a[94:95]") \
+    X(12, "a[96:97]", "a[98:99]", "a[100:101]", "a[102:103]") \
+    X(13, "a[104:105]", "a[106:107]", "a[108:109]", "a[110:111]") \
+    X(14, "a[112:113]", "a[114:115]", "a[116:117]", "a[118:119]") \
+    X(15, "a[120:121]", "a[122:123]", "a[124:125]", "a[126:127]") \
+    X(16, "a[128:129]", "a[130:131]", "a[132:133]", "a[134:135]") \
+    X(17, "a[136:137]", "a[138:139]", "a[140:141]", "a[142:143]") \
+    X(18, "a[144:145]", "a[146:147]", "a[148:149]", "a[150:151]") \
+    X(19, "a[152:153]", "a[154:155]", "a[156:157]", "a[158:159]") \
+    X(20, "a[160:161]", "a[162:163]", "a[164:165]", "a[166:167]") \
+    X(21, "a[168:169]", "a[170:171]", "a[172:173]", "a[174:175]") \
+    X(22, "a[176:177]", "a[178:179]", "a[180:181]", "a[182:183]") \
+    X(23, "a[184:185]", "a[186:187]", "a[188:189]", "a[190:191]")
+
 #define W4_AGPRS "a0", "a1", "a2", "a3", "a4", "a5", "a6", "a7", "a8", "a9", "a10", "a11", "a12", "a13", "a14", "a15", "a16", "a17", "a18", "a19", "a20", "a21", "a22", "a23", "a24", "a25", "a26", "a27", "a28", "a29", "a30", "a31", "a32", "a33", "a34", "a35", "a36", "a37", "a38", "a39", "a40", "a41", "a42", "a43", "a44", "a45", "a46", "a47", "a48", "a49", "a50", "a51", "a52", "a53", "a54", "a55", "a56", "a57", "a58", "a59", "a60", "a61", "a62", "a63", "a64", "a65", "a66", "a67", "a68", "a69", "a70", "a71", "a72", "a73", "a74", "a75", "a76", "a77", "a78", "a79", "a80", "a81", "a82", "a83", "a84", "a85", "a86", "a87", "a88", "a89", "a90", "a91", "a92", "a93", "a94", "a95", "a96", "a97", "a98", "a99", "a100", "a101", "a102", "a103", "a104", "a105", "a106", "a107", "a108", "a109", "a110", "a111", "a112", "a113", "a114", "a115", "a116", "a117", "a118", "a119", "a120", "a121", "a122", "a123", "a124", "a125", "a126", "a127", "a128", "a129", "a130", "a131", "a132", "a133", "a134", "a135", "a136", "a137", "a138", "a139", "a140", "a141", "a142", "a143", "a144", "a145", "a146", "a147", "a148", "a149", "a150", "a151", "a152", "a153", "a154", "a155", "a156", "a157", "a158", "a159", "a160", "a161", "a162", "a163", "a164", "a165", "a166", "a167", "a168", "a169", "a170", "a171", "a172", "a173", "a174", "a175", "a176", "a177", "a178", "a179", "a180", "a181", "a182", "a183", "a184", "a185", "a186", "a187", "a188", "a189", "a190", "a191"
 
 // A fragments (multiplicand rows) and B fragments by number, for the MFMA
@@ -110,6 +137,21 @@ __device__ __forceinline__ void w4_read_half(uint32_t addr)
         else asm volatile("ds_read_b128 " HI ", %0 offset:%1" ::"v"(addr), "i"(OFF) : "memory", W4_AGPRS); \
     }
     W4_FRAGS(X)
+#undef X
+}
+
+// transposing 8-byte LDS read into quarter Q of fragment F
+template <int F, int Q, int OFF>
+__device__ __forceinline__ void w4_read_quarter(uint32_t addr)
+{
+#define X(FI, Q0, Q1, Q2, Q3) \
+    if constexpr (F == FI) { \
+        if constexpr (Q == 0) asm volatile("ds_read_b64_tr_b8 " Q0 ", %0 offset:%1" ::"v"(addr), "i"(OFF) : "memory", W4_AGPRS); \
+        else if constexpr (Q == 1) asm volatile("ds_read_b64_tr_b8 " Q1 ", %0 offset:%1" ::"v"(addr), "i"(OFF) : "memory", W4_AGPRS); \
+        else if constexpr (Q == 2) asm volatile("ds_read_b64_tr_b8 " Q2 ", %0 offset:%1" ::"v"(addr), "i"(OFF) : "memory", W4_AGPRS); \
+        else asm volatile("ds_read_b64_tr_b8 " Q3 ", %0 offset:%1" ::"v"(addr), "i"(OFF) : "memory", W4_AGPRS); \
+    }
+    W4_QUARTERS(X)
 #undef X
 }
 
@@ -197,9 +239,13 @@ struct W4Scales {
 //   largest group first, so a group's operands share one L2 and the K loops
 //   balance across XCDs.  Empty groups get dW[e] = 0, their tiles stored by
 //   all workgroups before the chunk stream.
-template <int SA_MODE, int SB_MODE, int OUT, int GMODE>
+// B_KN: B read as stored [K][N] (the MoE dgrad's expert weights): the load
+// stages 32 K rows x 256 columns per wave and the fragment reads transpose
+// 8-byte quarters (ds_read_b64_tr_b8), twice the reads of [N][K] B.
+template <int SA_MODE, int SB_MODE, int OUT, int GMODE, bool B_KN = false>
 __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4_kernel(GemmArgs p)
 {
+    static_assert(!B_KN || (GMODE == 1 && SB_MODE == SB_BLOCK), "[K][N] B: the grouped dgrad only");
     static_assert(GMODE != 1 || (SA_MODE == SA_ROW && SB_MODE == SB_BLOCK && OUT != OUT_E4M3),
                   "groups of rows: row-scaled A, block-scaled B, fp32 or bf16 out");
     static_assert(GMODE != 2 || (SA_MODE == SA_ROW && SB_MODE == SB_ROW && OUT == OUT_F32),
@@ -331,11 +377,13 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     // start past the bound and read as zero (they feed outputs not stored).
     const int64_t nblocks = (N + 127) / 128;
     const __amdgpu_buffer_rsrc_t ra = rsrc(p.a, (M - 1) * p.lda + K);
-    __amdgpu_buffer_rsrc_t rb = rsrc(p.b, (N - 1) * p.ldb + K);
+    const int64_t b_ext = B_KN ? (K - 1) * p.ldb + ((N + 15) & ~(int64_t)15) : (N - 1) * p.ldb + K;
+    __amdgpu_buffer_rsrc_t rb = rsrc(p.b, b_ext);
     const __amdgpu_buffer_rsrc_t rsa = rsrc(p.sa, SA_MODE == SA_ROW ? ((M - 1) * p.ldsa + KB) * 4 : 4);
     __amdgpu_buffer_rsrc_t rsb =
         rsrc(p.sb, SB_MODE == SB_ROW     ? ((N - 1) * p.ldsb + KB) * 4
-                   : SB_MODE == SB_BLOCK ? ((nblocks - 1) * p.ldsb + KB) * 4
+                   : SB_MODE == SB_BLOCK ? (B_KN ? ((int64_t)(KB - 1) * p.ldsb + nblocks) * 4
+                                                 : ((nblocks - 1) * p.ldsb + KB) * 4)
                                          : 4);
     const float sa_t = SA_MODE == SA_TENSOR ? p.sa[0] : 0.0f;
     const float sb_t = SB_MODE == SB_TENSOR ? p.sb[0] : 0.0f;
@@ -354,15 +402,25 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         const int64_t arow = lm0 + 32 * wq + (l >> 3);
         va0 = (uint32_t)(arow * p.lda) + 16u * (uint32_t)((l & 7) ^ (l >> 3));
         va1 = (uint32_t)(arow * p.lda) + 16u * (uint32_t)((l & 7) ^ (l >> 3) ^ 1);
-        const int64_t brow = ln0 + 64 * wq + (l >> 3);
-        vb0 = (uint32_t)(brow * p.ldb) + 16u * (uint32_t)((l & 7) ^ (l >> 3));
-        vb1 = (uint32_t)(brow * p.ldb) + 16u * (uint32_t)((l & 7) ^ (l >> 3) ^ 1);
+        if (B_KN) {
+            // K rows [32 wq, 32 wq + 32) of the chunk, 4 per load, each 256
+            // columns; the 16-byte slot of column group (l & 15) is xor-ed
+            // with the row's key
+            const int r = 32 * wq + (l >> 4);
+            const int k0 = (l >> 4) ^ (8 * (wq & 1)), k1 = (4 + (l >> 4)) ^ (8 * (wq & 1));
+            vb0 = (uint32_t)(r * p.ldb + ln0) + 16u * (uint32_t)((l & 15) ^ k0);
+            vb1 = (uint32_t)(r * p.ldb + ln0) + 16u * (uint32_t)((l & 15) ^ k1);
+        } else {
+            const int64_t brow = ln0 + 64 * wq + (l >> 3);
+            vb0 = (uint32_t)(brow * p.ldb) + 16u * (uint32_t)((l & 7) ^ (l >> 3));
+            vb1 = (uint32_t)(brow * p.ldb) + 16u * (uint32_t)((l & 7) ^ (l >> 3) ^ 1);
+        }
         if (SA_MODE == SA_ROW) vsa = (uint32_t)((lm0 + 32 * wq + l) * p.ldsa * 4);
         if (SB_MODE == SB_ROW) vsb = (uint32_t)((ln0 + 64 * wq + l) * p.ldsb * 4);
-        if (SB_MODE == SB_BLOCK) vsb = (uint32_t)((ln0 / 128 + (wq >> 1)) * p.ldsb * 4);
+        if (SB_MODE == SB_BLOCK) vsb = (uint32_t)((ln0 / 128 + (wq >> 1)) * (B_KN ? 4 : p.ldsb * 4));
         if (GMODE == 1) {
             // the expert of the load cursor's tile: its B and block scales
-            rb = rsrc(p.b + (int64_t)lt.e * p.b_group_stride, (N - 1) * p.ldb + K);
+            rb = rsrc(p.b + (int64_t)lt.e * p.b_group_stride, b_ext);
             rsb = rsrc(p.sb + (int64_t)lt.e * p.sb_group_stride, p.sb_group_stride * 4);
         }
     };
@@ -376,14 +434,18 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
                      kg * TBK + (uint32_t)(8 * d) * (uint32_t)p.lda);
         } else if constexpr (d < 12) {
             constexpr int t = d - 4;
-            dma16_at(rb, lds_addr(&Stg[st][kAStage]) + (uint32_t)((64 * wq + 8 * t) * TBK), (t & 1) ? vb1 : vb0,
-                     kg * TBK + 8u * t * (uint32_t)p.ldb);
+            if constexpr (B_KN)
+                dma16_at(rb, lds_addr(&Stg[st][kAStage]) + (uint32_t)((32 * wq + 4 * t) * TBN), (t & 1) ? vb1 : vb0,
+                         (kg * TBK + 4u * t) * (uint32_t)p.ldb);
+            else
+                dma16_at(rb, lds_addr(&Stg[st][kAStage]) + (uint32_t)((64 * wq + 8 * t) * TBK), (t & 1) ? vb1 : vb0,
+                         kg * TBK + 8u * t * (uint32_t)p.ldb);
         } else if constexpr (SA_MODE == SA_ROW && d == 12) {
             if (lane < 32) dma4(rsa, &SAs[st][32 * wq], vsa, kg * 4);
         } else {
             if constexpr (SB_MODE == SB_ROW) dma4(rsb, &SBs[st][64 * wq], vsb, kg * 4);
             if constexpr (SB_MODE == SB_BLOCK) {
-                if (lane == 0) dma4(rsb, &SBs[st][wq], vsb, kg * 4);
+                if (lane == 0) dma4(rsb, &SBs[st][wq], vsb, B_KN ? kg * (uint32_t)p.ldsb * 4 : kg * 4);
             }
         }
     };
@@ -407,14 +469,24 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     const uint32_t a_rel0 = (uint32_t)sw(lrow, 2 * kgrp), a_rel1 = (uint32_t)sw(lrow, 2 * kgrp + 1);
     const uint32_t b_rel0 = (uint32_t)(kAStage + sw(64 * wq + lrow, 2 * kgrp));
     const uint32_t b_rel1 = (uint32_t)(kAStage + sw(64 * wq + lrow, 2 * kgrp + 1));
+    // [K][N] B: lane (kgrp, lrow) addresses K row 32 kgrp + lrow / 2 at column
+    // 64 wq + 16 j + 8 (lrow & 1); fragment j is fragment 0 with the 16-byte
+    // slot index xor j
+    uint32_t kn_rel[NNI] = {};
+    if (B_KN) {
+        const int r = 32 * kgrp + (lrow >> 1);
+        const uint32_t rel = (uint32_t)(kAStage + r * TBN + (((4 * wq) ^ kn_key(r)) << 4) + 8 * (lrow & 1));
+#pragma unroll
+        for (int j = 0; j < NNI; ++j) kn_rel[j] = rel ^ (uint32_t)(j << 4);
+    }
     const uint32_t sa_rel = lds_addr(&SAs[0][0]) + (uint32_t)lrow * 4;
     const uint32_t sb_rel = SB_MODE == SB_ROW ? lds_addr(&SBs[0][0]) + (uint32_t)(64 * wq + 4 * kgrp) * 4
                                               : lds_addr(&SBs[0][0]) + (uint32_t)wq * 4;
 
     W4Scales<SB_MODE> scl[2];
     // read item k (0 .. 31) of the chunk in stage st into fragment set NS and
-    // scale set NS: 0-1 B0, 2-17 A0..A7 (two halves each), 18-23 B1..B3,
-    // 24-31 the scales.
+    // scale set NS: 0-1 B0, 2-17 A0..A7 (two halves each), 18-23 B1..B3
+    // (with [K][N] B as two transposing quarters each), 24-31 the scales.
     auto read_item = [&](auto kt, auto nst, int st) __attribute__((always_inline)) {
         constexpr int k = decltype(kt)::value;
         constexpr int NS = decltype(nst)::value;
@@ -426,7 +498,12 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
             constexpr int j = k < 2 ? 0 : 1 + (k - 18) / 2;
             constexpr int h = k < 2 ? k : (k - 18) % 2;
             constexpr int F = 12 * NS + 8 + j;
-            w4_read_half<F, h, j * 16 * TBK>(base + (h ? b_rel1 : b_rel0));
+            if constexpr (B_KN) {
+                w4_read_quarter<F, 2 * h, (2 * h) * 8 * TBN>(base + kn_rel[j]);
+                w4_read_quarter<F, 2 * h + 1, (2 * h + 1) * 8 * TBN>(base + kn_rel[j]);
+            } else {
+                w4_read_half<F, h, j * 16 * TBK>(base + (h ? b_rel1 : b_rel0));
+            }
         } else {
             constexpr int i = k - 24;
             if constexpr (SA_MODE == SA_ROW) scl[NS].sa[i] = w4_ds32<i * 64>(sa_rel + (uint32_t)(st * TBM * 4));
@@ -666,7 +743,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     w4_wait_vm<0>();
 }
 
-template <int SA_MODE, int SB_MODE, int GMODE = 0>
+template <int SA_MODE, int SB_MODE, int GMODE = 0, bool B_KN = false>
 static void w4_launch_out(const GemmArgs& g, int out, hipStream_t st)
 {
     GemmArgs a = g;
@@ -677,10 +754,10 @@ static void w4_launch_out(const GemmArgs& g, int out, hipStream_t st)
     dim3 grid((uint32_t)(tiles < g.num_cus ? tiles : g.num_cus));
     if (out == OUT_BF16) {
         if constexpr (GMODE != 2)
-            hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_BF16, GMODE>), grid, dim3(kW4Threads), 0, st, a);
+            hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_BF16, GMODE, B_KN>), grid, dim3(kW4Threads), 0, st, a);
     } else if (out == OUT_F32) {
-        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_F32, GMODE>), grid, dim3(kW4Threads), 0, st, a);
-    } else if constexpr (SB_MODE != SB_ROW && GMODE == 0) {
+        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_F32, GMODE, B_KN>), grid, dim3(kW4Threads), 0, st, a);
+    } else if constexpr (SB_MODE != SB_ROW && GMODE == 0 && !B_KN) {
         hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_E4M3, GMODE>), grid, dim3(kW4Threads), 0, st, a);
     }
 }
@@ -705,17 +782,21 @@ bool launch_gemm_w4(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, int 
     return true;
 }
 
-// The MoE forward (groups of rows, expert B stored [N][K]) with K a multiple
-// of 128; false if it does not cover the call.  Every operand must span less
-// than 2 GiB (32-bit buffer offsets; A's loads run up to a tile past M).
-bool launch_grouped_gemm_w4(const GemmArgs& g, bool out_bf16, hipStream_t st)
+// The MoE forward (groups of rows, expert B stored [N][K]) and dgrad (expert
+// weight read as stored, [K][N]) with K a multiple of 128; false if it does
+// not cover the call.  Every operand must span less than 2 GiB (32-bit buffer
+// offsets; A's loads run up to a tile past M, B's up to a chunk past K).
+bool launch_grouped_gemm_w4(const GemmArgs& g, bool out_bf16, bool b_kn, hipStream_t st)
 {
     const int64_t lim = (int64_t)1 << 31;
     if (g.K <= 0 || g.K % 128 != 0 || g.G < 1 || g.G > kMaxLdsGroups) return false;
-    if ((g.M + TBM) * g.lda >= lim || g.N * g.ldb >= lim || (g.M + TBM) * g.ldsa * 4 >= lim ||
+    const int64_t b_span = b_kn ? (g.K + TBK) * g.ldb : g.N * g.ldb;
+    if ((g.M + TBM) * g.lda >= lim || b_span >= lim || (g.M + TBM) * g.ldsa * 4 >= lim ||
         g.sb_group_stride * 4 >= lim)
         return false;
-    w4_launch_out<SA_ROW, SB_BLOCK, 1>(g, out_bf16 ? OUT_BF16 : OUT_F32, st);
+    const int out = out_bf16 ? OUT_BF16 : OUT_F32;
+    if (b_kn) w4_launch_out<SA_ROW, SB_BLOCK, 1, true>(g, out, st);
+    else w4_launch_out<SA_ROW, SB_BLOCK, 1>(g, out, st);
     return true;
 }
 

@@ -139,18 +139,23 @@ def _run_wgrad(at, sat, bt, sbt, off, c=None):
     return c
 
 
-def test_dgrad_small_groups_with_empty_and_ragged():
+# contraction N = 300 (a partial last chunk) takes the eight-wave kernel,
+# N = 384 the four-wave kernel's transposing reads; K = 400 leaves a ragged
+# last column tile either way
+@pytest.mark.parametrize("N", [300, 384])
+def test_dgrad_small_groups_with_empty_and_ragged(N):
     counts = [100, 0, 260, 1, 0, 128]
-    G, N, K = len(counts), 300, 400          # contraction N = 300: a partial last chunk
+    G, K = len(counts), 400
+    NB = -(-N // 128)
     off = _groups(counts)
     M = int(off[-1])
     A = np.zeros((M, N), np.uint8)
-    sa = np.zeros((M, 3), np.float32)
+    sa = np.zeros((M, NB), np.float32)
     for e, cnt in enumerate(counts):
         A[off[e]:off[e] + cnt] = _codes((cnt, N), 110 + e)
-        sa[off[e]:off[e] + cnt] = _scales((cnt, 3), 120 + e)
+        sa[off[e]:off[e] + cnt] = _scales((cnt, NB), 120 + e)
     W = _codes((G, N, K), 130)
-    sw = _scales((G, 3, 4), 131)
+    sw = _scales((G, NB, 4), 131)
     c = host(_run_dgrad(A, sa, off, W, sw))
     co = oracle.grouped_gemm_dgrad(A, sa, off, W, sw)
     _, R = oracle.grouped_gemm_dgrad(A, sa, off, W, sw, f64=True)
