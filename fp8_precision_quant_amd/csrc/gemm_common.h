@@ -60,9 +60,9 @@ __device__ __forceinline__ uint4 mask_bytes(uint4 v, int valid)
 // caller then uses the general kernel).
 // `out` is OUT_F32, OUT_BF16 or OUT_E4M3 (codes in c, scales in cs).
 bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, int out, hipStream_t st);
-// The four-wave kernel (gemm_w4.hip) for dense calls with B stored [N][K]
-// and K a multiple of 128 (fp32, bf16 or E4M3 output); false if it does not
-// cover the call.
+// The four-wave kernel (gemm_w4.hip) for dense calls with K a multiple of
+// 128, B stored [N][K] or read as stored [K][N] (fp32, bf16 or E4M3 output);
+// false if it does not cover the call.
 bool launch_gemm_w4(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, int out, hipStream_t st);
 // The four-wave kernel over groups of rows (MoE forward, B [N][K], and
 // dgrad, B read as stored [K][N]; K % 128 == 0); false if it does not cover

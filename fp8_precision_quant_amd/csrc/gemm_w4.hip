@@ -8,9 +8,8 @@
 // "FP8-RL" article, 一; the weight read as stored for dgrad: "FP8 on-demand
 // transpose weight".)
 //
-// For B stored [N][K] (forward and weight gradient).  The same 128 x 256 x 128
-// tile, LDS layout and direct global -> LDS loads as gemm_nk.hip, with a
-// different division of work:
+// The same 128 x 256 x 128 tile, LDS layout and direct global -> LDS loads
+// as gemm_nk.hip, with a different division of work:
 //  * four waves per workgroup, one per SIMD, each owning all 128 rows of 64
 //    columns for every K chunk, so no partial tiles are exchanged;
 //  * one wave per SIMD may hold 512 registers: the operand fragments of two
@@ -239,13 +238,14 @@ struct W4Scales {
 //   largest group first, so a group's operands share one L2 and the K loops
 //   balance across XCDs.  Empty groups get dW[e] = 0, their tiles stored by
 //   all workgroups before the chunk stream.
-// B_KN: B read as stored [K][N] (the MoE dgrad's expert weights): the load
-// stages 32 K rows x 256 columns per wave and the fragment reads transpose
-// 8-byte quarters (ds_read_b64_tr_b8), twice the reads of [N][K] B.
+// B_KN: B read as stored [K][N] (dgrad: the weight, or the MoE experts'
+// weights, without a transposed copy): the load stages 32 K rows x 256
+// columns per wave and the fragment reads transpose 8-byte quarters
+// (ds_read_b64_tr_b8), twice the reads of [N][K] B.
 template <int SA_MODE, int SB_MODE, int OUT, int GMODE, bool B_KN = false>
 __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4_kernel(GemmArgs p)
 {
-    static_assert(!B_KN || (GMODE == 1 && SB_MODE == SB_BLOCK), "[K][N] B: the grouped dgrad only");
+    static_assert(!B_KN || (GMODE <= 1 && SB_MODE != SB_ROW), "[K][N] B: block or tensor scales, no groups of K");
     static_assert(GMODE != 1 || (SA_MODE == SA_ROW && SB_MODE == SB_BLOCK && OUT != OUT_E4M3),
                   "groups of rows: row-scaled A, block-scaled B, fp32 or bf16 out");
     static_assert(GMODE != 2 || (SA_MODE == SA_ROW && SB_MODE == SB_ROW && OUT == OUT_F32),
@@ -757,19 +757,29 @@ static void w4_launch_out(const GemmArgs& g, int out, hipStream_t st)
             hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_BF16, GMODE, B_KN>), grid, dim3(kW4Threads), 0, st, a);
     } else if (out == OUT_F32) {
         hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_F32, GMODE, B_KN>), grid, dim3(kW4Threads), 0, st, a);
-    } else if constexpr (SB_MODE != SB_ROW && GMODE == 0 && !B_KN) {
-        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_E4M3, GMODE>), grid, dim3(kW4Threads), 0, st, a);
+    } else if constexpr (SB_MODE != SB_ROW && GMODE == 0) {
+        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_E4M3, GMODE, B_KN>), grid, dim3(kW4Threads), 0, st, a);
     }
 }
 
-// [N][K] B only.  B read as stored ([K][N], data gradient) takes twice as
-// many fragment reads (transposing 8-byte ones); with one wave per SIMD
-// issuing every read, load, MFMA and FMA itself, that form measured 4%
-// slower than gemm_nk_kernel, whose two waves per SIMD share the issue work.
+// Every dense call with K a multiple of 128: B stored [N][K] (forward,
+// wgrad) or read as stored [K][N] (dgrad; not with row-scaled B).  Returns
+// false otherwise.
 bool launch_gemm_w4(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, int out, hipStream_t st)
 {
-    if (g.K <= 0 || g.K % 128 != 0 || b_kn) return false;
+    if (g.K <= 0 || g.K % 128 != 0) return false;
     if (out == OUT_E4M3 && sb_mode == SB_ROW) return false;
+    if (b_kn) {
+        if (sb_mode == SB_ROW) return false;
+        if (sa_mode == SA_ROW) {
+            if (sb_mode == SB_BLOCK) w4_launch_out<SA_ROW, SB_BLOCK, 0, true>(g, out, st);
+            else w4_launch_out<SA_ROW, SB_TENSOR, 0, true>(g, out, st);
+        } else {
+            if (sb_mode == SB_BLOCK) w4_launch_out<SA_TENSOR, SB_BLOCK, 0, true>(g, out, st);
+            else w4_launch_out<SA_TENSOR, SB_TENSOR, 0, true>(g, out, st);
+        }
+        return true;
+    }
     if (sa_mode == SA_ROW) {
         if (sb_mode == SB_BLOCK) w4_launch_out<SA_ROW, SB_BLOCK>(g, out, st);
         else if (sb_mode == SB_ROW) w4_launch_out<SA_ROW, SB_ROW>(g, out, st);
