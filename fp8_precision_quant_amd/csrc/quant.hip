@@ -93,9 +93,17 @@ __global__ __launch_bounds__(kBlockThreads) void quant_block_kernel(
         r0 = (int64_t)br * kTile;
         c = (int64_t)(b - br * blocks_per_row.d) * kTile + l * 8;
     };
+    // a block inside the matrix needs no bounds test on any element
+    auto interior = [&](int64_t r0, int64_t c) { return r0 + kTile <= rows && c - l * 8 + kTile <= cols; };
     auto load = [&](uint32_t b, Raw8<T>* R) {
         int64_t r0, c;
         origin(b, r0, c);
+        if (interior(r0, c)) {
+            const T* xb = x + (r0 + g) * ldx + c;
+#pragma unroll
+            for (int u = 0; u < kBlockRows; ++u) raw_load_full(xb + (kBlockThreads / 16) * u * ldx, R[u]);
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < kBlockRows; ++u) {
             const int64_t r = r0 + g + (kBlockThreads / 16) * u;
@@ -105,13 +113,18 @@ __global__ __launch_bounds__(kBlockThreads) void quant_block_kernel(
     auto quantize = [&](uint32_t b, const Raw8<T>* R, int parity) {
         int64_t r0, c;
         origin(b, r0, c);
+        const bool full = interior(r0, c);
+        float v[kBlockRows][8];
+        if (full) {
+#pragma unroll
+            for (int u = 0; u < kBlockRows; ++u) raw_f32_full(R[u], v[u]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kBlockRows; ++u) raw_f32(R[u], c, cols, v[u]);
+        }
         float m = 0.0f;
 #pragma unroll
-        for (int u = 0; u < kBlockRows; ++u) {
-            float v[8];
-            raw_f32(R[u], c, cols, v);
-            m = fmaxf(m, absmax8(v));
-        }
+        for (int u = 0; u < kBlockRows; ++u) m = fmaxf(m, absmax8(v[u]));
         m = dpp_max16(m);
         m = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 0)),
                         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 16))),
@@ -126,14 +139,15 @@ __global__ __launch_bounds__(kBlockThreads) void quant_block_kernel(
 #pragma unroll
         for (int w = 1; w < kBlockThreads / 64; ++w) amax = fmaxf(amax, wave_max[parity][w]);
         const TileScale ts = make_tile_scale<S>(amax);
+        uint8_t* const qb = q + (r0 + g) * ldq + c;
 #pragma unroll
         for (int u = 0; u < kBlockRows; ++u) {
             const int64_t r = r0 + g + (kBlockThreads / 16) * u;
-            float v[8];
-            raw_f32(R[u], c, cols, v);
             uint32_t lo, hi;
-            quant8_as<S>(v, ts, lo, hi);
-            if (r < rows && c < cols)
+            quant8_as<S>(v[u], ts, lo, hi);
+            if (full)
+                *reinterpret_cast<uint2*>(qb + (kBlockThreads / 16) * u * ldq) = make_uint2(lo, hi);
+            else if (r < rows && c < cols)
                 store8(q + r * ldq, c, cols, lo, hi);
         }
         if (threadIdx.x == 0)
