@@ -109,7 +109,8 @@ def test_pow2_chunk_scales_exact(mode):
 
 
 MODES = [("row", "block", "NK"), ("row", "block", "KN"), ("row", "row", "NK"),
-         ("tensor", "tensor", "NK"), ("row", "tensor", "KN"), ("tensor", "block", "NK")]
+         ("tensor", "tensor", "NK"), ("row", "tensor", "KN"), ("tensor", "block", "NK"),
+         ("tensor", "block", "KN"), ("tensor", "tensor", "KN")]
 
 
 @pytest.mark.parametrize("shape", [(1, 1, 1), (300, 200, 300), (256, 256, 512), (64, 1000, 2048),
@@ -127,7 +128,7 @@ def test_random_codes_parity(shape, modes):
 
 
 E4M3_MODES = [("row", "block", "NK"), ("row", "block", "KN"), ("tensor", "tensor", "NK"),
-              ("row", "tensor", "KN"), ("tensor", "block", "NK")]
+              ("row", "tensor", "KN"), ("tensor", "block", "NK"), ("tensor", "tensor", "KN")]
 
 
 @pytest.mark.parametrize("shape", [(300, 200, 300), (256, 384, 512), (17, 700, 4100), (513, 129, 129)])
