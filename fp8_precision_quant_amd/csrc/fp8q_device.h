@@ -20,18 +20,23 @@ constexpr float kE4M3Max = 448.0f;
 // residual; such tiles divide with the IEEE quotient instead.
 constexpr float kFastScaleMin = 0x1p-90f;
 
-__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+// bf16 -> fp32 as a floating-point extension (exact; the compiler then knows
+// the values are canonical and forms |x| maxima without quieting steps)
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return (float)__builtin_bit_cast(__bf16, (uint16_t)(pair & 0xFFFFu)); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return (float)__builtin_bit_cast(__bf16, (uint16_t)(pair >> 16)); }
 
-// |x| max across the 16 lanes of a DPP row (lanes 16r .. 16r+15).  All lanes
-// of the wave must be active.
+// |x| max across the 16 lanes of a DPP row (lanes 16r .. 16r+15), for
+// non-negative v: such floats order like their bit patterns, so the steps
+// are integer maxima (no quieting steps; inputs are finite by contract).
+// All lanes of the wave must be active.
 __device__ __forceinline__ float dpp_max16(float v)
 {
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));  // quad [1,0,3,2]
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));  // quad [2,3,0,1]
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false))); // half-row mirror
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false))); // row mirror
-    return v;
+    uint32_t u = __float_as_uint(v);
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x141, 0xF, 0xF, false));  // half-row mirror
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x140, 0xF, 0xF, false));  // row mirror
+    return __uint_as_float(u);
 }
 
 // Per-tile quantization constants: the scale s, its correctly rounded
@@ -81,6 +86,18 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
     return (uint32_t)w;
 }
 
+// The same for values with |v| <= 448 (1 + 2^-23): their nearest E4M3 value
+// is at most 448, so the conversion needs no clamp.  That holds for every
+// quotient x / s of a tile with s = RN(amax / 448) normal and amax the
+// tile's max |x| (s is within 2^-24 relative of amax / 448), and for x * 2^-e
+// with power-of-two scales.
+__device__ __forceinline__ uint32_t pack4_inrange(float a, float b, float c, float d)
+{
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
 // Quantize four values of one tile.
 __device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, const TileScale& t)
 {
@@ -106,8 +123,8 @@ __device__ __forceinline__ void quant8(const float v[8], const TileScale& t, uin
             const float e = __builtin_fmaf(q0, t.s, -v[i]);
             q[i] = __builtin_fmaf(-e, t.y, q0);
         }
-        lo = pack4_e4m3(q[0], q[1], q[2], q[3]);
-        hi = pack4_e4m3(q[4], q[5], q[6], q[7]);
+        lo = pack4_inrange(q[0], q[1], q[2], q[3]);
+        hi = pack4_inrange(q[4], q[5], q[6], q[7]);
     } else {
         lo = quant4(v[0], v[1], v[2], v[3], t);
         hi = quant4(v[4], v[5], v[6], v[7], t);
@@ -157,8 +174,8 @@ __device__ __forceinline__ void quant8_as(const float v[8], const TileScale& t, 
     if constexpr (sizeof(S) == 4) {
         quant8(v, t, lo, hi);
     } else {
-        lo = pack4_e4m3(v[0] * t.y, v[1] * t.y, v[2] * t.y, v[3] * t.y);
-        hi = pack4_e4m3(v[4] * t.y, v[5] * t.y, v[6] * t.y, v[7] * t.y);
+        lo = pack4_inrange(v[0] * t.y, v[1] * t.y, v[2] * t.y, v[3] * t.y);
+        hi = pack4_inrange(v[4] * t.y, v[5] * t.y, v[6] * t.y, v[7] * t.y);
     }
 }
 

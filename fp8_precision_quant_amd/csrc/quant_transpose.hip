@@ -30,49 +30,92 @@ constexpr int kQtThreads = 512;
 constexpr int kQtGroups = kQtThreads / 16;     // row groups of 16 lanes
 constexpr int kQtRows = kTile / kQtGroups;     // rows per thread
 constexpr int kStagePitch = 128;   // bytes per staged X^T row
-constexpr int kColPitch = 130;     // floats per row group in the column-maxima array
+constexpr int kColPitch = 129;     // words per row group in the column-maxima array
+constexpr int kRecs = kTile + kTile / 16;      // 16-byte scale records (skewed)
 
-// LDS layouts (64 banks of 4 bytes; a wave's 4-byte accesses take one pass
-// when their 64 lanes hit distinct banks or share addresses):
-//  * column maxima: row group g, column c = 8l + j at g * 130 + 8l + (j ^ (l >> 3));
-//    the writes (fixed j: banks 2g + 8l + (j or j ^ 1)) and the per-column
-//    reads (64 consecutive words) are conflict-free;
-//  * column scales: column c at c + 4 (c >> 6).  The column-code pass reads
-//    columns 8l + j (fixed j) for l = 0..15; without the skew l and l + 8
-//    would share a bank;
-//  * staged X^T block: X^T row c at physical row p(c) = c ^ ((c >> 6) & 1),
-//    its 16-byte slot t (X rows 16t..16t+15, in order) at
-//    p(c) * 128 + 16 (t ^ k(c)), k(c) = (c ^ (c >> 3)) & 7.  A code write
-//    (column 8l + j, rows 4g..4g+3 of wave w = g / 4) hits bank
-//    32 ((j & 1) ^ (l >> 3)) + 4 (w ^ j ^ (l & 7)) + g % 4: all 64 distinct.
-//    A 16-byte read pass (16 lanes: two X^T rows, which p keeps in one
-//    pair of physical rows) covers the 64 banks once.
-__device__ __forceinline__ int colmax_idx(int c) { return 8 * (c >> 3) + ((c & 7) ^ ((c >> 6) & 1)); }
-__device__ __forceinline__ int colscale_idx(int c) { return c + 4 * (c >> 6); }
-__device__ __forceinline__ int stage_row(int c) { return c ^ ((c >> 6) & 1); }
+// LDS layouts.  Measured on gfx950: a wave's 4-byte accesses are served in
+// two halves of 32 lanes, each conflict-free when its lanes hit distinct
+// word addresses mod 32 (or share one address); 16-byte reads go in groups
+// of 16 lanes, conflict-free when a group covers 256 contiguous bytes.
+//  * column maxima: row group g, column c at 129 g + rot(c), rot rotating
+//    each aligned run of 32 columns by 2 (c >> 5).  A write (fixed j, c =
+//    8l + j, two row groups per half) hits banks g + 8 (l & 3) + 2 (l >> 2)
+//    + j: 32 distinct; the per-column reads (32 consecutive columns, fixed
+//    g) are a rotation;
+//  * scale records {s, y, mode} of column (or row) c at c + (c >> 4): the
+//    column pass reads columns 8l + j for l = 0..15 (16 distinct records mod
+//    16 slots) and the writers (16 consecutive c) hit 16 consecutive slots;
+//  * staged X^T block: X^T row c at byte 128 c, its 16-byte slot t (X rows
+//    16t..16t+15) at 16 (t ^ k(c)), k(c) = (c ^ (c >> 3)) & 7, and within the
+//    slot the dword of X rows 4g..4g+3 at position (g & 3) ^ (2 (c >> 6)).
+//    A code write (column 8l + j, rows 4g..4g+3 of wave w = g / 4) hits bank
+//    4 (w ^ k(c)) + ((g & 3) ^ 2 (l >> 3)): 32 distinct per half; a 16-byte
+//    read group (two X^T rows, 8 slots each) covers 256 contiguous bytes.
+__device__ __forceinline__ int colmax_idx(int c) { return (c & ~31) | ((c + 2 * (c >> 5)) & 31); }
+__device__ __forceinline__ int rec_idx(int c) { return c + (c >> 4); }
 __device__ __forceinline__ int stage_key(int c) { return (c ^ (c >> 3)) & 7; }
 
-// Four values of one tile -> four codes (the 4-row column units).
-template <typename S>
-__device__ __forceinline__ uint32_t quant4_as(float a, float b, float c, float d, const TileScale& t)
+// Maxima of |x| cross lanes and LDS as fp32 bit patterns: non-negative
+// floats order like their bit patterns, so those maxima are integer maxima
+// (exact; inputs are finite by contract).
+// maxima of four values across the 16 lanes of a DPP row
+template <int CTRL>
+__device__ __forceinline__ void dpp_umax_step(uint32_t (&v)[4])
 {
-    if constexpr (sizeof(S) == 4) {
-        if (__builtin_amdgcn_ballot_w64(t.mode == 2) == 0) {
-            const float v[4] = {a, b, c, d};
-            float q[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float q0 = v[i] * t.y;
-                const float e = __builtin_fmaf(q0, t.s, -v[i]);
-                q[i] = __builtin_fmaf(-e, t.y, q0);
-            }
-            return pack4_e4m3(q[0], q[1], q[2], q[3]);
-        }
-        return quant4(a, b, c, d, t);
+    for (int u = 0; u < 4; ++u) v[u] = max(v[u], (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v[u], CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void dpp_umax16x4(uint32_t (&v)[4])
+{
+    dpp_umax_step<0xB1>(v);    // quad [1,0,3,2]
+    dpp_umax_step<0x4E>(v);    // quad [2,3,0,1]
+    dpp_umax_step<0x141>(v);   // half-row mirror
+    dpp_umax_step<0x140>(v);   // row mirror
+}
+
+// RN_fp32(x / s) for a tile with s >= 2^-90 or s = 0 (see quotient())
+__device__ __forceinline__ float quotient_fast(float x, float s, float y)
+{
+    const float q0 = x * y;
+    const float e = __builtin_fmaf(q0, s, -x);
+    return __builtin_fmaf(-e, y, q0);
+}
+
+// Per-tile constants of the code passes, {s', y', p}: the codes are
+// E4M3(RN(x p / s')) with y' = RN(1 / s').  p = 1 and s' = s except for
+// 0 < s < 2^-90 (IEEE quotient tiles), where p = 2^64 and s' = s 2^64: both
+// scalings are exact and x p / s' = x / s, and s' >= 2^-85 lies in the range
+// where the corrected reciprocal gives the correctly rounded quotient.
+__device__ __forceinline__ float4 pass_record(const TileScale& t)
+{
+    if (t.mode == 2) {
+        const float sp = t.s * 0x1p64f;
+        return make_float4(sp, 1.0f / sp, 0x1p64f, 0.0f);
+    }
+    return make_float4(t.s, t.y, 1.0f, 0.0f);
+}
+
+// Four values of one tile -> four codes.  FAST: every tile of the block has
+// s >= 2^-90 or s = 0 (fp32 scales), or power-of-two scales; then s is
+// normal, RN(amax / 448) is within 2^-24 relative of amax / 448, every
+// quotient is at most 448 (1 + 2^-23) in magnitude and the clamp is not
+// needed.  Otherwise the pre-scaled quotient and the clamp at 448 (a
+// subnormal s can be far below amax / 448).
+template <typename S, bool FAST>
+__device__ __forceinline__ uint32_t quant4_as(float a, float b, float c, float d, const float4& r)
+{
+    if constexpr (sizeof(S) != 4) {
+        return pack4_inrange(a * r.y, b * r.y, c * r.y, d * r.y);
+    } else if constexpr (FAST) {
+        return pack4_inrange(quotient_fast(a, r.x, r.y), quotient_fast(b, r.x, r.y), quotient_fast(c, r.x, r.y),
+                             quotient_fast(d, r.x, r.y));
     } else {
-        return pack4_e4m3(a * t.y, b * t.y, c * t.y, d * t.y);
+        return pack4_e4m3(quotient_fast(a * r.z, r.x, r.y), quotient_fast(b * r.z, r.x, r.y),
+                          quotient_fast(c * r.z, r.x, r.y), quotient_fast(d * r.z, r.x, r.y));
     }
 }
+
+static_assert(kQtRows == 4, "four rows per thread (one 16-byte write of the row maxima)");
 
 template <typename T, typename S>
 __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
@@ -81,12 +124,11 @@ __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
     uint8_t* __restrict__ q_colT, int64_t ldq_colT, S* __restrict__ s_colT, int64_t lds_colT,
     FastDiv blocks_per_row)
 {
-    __shared__ float col_part[kQtGroups * kColPitch];   // per row-group column maxima
-    __shared__ float row_amax[kTile];
-    __shared__ float row_s[kTile], row_y[kTile];
-    __shared__ int row_mode[kTile];
-    __shared__ float col_s[kTile + 4], col_y[kTile + 4];
-    __shared__ int col_mode[kTile + 4];
+    __shared__ uint32_t col_part[kQtGroups * kColPitch];   // per row-group column maxima (|x| bits)
+    __shared__ __attribute__((aligned(16))) uint32_t row_amax[kTile];
+    __shared__ __attribute__((aligned(16))) float4 col_rec[kRecs];
+    __shared__ __attribute__((aligned(16))) float4 row_rec[kRecs];
+    __shared__ __attribute__((aligned(16))) int slow_wave[4];
     __shared__ __attribute__((aligned(16))) uint8_t stage[kTile * kStagePitch];
 
     const int tid = threadIdx.x;
@@ -129,87 +171,102 @@ __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
             }
         }
 
-        // row maxima (DPP over the 16 lanes of each row), column partial maxima
+        // row maxima (DPP over the 16 lanes of each row, the four rows'
+        // steps interleaved), column partial maxima
+        {
+            uint32_t mb[kQtRows];
 #pragma unroll
-        for (int u = 0; u < kQtRows; ++u) {
-            float m = fabsf(v[u][0]);
+            for (int u = 0; u < kQtRows; ++u) {
+                float m = fmaxf(fmaxf(fabsf(v[u][0]), fabsf(v[u][1])), fabsf(v[u][2]));
+                m = fmaxf(fmaxf(m, fabsf(v[u][3])), fabsf(v[u][4]));
+                m = fmaxf(fmaxf(m, fabsf(v[u][5])), fabsf(v[u][6]));
+                mb[u] = __float_as_uint(fmaxf(m, fabsf(v[u][7])));
+            }
+            dpp_umax16x4(mb);
+            if (l == 0) *reinterpret_cast<uint4*>(&row_amax[kQtRows * g]) = make_uint4(mb[0], mb[1], mb[2], mb[3]);
 #pragma unroll
-            for (int j = 1; j < 8; ++j) m = fmaxf(m, fabsf(v[u][j]));
-            m = dpp_max16(m);
-            if (l == 0) row_amax[kQtRows * g + u] = m;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float m = fabsf(v[0][j]);
-#pragma unroll
-            for (int u = 1; u < kQtRows; ++u) m = fmaxf(m, fabsf(v[u][j]));
-            col_part[g * kColPitch + colmax_idx(8 * l + j)] = m;
+            for (int j = 0; j < 8; ++j) {
+                const float cm = fmaxf(fmaxf(fmaxf(fabsf(v[0][j]), fabsf(v[1][j])), fabsf(v[2][j])), fabsf(v[3][j]));
+                col_part[g * kColPitch + colmax_idx(8 * l + j)] = __float_as_uint(cm);
+            }
         }
         __syncthreads();
 
         // one thread per column (tid < 128) and per row (128 <= tid < 256)
-        if (tid < kTile) {
-            const int ci = colmax_idx(tid);
-            float m = col_part[ci];
+        if (tid < 2 * kTile) {
+            TileScale ts;
+            if (tid < kTile) {
+                const int ci = colmax_idx(tid);
+                uint32_t m = col_part[ci];
 #pragma unroll
-            for (int k = 1; k < kQtGroups; ++k) m = fmaxf(m, col_part[k * kColPitch + ci]);
-            TileScale ts = make_tile_scale<S>(m);
-            const int si = colscale_idx(tid);
-            col_s[si] = ts.s;
-            col_y[si] = ts.y;
-            col_mode[si] = ts.mode;
-            if (do_col && (FULL || c0 + tid < cols))
-                s_colT[(c0 + tid) * lds_colT + rb] = stored_scale<S>(ts);
-        } else if (tid < 2 * kTile) {
-            int i = tid - kTile;
-            TileScale ts = make_tile_scale<S>(row_amax[i]);
-            row_s[i] = ts.s;
-            row_y[i] = ts.y;
-            row_mode[i] = ts.mode;
-            if (do_row && (FULL || r0 + i < rows))
-                s_row[(r0 + i) * lds_row + cb] = stored_scale<S>(ts);
+                for (int k = 1; k < kQtGroups; ++k) m = max(m, col_part[k * kColPitch + ci]);
+                ts = make_tile_scale<S>(__uint_as_float(m));
+                col_rec[rec_idx(tid)] = pass_record(ts);
+                if (do_col && (FULL || c0 + tid < cols))
+                    s_colT[(c0 + tid) * lds_colT + rb] = stored_scale<S>(ts);
+            } else {
+                const int i = tid - kTile;
+                ts = make_tile_scale<S>(__uint_as_float(row_amax[i]));
+                row_rec[rec_idx(i)] = pass_record(ts);
+                if (do_row && (FULL || r0 + i < rows))
+                    s_row[(r0 + i) * lds_row + cb] = stored_scale<S>(ts);
+            }
+            // waves 0-3: does any of their tiles need the IEEE quotient
+            const bool any_slow = __builtin_amdgcn_ballot_w64(ts.mode == 2) != 0;
+            if ((tid & 63) == 0) slow_wave[tid >> 6] = any_slow ? 1 : 0;
         }
         __syncthreads();
 
-        if (do_row) {
-            const int64_t c = c0 + 8 * l;
-            uint8_t* const qb = q_row + (r0 + kQtRows * g) * ldq_row + c;
+        auto passes = [&](auto fast_tag) {
+            constexpr bool FAST = decltype(fast_tag)::value;
+            if (do_row) {
+                const int64_t c = c0 + 8 * l;
+                uint8_t* const qb = q_row + (r0 + kQtRows * g) * ldq_row + c;
 #pragma unroll
-            for (int u = 0; u < kQtRows; ++u) {
-                int i = kQtRows * g + u;
-                TileScale ts{row_s[i], row_y[i], row_mode[i]};
-                uint32_t lo, hi;
-                quant8_as<S>(v[u], ts, lo, hi);
-                if constexpr (FULL) {
-                    *reinterpret_cast<uint2*>(qb + u * ldq_row) = make_uint2(lo, hi);
-                } else {
-                    const int64_t r = r0 + i;
-                    if (r < rows && c < cols) store8(q_row + r * ldq_row, c, cols, lo, hi);
+                for (int u = 0; u < kQtRows; ++u) {
+                    const int i = kQtRows * g + u;
+                    const float4 rr = row_rec[rec_idx(i)];
+                    const uint32_t lo = quant4_as<S, FAST>(v[u][0], v[u][1], v[u][2], v[u][3], rr);
+                    const uint32_t hi = quant4_as<S, FAST>(v[u][4], v[u][5], v[u][6], v[u][7], rr);
+                    if constexpr (FULL) {
+                        *reinterpret_cast<uint2*>(qb + u * ldq_row) = make_uint2(lo, hi);
+                    } else {
+                        const int64_t r = r0 + i;
+                        if (r < rows && c < cols) store8(q_row + r * ldq_row, c, cols, lo, hi);
+                    }
                 }
             }
-        }
+
+            if (do_col) {
+                // column j of this thread, rows 4g..4g+3, packed in row order
+                const int pos = 4 * ((g & 3) ^ (2 * (l >> 3)));
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int cj = 8 * l + j;
+                    const float4 cr = col_rec[rec_idx(cj)];
+                    const uint32_t w = quant4_as<S, FAST>(v[0][j], v[1][j], v[2][j], v[3][j], cr);
+                    *reinterpret_cast<uint32_t*>(stage + cj * kStagePitch + 16 * ((g >> 2) ^ stage_key(cj)) + pos) = w;
+                }
+            }
+        };
+        const int4 sw = *reinterpret_cast<const int4*>(slow_wave);
+        if (sizeof(S) != 4 || __builtin_amdgcn_readfirstlane(sw.x | sw.y | sw.z | sw.w) == 0)
+            passes(std::true_type{});
+        else
+            passes(std::false_type{});
 
         if (do_col) {
-            // column j of this thread, rows 4g..4g+3, packed in row order
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int cj = 8 * l + j;
-                const int si = colscale_idx(cj);
-                TileScale ts{col_s[si], col_y[si], col_mode[si]};
-                const uint32_t w = quant4_as<S>(v[0][j], v[1][j], v[2][j], v[3][j], ts);
-                *reinterpret_cast<uint32_t*>(stage + stage_row(cj) * kStagePitch +
-                                             16 * ((g >> 2) ^ stage_key(cj)) + 4 * (g & 3)) = w;
-            }
             __syncthreads();
-            // 8 threads per X^T row (16 bytes each), 64 rows per pass
+            // 8 threads per X^T row (16 bytes each), 64 rows per pass; rows
+            // 64..127 hold their dwords in the order 2, 3, 0, 1
 #pragma unroll
             for (int pass = 0; pass < kTile / (kQtThreads / 8); ++pass) {
-                int cr = pass * (kQtThreads / 8) + (tid >> 3);   // row of the staged X^T block
-                int seg = (tid & 7) * 16;              // byte offset along X's rows
-                int64_t cglob = c0 + cr;
-                int64_t rglob = r0 + seg;
-                const uint4 w = *reinterpret_cast<const uint4*>(stage + stage_row(cr) * kStagePitch +
-                                                                16 * ((tid & 7) ^ stage_key(cr)));
+                const int cr = pass * (kQtThreads / 8) + (tid >> 3);   // row of the staged X^T block
+                const int seg = (tid & 7) * 16;              // byte offset along X's rows
+                const int64_t cglob = c0 + cr;
+                const int64_t rglob = r0 + seg;
+                uint4 w = *reinterpret_cast<const uint4*>(stage + cr * kStagePitch + 16 * ((tid & 7) ^ stage_key(cr)));
+                if (pass == 1) w = make_uint4(w.z, w.w, w.x, w.y);
                 uint8_t* dst = q_colT + cglob * ldq_colT + rglob;
                 if (FULL || (cglob < cols && rglob + 16 <= rows)) {
                     *reinterpret_cast<uint4*>(dst) = w;
