@@ -31,20 +31,27 @@ constexpr int kQtGroups = kQtThreads / 16;     // row groups of 16 lanes
 constexpr int kQtRows = kTile / kQtGroups;     // rows per thread
 constexpr int kStagePitch = 128;   // bytes per staged X^T row
 constexpr int kColPitch = 129;     // words per row group in the column-maxima array
-constexpr int kRecs = kTile + kTile / 16;      // 16-byte scale records (skewed)
 
 // LDS layouts.  Measured on gfx950: a wave's 4-byte accesses are served in
 // two halves of 32 lanes, each conflict-free when its lanes hit distinct
-// word addresses mod 32 (or share one address); 16-byte reads go in groups
-// of 16 lanes, conflict-free when a group covers 256 contiguous bytes.
+// word addresses mod 32 (or share one address); 8-byte reads take two
+// cycles when the lanes read consecutive 8-byte words; 16-byte reads go in
+// groups of 16 lanes, conflict-free when a group covers 256 contiguous
+// bytes.  The compiler's merged form of two 8-byte reads (one instruction,
+// two addresses) measured slower than two plain reads, and took 15 cycles
+// with conflicts on 16-byte records 16 bytes apart, so the scale reads below
+// are kept separate.
 //  * column maxima: row group g, column c at 129 g + rot(c), rot rotating
 //    each aligned run of 32 columns by 2 (c >> 5).  A write (fixed j, c =
 //    8l + j, two row groups per half) hits banks g + 8 (l & 3) + 2 (l >> 2)
 //    + j: 32 distinct; the per-column reads (32 consecutive columns, fixed
 //    g) are a rotation;
-//  * scale records {s, y, mode} of column (or row) c at c + (c >> 4): the
-//    column pass reads columns 8l + j for l = 0..15 (16 distinct records mod
-//    16 slots) and the writers (16 consecutive c) hit 16 consecutive slots;
+//  * scale pairs {s', y'} (8 bytes; 8-byte accesses: 32 lanes per cycle,
+//    conflict-free on distinct 8-byte slots mod 32) of column c at
+//    c ^ ((c >> 5) & 3): the column pass reads columns 8l + j (fixed j) for
+//    l = 0..15, slots 8 (l & 3) + (j ^ (l >> 2)), 16 distinct; the writers
+//    (32 consecutive columns) a permutation of 32 slots.  Row pairs in row
+//    order (a half-wave reads two rows);
 //  * staged X^T block: X^T row c at byte 128 c, its 16-byte slot t (X rows
 //    16t..16t+15) at 16 (t ^ k(c)), k(c) = (c ^ (c >> 3)) & 7, and within the
 //    slot the dword of X rows 4g..4g+3 at position (g & 3) ^ (2 (c >> 6)).
@@ -52,7 +59,7 @@ constexpr int kRecs = kTile + kTile / 16;      // 16-byte scale records (skewed)
 //    4 (w ^ k(c)) + ((g & 3) ^ 2 (l >> 3)): 32 distinct per half; a 16-byte
 //    read group (two X^T rows, 8 slots each) covers 256 contiguous bytes.
 __device__ __forceinline__ int colmax_idx(int c) { return (c & ~31) | ((c + 2 * (c >> 5)) & 31); }
-__device__ __forceinline__ int rec_idx(int c) { return c + (c >> 4); }
+__device__ __forceinline__ int csy_idx(int c) { return c ^ ((c >> 5) & 3); }
 __device__ __forceinline__ int stage_key(int c) { return (c ^ (c >> 3)) & 7; }
 
 // Maxima of |x| cross lanes and LDS as fp32 bit patterns: non-negative
@@ -95,6 +102,11 @@ __device__ __forceinline__ float4 pass_record(const TileScale& t)
     return make_float4(t.s, t.y, 1.0f, 0.0f);
 }
 
+typedef float f2 __attribute__((ext_vector_type(2)));
+// one 8-byte LDS read, not merged with its neighbours into a two-address read
+typedef const volatile __attribute__((address_space(3))) f2 lds_f2;
+__device__ __forceinline__ f2 lds_pair(const f2* p) { return *(lds_f2*)p; }
+
 // Four values of one tile -> four codes.  FAST: every tile of the block has
 // s >= 2^-90 or s = 0 (fp32 scales), or power-of-two scales; then s is
 // normal, RN(amax / 448) is within 2^-24 relative of amax / 448, every
@@ -102,16 +114,16 @@ __device__ __forceinline__ float4 pass_record(const TileScale& t)
 // needed.  Otherwise the pre-scaled quotient and the clamp at 448 (a
 // subnormal s can be far below amax / 448).
 template <typename S, bool FAST>
-__device__ __forceinline__ uint32_t quant4_as(float a, float b, float c, float d, const float4& r)
+__device__ __forceinline__ uint32_t quant4_as(float a, float b, float c, float d, f2 sy, float pre)
 {
     if constexpr (sizeof(S) != 4) {
-        return pack4_inrange(a * r.y, b * r.y, c * r.y, d * r.y);
+        return pack4_inrange(a * sy.y, b * sy.y, c * sy.y, d * sy.y);
     } else if constexpr (FAST) {
-        return pack4_inrange(quotient_fast(a, r.x, r.y), quotient_fast(b, r.x, r.y), quotient_fast(c, r.x, r.y),
-                             quotient_fast(d, r.x, r.y));
+        return pack4_inrange(quotient_fast(a, sy.x, sy.y), quotient_fast(b, sy.x, sy.y), quotient_fast(c, sy.x, sy.y),
+                             quotient_fast(d, sy.x, sy.y));
     } else {
-        return pack4_e4m3(quotient_fast(a * r.z, r.x, r.y), quotient_fast(b * r.z, r.x, r.y),
-                          quotient_fast(c * r.z, r.x, r.y), quotient_fast(d * r.z, r.x, r.y));
+        return pack4_e4m3(quotient_fast(a * pre, sy.x, sy.y), quotient_fast(b * pre, sy.x, sy.y),
+                          quotient_fast(c * pre, sy.x, sy.y), quotient_fast(d * pre, sy.x, sy.y));
     }
 }
 
@@ -126,8 +138,9 @@ __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
 {
     __shared__ uint32_t col_part[kQtGroups * kColPitch];   // per row-group column maxima (|x| bits)
     __shared__ __attribute__((aligned(16))) uint32_t row_amax[kTile];
-    __shared__ __attribute__((aligned(16))) float4 col_rec[kRecs];
-    __shared__ __attribute__((aligned(16))) float4 row_rec[kRecs];
+    __shared__ f2 col_sy[kTile];
+    __shared__ f2 row_sy[kTile];
+    __shared__ float col_pre[kTile], row_pre[kTile];
     __shared__ __attribute__((aligned(16))) int slow_wave[4];
     __shared__ __attribute__((aligned(16))) uint8_t stage[kTile * kStagePitch];
 
@@ -201,13 +214,17 @@ __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
 #pragma unroll
                 for (int k = 1; k < kQtGroups; ++k) m = max(m, col_part[k * kColPitch + ci]);
                 ts = make_tile_scale<S>(__uint_as_float(m));
-                col_rec[rec_idx(tid)] = pass_record(ts);
+                const float4 pr = pass_record(ts);
+                col_sy[csy_idx(tid)] = f2{pr.x, pr.y};
+                col_pre[tid] = pr.z;
                 if (do_col && (FULL || c0 + tid < cols))
                     s_colT[(c0 + tid) * lds_colT + rb] = stored_scale<S>(ts);
             } else {
                 const int i = tid - kTile;
                 ts = make_tile_scale<S>(__uint_as_float(row_amax[i]));
-                row_rec[rec_idx(i)] = pass_record(ts);
+                const float4 pr = pass_record(ts);
+                row_sy[i] = f2{pr.x, pr.y};
+                row_pre[i] = pr.z;
                 if (do_row && (FULL || r0 + i < rows))
                     s_row[(r0 + i) * lds_row + cb] = stored_scale<S>(ts);
             }
@@ -225,9 +242,10 @@ __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
 #pragma unroll
                 for (int u = 0; u < kQtRows; ++u) {
                     const int i = kQtRows * g + u;
-                    const float4 rr = row_rec[rec_idx(i)];
-                    const uint32_t lo = quant4_as<S, FAST>(v[u][0], v[u][1], v[u][2], v[u][3], rr);
-                    const uint32_t hi = quant4_as<S, FAST>(v[u][4], v[u][5], v[u][6], v[u][7], rr);
+                    const f2 sy = lds_pair(&row_sy[i]);
+                    const float pre = FAST ? 1.0f : row_pre[i];
+                    const uint32_t lo = quant4_as<S, FAST>(v[u][0], v[u][1], v[u][2], v[u][3], sy, pre);
+                    const uint32_t hi = quant4_as<S, FAST>(v[u][4], v[u][5], v[u][6], v[u][7], sy, pre);
                     if constexpr (FULL) {
                         *reinterpret_cast<uint2*>(qb + u * ldq_row) = make_uint2(lo, hi);
                     } else {
@@ -243,8 +261,9 @@ __global__ __launch_bounds__(kQtThreads) void quant_transpose_kernel(
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int cj = 8 * l + j;
-                    const float4 cr = col_rec[rec_idx(cj)];
-                    const uint32_t w = quant4_as<S, FAST>(v[0][j], v[1][j], v[2][j], v[3][j], cr);
+                    const f2 sy = lds_pair(&col_sy[csy_idx(cj)]);
+                    const float pre = FAST ? 1.0f : col_pre[cj];
+                    const uint32_t w = quant4_as<S, FAST>(v[0][j], v[1][j], v[2][j], v[3][j], sy, pre);
                     *reinterpret_cast<uint32_t*>(stage + cj * kStagePitch + 16 * ((g >> 2) ^ stage_key(cj)) + pos) = w;
                 }
             }
