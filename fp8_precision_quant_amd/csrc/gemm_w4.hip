@@ -633,6 +633,83 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
             }
             return;
         }
+        if constexpr (OUT == OUT_BF16) {
+            if (cn0 + 64 * wq + 64 <= N) {
+                // 16-byte stores: for each pair of 16-column blocks (2p, 2p+1)
+                // the four lanes of a row (kgrp 0..3, four columns of each
+                // block) exchange halves in two swaps, lane ^ 32 then lane ^ 16,
+                // after which lane kgrp holds columns 32p + 8 kgrp .. + 7: half
+                // the store instructions of one 8-byte store per block
+                const bool lo = kgrp < 2;
+                const bool give_x = ((kgrp ^ (kgrp >> 1)) & 1) != 0;
+                const bool got_first = (kgrp & 1) != 0;
+#pragma unroll
+                for (int i = 0; i < PMI; ++i) {
+                    const int64_t m = cm0 + 16 * i + lrow;
+#pragma unroll
+                    for (int pq = 0; pq < NNI / 2; ++pq) {
+                        const v4f A = acc[i][2 * pq], B = acc[i][2 * pq + 1];
+                        const uint32_t a0 = bf16_rne(A[0]) | (bf16_rne(A[1]) << 16);
+                        const uint32_t a1 = bf16_rne(A[2]) | (bf16_rne(A[3]) << 16);
+                        const uint32_t b0 = bf16_rne(B[0]) | (bf16_rne(B[1]) << 16);
+                        const uint32_t b1 = bf16_rne(B[2]) | (bf16_rne(B[3]) << 16);
+                        // swap 1 (lane ^ 32): kgrp 0, 1 keep block 2p and take
+                        // its columns 4 kgrp + 8 from kgrp + 2; kgrp 2, 3 keep
+                        // block 2p + 1 and take its columns 4 kgrp - 8
+                        const uint32_t x0 = lo ? a0 : b0, x1 = lo ? a1 : b1;
+                        const uint32_t y0 = (uint32_t)__shfl_xor((int)(lo ? b0 : a0), 32);
+                        const uint32_t y1 = (uint32_t)__shfl_xor((int)(lo ? b1 : a1), 32);
+                        // swap 2 (lane ^ 16): each lane keeps the four columns
+                        // of its target and takes the other four
+                        const uint32_t k0 = give_x ? y0 : x0, k1 = give_x ? y1 : x1;
+                        const uint32_t t0 = (uint32_t)__shfl_xor((int)(give_x ? x0 : y0), 16);
+                        const uint32_t t1 = (uint32_t)__shfl_xor((int)(give_x ? x1 : y1), 16);
+                        if (m >= m_end) continue;
+                        const uint4 w = got_first ? make_uint4(t0, t1, k0, k1) : make_uint4(k0, k1, t0, t1);
+                        const int64_t n = cn0 + 64 * wq + 32 * pq + 8 * kgrp;
+                        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(cbase) + m * p.ldc + n) = w;
+                    }
+                }
+                return;
+            }
+        }
+        if constexpr (OUT == OUT_F32) {
+            if (cn0 + 64 * wq + 64 <= N) {
+                // whole 128-byte lines per store instruction: for each pair
+                // of 16-column blocks (2p, 2p+1) lanes l and l ^ 8 (rows r and
+                // r ^ 8) swap one block (DPP rotate by 8 within each row of
+                // 16 lanes); the first store then covers rows 0-7 of the pair's
+                // 32 columns, the second rows 8-15
+                const bool top = lrow < 8;
+#pragma unroll
+                for (int i = 0; i < PMI; ++i) {
+#pragma unroll
+                    for (int pq = 0; pq < NNI / 2; ++pq) {
+                        const v4f A = acc[i][2 * pq], B = acc[i][2 * pq + 1];
+                        v4f R;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            R[r] = __int_as_float(__builtin_amdgcn_update_dpp(
+                                0, __float_as_int(top ? B[r] : A[r]), 0x128, 0xF, 0xF, false));
+                        // store 1: rows 16i .. 16i+7; store 2: rows 16i+8 .. 16i+15
+                        const int64_t m1 = cm0 + 16 * i + (lrow & 7), m2 = m1 + 8;
+                        // top lanes store block 2p, the others block 2p + 1
+                        const int64_t n = cn0 + 64 * wq + 32 * pq + 4 * kgrp + (top ? 0 : 16);
+                        const v4f w1 = top ? A : R, w2 = top ? R : B;
+                        float* const c0 = reinterpret_cast<float*>(cbase);
+                        if (m1 < m_end) {
+                            if constexpr (GMODE == 2) __builtin_nontemporal_store(w1, reinterpret_cast<v4f*>(c0 + m1 * p.ldc + n));
+                            else *reinterpret_cast<v4f*>(c0 + m1 * p.ldc + n) = w1;
+                        }
+                        if (m2 < m_end) {
+                            if constexpr (GMODE == 2) __builtin_nontemporal_store(w2, reinterpret_cast<v4f*>(c0 + m2 * p.ldc + n));
+                            else *reinterpret_cast<v4f*>(c0 + m2 * p.ldc + n) = w2;
+                        }
+                    }
+                }
+                return;
+            }
+        }
 #pragma unroll
         for (int i = 0; i < PMI; ++i) {
             const int64_t m = cm0 + 16 * i + lrow;
