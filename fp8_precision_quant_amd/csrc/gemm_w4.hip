@@ -615,8 +615,29 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
                     quant8(v, ts, code[2 * jp], code[2 * jp + 1]);
                 }
                 const int64_t m = cm0 + 16 * i + lrow;
-                if (m >= m_end) continue;
                 uint8_t* qrow = reinterpret_cast<uint8_t*>(cbase) + m * p.ldc;
+                if (cn0 + 64 * wq + 64 <= N) {
+                    // one 16-byte store per lane: the four lanes of a row
+                    // (kgrp L holds the codes of columns 16j + 4L .. + 3,
+                    // j = 0..3) transpose their 4 x 4 dwords in two swaps
+                    // (lane ^ 32, then lane ^ 16), after which lane L holds
+                    // columns 16L .. 16L + 15
+                    const int L = kgrp, h = L >> 1, e = L & 1;
+                    // swap 1: keep the blocks 2h, 2h + 1, send the other two
+                    const uint32_t own0 = h ? code[2] : code[0], own1 = h ? code[3] : code[1];
+                    const uint32_t r0 = (uint32_t)__shfl_xor((int)(h ? code[0] : code[2]), 32);
+                    const uint32_t r1 = (uint32_t)__shfl_xor((int)(h ? code[1] : code[3]), 32);
+                    // swap 2: keep block L (sources L and L ^ 2), send block L ^ 1
+                    const uint32_t own_keep = e ? own1 : own0, r_keep = e ? r1 : r0;
+                    const uint32_t recv_own = (uint32_t)__shfl_xor((int)(e ? own0 : own1), 16);
+                    const uint32_t recv_r = (uint32_t)__shfl_xor((int)(e ? r0 : r1), 16);
+                    // dword s of the lane's 16 bytes comes from lane s: V[s ^ L]
+                    const uint32_t v0 = e ? recv_own : own_keep, v1 = e ? own_keep : recv_own;
+                    const uint32_t v2 = e ? recv_r : r_keep, v3 = e ? r_keep : recv_r;
+                    if (m < m_end)
+                        *reinterpret_cast<uint4*>(qrow + cn0 + 64 * wq + 16 * L) =
+                            h ? make_uint4(v2, v3, v0, v1) : make_uint4(v0, v1, v2, v3);
+                } else if (m < m_end) {
 #pragma unroll
                 for (int j = 0; j < NNI; ++j) {
                     const int64_t n = ncol0 + 16 * j;
@@ -628,8 +649,9 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
                             if (n + r < N) qrow[n + r] = (uint8_t)(code[j] >> (8 * r));
                     }
                 }
+                }
                 const int64_t n_tile = cn0 + 64 * wq;
-                if (kgrp == 0 && (wq & 1) == 0 && n_tile < N) p.cs[m * p.ldcs + n_tile / 128] = ts.s;
+                if (m < m_end && kgrp == 0 && (wq & 1) == 0 && n_tile < N) p.cs[m * p.ldcs + n_tile / 128] = ts.s;
             }
             return;
         }
