@@ -64,6 +64,8 @@ bool launch_gemm_nk(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, int 
 // 128, B stored [N][K] or read as stored [K][N] (fp32, bf16 or E4M3 output);
 // false if it does not cover the call.
 bool launch_gemm_w4(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, int out, hipStream_t st);
+// ... and with power-of-two scales (E8M0 bytes, as launch_gemm_nk_e8m0).
+bool launch_gemm_w4_e8m0(const GemmArgs& g, int sb_mode, bool b_kn, bool out_bf16, hipStream_t st);
 // The four-wave kernel over groups of rows (MoE forward, B [N][K], and
 // dgrad, B read as stored [K][N]; K % 128 == 0); false if it does not cover
 // the call.

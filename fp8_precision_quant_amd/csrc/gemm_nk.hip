@@ -739,6 +739,7 @@ bool launch_gemm_nk_e8m0(const GemmArgs& g, int sb_mode, bool b_kn, bool out_bf1
 {
     if (!dense_fits(g, SA_ROW, sb_mode, b_kn, 1)) return false;
     if (b_kn && sb_mode != SB_BLOCK) return false;
+    if (launch_gemm_w4_e8m0(g, sb_mode, b_kn, out_bf16, st)) return true;
     if (b_kn) {
         if (out_bf16) launch_out<SA_ROW, SB_BLOCK, true, OUT_BF16, 0, true>(g, st);
         else launch_out<SA_ROW, SB_BLOCK, true, OUT_F32, 0, true>(g, st);

@@ -167,6 +167,28 @@ __device__ __forceinline__ void w4_mfma(v4f& d)
 #undef W4_MF_A
 }
 
+// the same with power-of-two scales applied by the matrix core (E8M0 bytes
+// in bits 0-7 of sb for the B rows, of sa for the A rows), accumulating in d
+template <int FB, int FA>
+__device__ __forceinline__ void w4_mfma_scaled(v4f& d, int sb, int sa)
+{
+#define W4_MS_A(BFULL, FAI, AFULL) \
+    if constexpr (FA == FAI) asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, " BFULL ", " AFULL ", %0, %1, %2" : "+v"(d) : "v"(sb), "v"(sa) : "memory");
+#define W4_MS_B(FBI, BFULL) \
+    if constexpr (FB == FBI) { W4_A_LIST(W4_MS_A, BFULL) }
+    W4_B_LIST(W4_MS_B)
+#undef W4_MS_B
+#undef W4_MS_A
+}
+
+template <int OFF>
+__device__ __forceinline__ int w4_ds8(uint32_t addr)
+{
+    int v;
+    asm volatile("ds_read_u8 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+    return v;
+}
+
 __device__ __forceinline__ void w4_fmac(float& acc, float p, float s)
 {
     asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(acc) : "v"(p), "v"(s) : "memory");
@@ -222,6 +244,8 @@ struct W4Scales {
     float sb;                                 // SB of the wave's 128-column block
     v4f sc[SB_MODE == SB_ROW ? NNI : 1];      // SB of the lane's 4 columns in 16-column block j
     float comb[PMI];                          // SA * SB (uniform B scale)
+    int e[PMI];                               // power-of-two scales: E8M0 byte of the lane's A row in block i
+    int eb[SB_MODE == SB_ROW ? NNI : 1];      // ... of its B row (column of block j, or the wave's block)
 };
 
 }  // namespace
@@ -242,9 +266,16 @@ struct W4Scales {
 // weights, without a transposed copy): the load stages 32 K rows x 256
 // columns per wave and the fragment reads transpose 8-byte quarters
 // (ds_read_b64_tr_b8), twice the reads of [N][K] B.
-template <int SA_MODE, int SB_MODE, int OUT, int GMODE, bool B_KN = false>
+// P2: power-of-two scales as E8M0 bytes (p.sa / p.sb point at bytes; the
+// micro-scaling form of block scaling), applied by the scaled MFMA, which
+// accumulates straight into the tile: no chunk partials, no scale FMAs.
+// Each chunk loads the 4-byte word of a scale row that holds its byte (the
+// grids' row strides are multiples of 4) and the reads select the byte.
+template <int SA_MODE, int SB_MODE, int OUT, int GMODE, bool B_KN = false, bool P2 = false>
 __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_w4_kernel(GemmArgs p)
 {
+    static_assert(!P2 || (GMODE == 0 && SA_MODE == SA_ROW && SB_MODE != SB_TENSOR && OUT != OUT_E4M3),
+                  "power-of-two scales: dense, row-scaled A, row- or block-scaled B, fp32 or bf16 out");
     static_assert(!B_KN || (GMODE <= 1 && SB_MODE != SB_ROW), "[K][N] B: block or tensor scales, no groups of K");
     static_assert(GMODE != 1 || (SA_MODE == SA_ROW && SB_MODE == SB_BLOCK && OUT != OUT_E4M3),
                   "groups of rows: row-scaled A, block-scaled B, fp32 or bf16 out");
@@ -379,11 +410,16 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     const __amdgpu_buffer_rsrc_t ra = rsrc(p.a, (M - 1) * p.lda + K);
     const int64_t b_ext = B_KN ? (K - 1) * p.ldb + ((N + 15) & ~(int64_t)15) : (N - 1) * p.ldb + K;
     __amdgpu_buffer_rsrc_t rb = rsrc(p.b, b_ext);
-    const __amdgpu_buffer_rsrc_t rsa = rsrc(p.sa, SA_MODE == SA_ROW ? ((M - 1) * p.ldsa + KB) * 4 : 4);
+    // (E8M0 grids: byte extents, each row's last word included)
+    const int64_t kb_words = (KB + 3) & ~3, nb_words = (nblocks + 3) & ~3;
+    const __amdgpu_buffer_rsrc_t rsa =
+        rsrc(p.sa, SA_MODE != SA_ROW ? 4 : P2 ? (M - 1) * p.ldsa + kb_words : ((M - 1) * p.ldsa + KB) * 4);
     __amdgpu_buffer_rsrc_t rsb =
-        rsrc(p.sb, SB_MODE == SB_ROW     ? ((N - 1) * p.ldsb + KB) * 4
-                   : SB_MODE == SB_BLOCK ? (B_KN ? ((int64_t)(KB - 1) * p.ldsb + nblocks) * 4
-                                                 : ((nblocks - 1) * p.ldsb + KB) * 4)
+        rsrc(p.sb, SB_MODE == SB_ROW     ? (P2 ? (N - 1) * p.ldsb + kb_words : ((N - 1) * p.ldsb + KB) * 4)
+                   : SB_MODE == SB_BLOCK ? (P2 ? (B_KN ? (int64_t)(KB - 1) * p.ldsb + nb_words
+                                                       : (nblocks - 1) * p.ldsb + kb_words)
+                                               : B_KN ? ((int64_t)(KB - 1) * p.ldsb + nblocks) * 4
+                                                      : ((nblocks - 1) * p.ldsb + KB) * 4)
                                          : 4);
     const float sa_t = SA_MODE == SA_TENSOR ? p.sa[0] : 0.0f;
     const float sb_t = SB_MODE == SB_TENSOR ? p.sb[0] : 0.0f;
@@ -415,9 +451,13 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
             vb0 = (uint32_t)(brow * p.ldb) + 16u * (uint32_t)((l & 7) ^ (l >> 3));
             vb1 = (uint32_t)(brow * p.ldb) + 16u * (uint32_t)((l & 7) ^ (l >> 3) ^ 1);
         }
-        if (SA_MODE == SA_ROW) vsa = (uint32_t)((lm0 + 32 * wq + l) * p.ldsa * 4);
-        if (SB_MODE == SB_ROW) vsb = (uint32_t)((ln0 + 64 * wq + l) * p.ldsb * 4);
-        if (SB_MODE == SB_BLOCK) vsb = (uint32_t)((ln0 / 128 + (wq >> 1)) * (B_KN ? 4 : p.ldsb * 4));
+        constexpr int se = P2 ? 1 : 4;   // bytes per scale
+        if (SA_MODE == SA_ROW) vsa = (uint32_t)((lm0 + 32 * wq + l) * p.ldsa * se);
+        if (SB_MODE == SB_ROW) vsb = (uint32_t)((ln0 + 64 * wq + l) * p.ldsb * se);
+        if (SB_MODE == SB_BLOCK) {
+            const int64_t nb = ln0 / 128 + (wq >> 1);
+            vsb = P2 ? (uint32_t)(B_KN ? (nb & ~(int64_t)3) : nb * p.ldsb) : (uint32_t)(nb * (B_KN ? 4 : p.ldsb * 4));
+        }
         if (GMODE == 1) {
             // the expert of the load cursor's tile: its B and block scales
             rb = rsrc(p.b + (int64_t)lt.e * p.b_group_stride, b_ext);
@@ -441,11 +481,14 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
                 dma16_at(rb, lds_addr(&Stg[st][kAStage]) + (uint32_t)((64 * wq + 8 * t) * TBK), (t & 1) ? vb1 : vb0,
                          kg * TBK + 8u * t * (uint32_t)p.ldb);
         } else if constexpr (SA_MODE == SA_ROW && d == 12) {
-            if (lane < 32) dma4(rsa, &SAs[st][32 * wq], vsa, kg * 4);
+            // (E8M0: the word of the row that holds the chunk's byte)
+            if (lane < 32) dma4(rsa, &SAs[st][32 * wq], vsa, P2 ? (kg & ~3u) : kg * 4);
         } else {
-            if constexpr (SB_MODE == SB_ROW) dma4(rsb, &SBs[st][64 * wq], vsb, kg * 4);
+            if constexpr (SB_MODE == SB_ROW) dma4(rsb, &SBs[st][64 * wq], vsb, P2 ? (kg & ~3u) : kg * 4);
             if constexpr (SB_MODE == SB_BLOCK) {
-                if (lane == 0) dma4(rsb, &SBs[st][wq], vsb, B_KN ? kg * (uint32_t)p.ldsb * 4 : kg * 4);
+                if (lane == 0)
+                    dma4(rsb, &SBs[st][wq], vsb,
+                         B_KN ? kg * (uint32_t)p.ldsb * (P2 ? 1u : 4u) : (P2 ? (kg & ~3u) : kg * 4));
             }
         }
     };
@@ -480,6 +523,25 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         for (int j = 0; j < NNI; ++j) kn_rel[j] = rel ^ (uint32_t)(j << 4);
     }
     const uint32_t sa_rel = lds_addr(&SAs[0][0]) + (uint32_t)lrow * 4;
+    // E8M0 B row scales: the lane's B row 64 wq + 16 j + lrow
+    const uint32_t sbp_rel = lds_addr(&SBs[0][0]) + (uint32_t)(64 * wq + lrow) * 4;
+    // E8M0: the read cursor (chunk being read into registers) and the byte
+    // of the staged scale words that belongs to it: byte kb & 3 of a row's
+    // word; for [K][N] B's block scales byte (n0 / 128 + wave block) & 3
+    int rd_k = 0, rd_ord = 0;
+    int64_t rd_n0 = P2 ? tile_at(0).n0 : 0;
+    uint32_t rsel = 0, bsel = 0;
+    auto read_cursor_set = [&]() __attribute__((always_inline)) {
+        rsel = (uint32_t)(rd_k & 3);
+        bsel = B_KN ? (uint32_t)((rd_n0 / 128 + (wq >> 1)) & 3) : rsel;
+    };
+    auto read_advance = [&]() __attribute__((always_inline)) {
+        if (++rd_k == p.KB) {
+            rd_k = 0;
+            if (++rd_ord < my_tiles) rd_n0 = tile_at(rd_ord).n0;
+        }
+        read_cursor_set();
+    };
     const uint32_t sb_rel = SB_MODE == SB_ROW ? lds_addr(&SBs[0][0]) + (uint32_t)(64 * wq + 4 * kgrp) * 4
                                               : lds_addr(&SBs[0][0]) + (uint32_t)wq * 4;
 
@@ -506,10 +568,17 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
             }
         } else {
             constexpr int i = k - 24;
+            if constexpr (P2) {
+                scl[NS].e[i] = w4_ds8<i * 64>(sa_rel + (uint32_t)(st * TBM * 4) + rsel);
+                if constexpr (SB_MODE == SB_BLOCK && i == 0) scl[NS].eb[0] = w4_ds8<0>(sb_rel + (uint32_t)(st * 16) + bsel);
+                if constexpr (SB_MODE == SB_ROW && i < NNI)
+                    scl[NS].eb[i] = w4_ds8<i * 64>(sbp_rel + (uint32_t)(st * TBN * 4) + rsel);
+            } else {
             if constexpr (SA_MODE == SA_ROW) scl[NS].sa[i] = w4_ds32<i * 64>(sa_rel + (uint32_t)(st * TBM * 4));
             if constexpr (SB_MODE == SB_BLOCK && i == 0) scl[NS].sb = w4_ds32<0>(sb_rel + (uint32_t)(st * 16));
             if constexpr (SB_MODE == SB_ROW && (i & 1) == 0)
                 scl[NS].sc[i / 2] = w4_ds128<(i / 2) * 64>(sb_rel + (uint32_t)(st * TBN * 4));
+            }
         }
     };
     // the closing wait of a chunk's reads; it names the scale registers so
@@ -517,6 +586,15 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     auto reads_done = [&](auto nst) __attribute__((always_inline)) {
         constexpr int NS = decltype(nst)::value;
         W4Scales<SB_MODE>& s = scl[NS];
+        if constexpr (P2) {
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(s.e[0]), "+v"(s.e[1]), "+v"(s.e[2]), "+v"(s.e[3]), "+v"(s.e[4]),
+                           "+v"(s.e[5]), "+v"(s.e[6]), "+v"(s.e[7]), "+v"(s.eb[0])
+                         :
+                         : "memory");
+            if constexpr (SB_MODE == SB_ROW) asm volatile("" : "+v"(s.eb[1]), "+v"(s.eb[2]), "+v"(s.eb[3]));
+            return;
+        }
         asm volatile("s_waitcnt lgkmcnt(0)"
                      : "+v"(s.sa[0]), "+v"(s.sa[1]), "+v"(s.sa[2]), "+v"(s.sa[3]), "+v"(s.sa[4]),
                        "+v"(s.sa[5]), "+v"(s.sa[6]), "+v"(s.sa[7]), "+v"(s.sb)
@@ -536,7 +614,12 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
-        for (int i = 0; i < PMI; ++i) scl[s].sa[i] = scl[s].comb[i] = 0.0f;
+        for (int i = 0; i < PMI; ++i) {
+            scl[s].sa[i] = scl[s].comb[i] = 0.0f;
+            scl[s].e[i] = 0;
+        }
+#pragma unroll
+        for (int j = 0; j < (SB_MODE == SB_ROW ? NNI : 1); ++j) scl[s].eb[j] = 0;
         scl[s].sb = 0.0f;
 #pragma unroll
         for (int j = 0; j < (SB_MODE == SB_ROW ? NNI : 1); ++j) scl[s].sc[j] = zero;
@@ -776,8 +859,10 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     }
     w4_wait_vm<2 * ND>();
     __builtin_amdgcn_s_barrier();
+    if constexpr (P2) read_cursor_set();
     w4_for<0, 32>([&](auto kt) __attribute__((always_inline)) { read_item(kt, std::integral_constant<int, 0>{}, 0); });
     reads_done(std::integral_constant<int, 0>{});
+    if constexpr (P2) read_advance();
 
     // ---- the chunk stream ----
     int ck = 0;
@@ -789,7 +874,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         // wave's have, and every wave is done reading chunk g's stage
         w4_wait_vm<ND>();
         __builtin_amdgcn_s_barrier();
-        if constexpr (SB_MODE != SB_ROW) {
+        if constexpr (!P2 && SB_MODE != SB_ROW) {
             const float sbv = SB_MODE == SB_BLOCK ? scl[S].sb : SB_MODE == SB_TENSOR ? sb_t : 1.0f;
 #pragma unroll
             for (int i = 0; i < PMI; ++i) scl[S].comb[i] = (SA_MODE == SA_ROW ? scl[S].sa[i] : sa_t) * sbv;
@@ -800,18 +885,36 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         const int st_r = st_w == 2 ? 0 : st_w + 1;
         w4_for<0, 32>([&](auto ut) __attribute__((always_inline)) {
             constexpr int u = decltype(ut)::value;
-            w4_mfma<12 * S + 8 + u / PMI, 12 * S + u % PMI>(P[u & 3]);
+            if constexpr (P2)
+                w4_mfma_scaled<12 * S + 8 + u / PMI, 12 * S + u % PMI>(
+                    acc[u % PMI][u / PMI], scl[S].eb[SB_MODE == SB_ROW ? u / PMI : 0], scl[S].e[u % PMI]);
+            else
+                w4_mfma<12 * S + 8 + u / PMI, 12 * S + u % PMI>(P[u & 3]);
             read_item(ut, std::integral_constant<int, NS>{}, st_r);
             if constexpr (u >= 4 && (u - 4) % 2 == 0 && (u - 4) / 2 < ND)
                 load_item(std::integral_constant<int, (u - 4) / 2>{}, st_w);
             // blocks 29..31 of the previous chunk (zero partials after a
             // tile's last chunk, whose blocks were scaled before its output)
-            if constexpr (u >= 3) block_fma(std::integral_constant<int, u - 3>{}, std::integral_constant<int, S>{});
-            else block_fma(std::integral_constant<int, 29 + u>{}, std::integral_constant<int, NS>{});
+            if constexpr (!P2) {
+                if constexpr (u >= 3) block_fma(std::integral_constant<int, u - 3>{}, std::integral_constant<int, S>{});
+                else block_fma(std::integral_constant<int, 29 + u>{}, std::integral_constant<int, NS>{});
+            }
         });
         load_advance();
         reads_done(std::integral_constant<int, NS>{});
-        if (ck == ct.kbn - 1) {
+        if constexpr (P2) read_advance();
+        if (ck == ct.kbn - 1 && P2) {
+            // the output reads accumulators the last MFMAs wrote (an 8-pass
+            // MFMA result needs 11 wait states before a vector read)
+            asm volatile("s_nop 7\n s_nop 7" ::: "memory");
+            store_tile();
+#pragma unroll
+            for (int i = 0; i < PMI; ++i)
+#pragma unroll
+                for (int j = 0; j < NNI; ++j) acc[i][j] = zero;
+            if (++c_ord < my_tiles) ct = tile_at(c_ord);
+            ck = 0;
+        } else if (ck == ct.kbn - 1) {
             // last chunk of the tile: blocks 29..31 (their MFMAs are more
             // than 12 instructions back after this padding), then the output
             asm volatile("s_nop 7" ::: "memory");
@@ -842,7 +945,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     w4_wait_vm<0>();
 }
 
-template <int SA_MODE, int SB_MODE, int GMODE = 0, bool B_KN = false>
+template <int SA_MODE, int SB_MODE, int GMODE = 0, bool B_KN = false, bool P2 = false>
 static void w4_launch_out(const GemmArgs& g, int out, hipStream_t st)
 {
     GemmArgs a = g;
@@ -853,10 +956,10 @@ static void w4_launch_out(const GemmArgs& g, int out, hipStream_t st)
     dim3 grid((uint32_t)(tiles < g.num_cus ? tiles : g.num_cus));
     if (out == OUT_BF16) {
         if constexpr (GMODE != 2)
-            hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_BF16, GMODE, B_KN>), grid, dim3(kW4Threads), 0, st, a);
+            hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_BF16, GMODE, B_KN, P2>), grid, dim3(kW4Threads), 0, st, a);
     } else if (out == OUT_F32) {
-        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_F32, GMODE, B_KN>), grid, dim3(kW4Threads), 0, st, a);
-    } else if constexpr (SB_MODE != SB_ROW && GMODE == 0) {
+        hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_F32, GMODE, B_KN, P2>), grid, dim3(kW4Threads), 0, st, a);
+    } else if constexpr (SB_MODE != SB_ROW && GMODE == 0 && !P2) {
         hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_E4M3, GMODE, B_KN>), grid, dim3(kW4Threads), 0, st, a);
     }
 }
@@ -888,6 +991,20 @@ bool launch_gemm_w4(const GemmArgs& g, int sa_mode, int sb_mode, bool b_kn, int 
         else if (sb_mode == SB_ROW) w4_launch_out<SA_TENSOR, SB_ROW>(g, out, st);
         else w4_launch_out<SA_TENSOR, SB_TENSOR>(g, out, st);
     }
+    return true;
+}
+
+// Dense calls with power-of-two scales (E8M0 bytes; row-scaled A, block-
+// scaled B [N][K] or [K][N], or row-scaled [N][K] B) and K a multiple of
+// 128; false otherwise.
+bool launch_gemm_w4_e8m0(const GemmArgs& g, int sb_mode, bool b_kn, bool out_bf16, hipStream_t st)
+{
+    if (g.K <= 0 || g.K % 128 != 0) return false;
+    if (b_kn && sb_mode != SB_BLOCK) return false;
+    const int out = out_bf16 ? OUT_BF16 : OUT_F32;
+    if (b_kn) w4_launch_out<SA_ROW, SB_BLOCK, 0, true, true>(g, out, st);
+    else if (sb_mode == SB_BLOCK) w4_launch_out<SA_ROW, SB_BLOCK, 0, false, true>(g, out, st);
+    else w4_launch_out<SA_ROW, SB_ROW, 0, false, true>(g, out, st);
     return true;
 }
 
