@@ -1,8 +1,13 @@
-// Block-scaled FP8 GEMM on gfx950: the forward y = x W^T (B = W stored
-// [N][K]), dgrad dx = dy W (B = W read as stored, [K][N], no transposed copy:
-// Ling 2.0 FP8 blog, "FP8 on-demand transpose weight"), the weight gradient
-// dW = dy^T x on transposed re-quantized operands (row-scaled B), per-tensor
-// scaling, and the grouped (MoE) forward.
+// Block-scaled FP8 GEMM on gfx950, eight-wave form.  The four-wave kernel
+// (gemm_w4.hip) runs every dense and grouped call whose K (the contraction
+// axis) is a multiple of 128, with fp32 or power-of-two scales; this kernel
+// takes the calls with a ragged last chunk (K % 128 != 0), whose fragment
+// bytes at or past K it zeroes in registers (a code past K may be anything):
+// the forward y = x W^T (B = W stored [N][K]), dgrad dx = dy W (B = W read as
+// stored, [K][N], no transposed copy: Ling 2.0 FP8 blog, "FP8 on-demand
+// transpose weight"), the weight gradient dW = dy^T x on transposed
+// re-quantized operands (row-scaled B), per-tensor scaling, E8M0 scales, and
+// the grouped (MoE) forward and dgrad.
 //
 //   C[m][n] = sum_kb SA(m,kb) * SB(n,kb) * sum_{k in chunk kb} dec(A[m][k]) * dec(B[n][k])
 //
