@@ -131,7 +131,8 @@ E4M3_MODES = [("row", "block", "NK"), ("row", "block", "KN"), ("tensor", "tensor
               ("row", "tensor", "KN"), ("tensor", "block", "NK"), ("tensor", "tensor", "KN")]
 
 
-@pytest.mark.parametrize("shape", [(300, 200, 300), (256, 384, 512), (17, 700, 4100), (513, 129, 129)])
+@pytest.mark.parametrize("shape", [(300, 200, 300), (256, 384, 512), (17, 700, 4100), (513, 129, 129),
+                                   (200, 512, 256), (64, 1000, 2048)])
 @pytest.mark.parametrize("modes", E4M3_MODES)
 def test_e4m3_output_quantizes_the_fp32_result(shape, modes):
     # the stored codes and 1x128 scales are (1) byte for byte the GPU
