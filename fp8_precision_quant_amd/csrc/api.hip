@@ -52,10 +52,10 @@ int check_device()
 
 // A pending launch error; with FP8Q_CHECK=1 the stream is also synchronized
 // so that an error of the work itself is reported by the call that enqueued it.
-int launch_status(void* stream)
+int launch_status(hipStream_t stream)
 {
     if (hipGetLastError() != hipSuccess) return FP8Q_ERR_LAUNCH;
-    if (fp8q::debug_checks_enabled() && hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) {
+    if (fp8q::debug_checks_enabled() && hipStreamSynchronize(stream) != hipSuccess) {
         (void)hipGetLastError();
         return FP8Q_ERR_LAUNCH;
     }
@@ -63,10 +63,10 @@ int launch_status(void* stream)
 }
 
 // FP8Q_CHECK=1: the group offsets are checked on the device first.
-int offsets_status(const int32_t* offsets, int64_t G, int64_t M_pad, void* stream)
+int offsets_status(const int32_t* offsets, int64_t G, int64_t M_pad, hipStream_t stream)
 {
     if (!fp8q::debug_checks_enabled()) return FP8Q_OK;
-    return fp8q::check_group_offsets(offsets, G, M_pad, static_cast<hipStream_t>(stream));
+    return fp8q::check_group_offsets(offsets, G, M_pad, stream);
 }
 
 }  // namespace
@@ -88,7 +88,7 @@ const char* fp8q_status_string(int status)
 }
 
 int fp8_quant_blockwise(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
-                        int kind, uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream)
+                        int kind, uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t stream)
 {
     if (!dtype_ok(x_dtype)) return FP8Q_ERR_UNSUPPORTED;
     if (kind != FP8Q_ROW_1x128 && kind != FP8Q_BLOCK_128x128 && kind != FP8Q_TENSOR)
@@ -108,14 +108,14 @@ int fp8_quant_blockwise(const void* x, int x_dtype, int64_t rows, int64_t cols, 
     int st = check_device();
     if (st != FP8Q_OK) return st;
     fp8q::launch_quant_blockwise(x, x_dtype, rows, cols, ldx, kind, q, ldq, s, lds,
-                                 static_cast<hipStream_t>(stream));
+                                 stream);
     return launch_status(stream);
 }
 
 int fp8_quant_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
                         uint8_t* q_row, int64_t ldq_row, float* s_row, int64_t lds_row,
                         uint8_t* q_colT, int64_t ldq_colT, float* s_colT, int64_t lds_colT,
-                        void* stream)
+                        hipStream_t stream)
 {
     if (!dtype_ok(x_dtype)) return FP8Q_ERR_UNSUPPORTED;
     if (rows < 0 || cols < 0) return FP8Q_ERR_SHAPE;
@@ -137,12 +137,12 @@ int fp8_quant_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols, 
     if (st != FP8Q_OK) return st;
     fp8q::launch_quant_transpose(x, x_dtype, rows, cols, ldx, want_row ? q_row : nullptr, ldq_row,
                                  s_row, lds_row, want_col ? q_colT : nullptr, ldq_colT, s_colT,
-                                 lds_colT, static_cast<hipStream_t>(stream));
+                                 lds_colT, stream);
     return launch_status(stream);
 }
 
 int fp8_quant_blockwise_e8m0(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
-                             int kind, uint8_t* q, int64_t ldq, uint8_t* e, int64_t lde, void* stream)
+                             int kind, uint8_t* q, int64_t ldq, uint8_t* e, int64_t lde, hipStream_t stream)
 {
     if (!dtype_ok(x_dtype)) return FP8Q_ERR_UNSUPPORTED;
     if (kind != FP8Q_ROW_1x128 && kind != FP8Q_BLOCK_128x128) return FP8Q_ERR_UNSUPPORTED;
@@ -158,14 +158,14 @@ int fp8_quant_blockwise_e8m0(const void* x, int x_dtype, int64_t rows, int64_t c
     int st = check_device();
     if (st != FP8Q_OK) return st;
     fp8q::launch_quant_blockwise_e8m0(x, x_dtype, rows, cols, ldx, kind, q, ldq, e, lde,
-                                      static_cast<hipStream_t>(stream));
+                                      stream);
     return launch_status(stream);
 }
 
 int fp8_quant_transpose_e8m0(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
                              uint8_t* q_row, int64_t ldq_row, uint8_t* e_row, int64_t lde_row,
                              uint8_t* q_colT, int64_t ldq_colT, uint8_t* e_colT, int64_t lde_colT,
-                             void* stream)
+                             hipStream_t stream)
 {
     if (!dtype_ok(x_dtype)) return FP8Q_ERR_UNSUPPORTED;
     if (rows < 0 || cols < 0) return FP8Q_ERR_SHAPE;
@@ -187,7 +187,7 @@ int fp8_quant_transpose_e8m0(const void* x, int x_dtype, int64_t rows, int64_t c
     if (st != FP8Q_OK) return st;
     fp8q::launch_quant_transpose_e8m0(x, x_dtype, rows, cols, ldx, want_row ? q_row : nullptr, ldq_row,
                                       e_row, lde_row, want_col ? q_colT : nullptr, ldq_colT, e_colT,
-                                      lde_colT, static_cast<hipStream_t>(stream));
+                                      lde_colT, stream);
     return launch_status(stream);
 }
 
@@ -195,7 +195,7 @@ int fp8_gemm_e8m0(int64_t M, int64_t N, int64_t K,
                   const uint8_t* a, int64_t lda, const uint8_t* ea, int64_t ldea,
                   const uint8_t* b, int64_t ldb, int b_layout,
                   const uint8_t* eb, int64_t ldeb, int eb_kind,
-                  void* c, int64_t ldc, int c_dtype, void* stream)
+                  void* c, int64_t ldc, int c_dtype, hipStream_t stream)
 {
     if (!dtype_ok(c_dtype)) return FP8Q_ERR_UNSUPPORTED;
     if (b_layout != FP8Q_B_NK && b_layout != FP8Q_B_KN) return FP8Q_ERR_UNSUPPORTED;
@@ -222,14 +222,14 @@ int fp8_gemm_e8m0(int64_t M, int64_t N, int64_t K,
     int st = check_device();
     if (st != FP8Q_OK) return st;
     if (!fp8q::launch_gemm_e8m0(M, N, K, a, lda, ea, ldea, b, ldb, b_layout, eb, ldeb, eb_kind, c, ldc,
-                                c_dtype, static_cast<hipStream_t>(stream)))
+                                c_dtype, stream))
         return FP8Q_ERR_UNSUPPORTED;
     return launch_status(stream);
 }
 
 int fp8_adam_step(int64_t n, float* p, const void* g, int g_dtype, uint8_t* mq, float* ms,
                   uint8_t* vq, float* vs, double lr, double beta1, double beta2, double eps,
-                  double weight_decay, int64_t step, void* stream)
+                  double weight_decay, int64_t step, hipStream_t stream)
 {
     if (!dtype_ok(g_dtype)) return FP8Q_ERR_UNSUPPORTED;
     if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0) || step < 1 ||
@@ -254,7 +254,7 @@ int fp8_adam_step(int64_t n, float* p, const void* g, int g_dtype, uint8_t* mq, 
     a.step_size = (float)(lr / (1.0 - std::pow(beta1, (double)step)));
     a.bc2_sqrt = (float)std::sqrt(1.0 - std::pow(beta2, (double)step));
     a.eps = (float)eps;
-    fp8q::launch_adam_fp8(n, p, g, g_dtype, mq, ms, vq, vs, a, static_cast<hipStream_t>(stream));
+    fp8q::launch_adam_fp8(n, p, g, g_dtype, mq, ms, vq, vs, a, stream);
     return launch_status(stream);
 }
 
@@ -293,7 +293,7 @@ int fp8_gemm_blockscaled_e4m3(int64_t M, int64_t N, int64_t K,
                               const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, int sa_kind,
                               const uint8_t* b, int64_t ldb, int b_layout,
                               const float* sb, int64_t ldsb, int sb_kind,
-                              uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream)
+                              uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t stream)
 {
     bool empty;
     int st = gemm_operands_status(M, N, K, a, lda, sa, ldsa, sa_kind, b, ldb, b_layout, sb, ldsb,
@@ -306,7 +306,7 @@ int fp8_gemm_blockscaled_e4m3(int64_t M, int64_t N, int64_t K,
     st = check_device();
     if (st != FP8Q_OK) return st;
     if (!fp8q::launch_gemm_e4m3(M, N, K, a, lda, sa, ldsa, sa_kind, b, ldb, b_layout, sb, ldsb, sb_kind,
-                                q, ldq, s, lds, static_cast<hipStream_t>(stream)))
+                                q, ldq, s, lds, stream))
         return FP8Q_ERR_UNSUPPORTED;
     return launch_status(stream);
 }
@@ -315,7 +315,7 @@ int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K,
                          const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, int sa_kind,
                          const uint8_t* b, int64_t ldb, int b_layout,
                          const float* sb, int64_t ldsb, int sb_kind,
-                         void* c, int64_t ldc, int c_dtype, void* stream)
+                         void* c, int64_t ldc, int c_dtype, hipStream_t stream)
 {
     if (!dtype_ok(c_dtype)) return FP8Q_ERR_UNSUPPORTED;
     if (b_layout != FP8Q_B_NK && b_layout != FP8Q_B_KN) return FP8Q_ERR_UNSUPPORTED;
@@ -341,7 +341,7 @@ int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K,
     int st = check_device();
     if (st != FP8Q_OK) return st;
     if (!fp8q::launch_gemm(M, N, K, a, lda, sa, ldsa, sa_kind, b, ldb, b_layout, sb, ldsb, sb_kind, c,
-                           ldc, c_dtype, static_cast<hipStream_t>(stream)))
+                           ldc, c_dtype, stream))
         return FP8Q_ERR_UNSUPPORTED;
     return launch_status(stream);
 }
@@ -350,7 +350,7 @@ int fp8_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K,
                      const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
                      const int32_t* group_offsets,
                      const uint8_t* b, const float* sb,
-                     void* c, int64_t ldc, int c_dtype, void* stream)
+                     void* c, int64_t ldc, int c_dtype, hipStream_t stream)
 {
     if (!dtype_ok(c_dtype)) return FP8Q_ERR_UNSUPPORTED;
     if (G < 1 || M_pad < 0 || N < 0 || K < 0 || M_pad % kTile) return FP8Q_ERR_SHAPE;
@@ -369,7 +369,7 @@ int fp8_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K,
     st = offsets_status(group_offsets, G, M_pad, stream);
     if (st != FP8Q_OK) return st;
     if (!fp8q::launch_grouped_gemm(G, M_pad, N, K, a, lda, sa, ldsa, group_offsets, b, sb, c, ldc,
-                                   c_dtype, static_cast<hipStream_t>(stream)))
+                                   c_dtype, stream))
         return FP8Q_ERR_UNSUPPORTED;
     return launch_status(stream);
 }
@@ -378,7 +378,7 @@ int fp8_grouped_gemm_dgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K,
                            const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
                            const int32_t* group_offsets,
                            const uint8_t* w, const float* sw,
-                           void* c, int64_t ldc, int c_dtype, void* stream)
+                           void* c, int64_t ldc, int c_dtype, hipStream_t stream)
 {
     if (!dtype_ok(c_dtype)) return FP8Q_ERR_UNSUPPORTED;
     if (G < 1 || M_pad < 0 || N < 0 || K < 0 || M_pad % kTile) return FP8Q_ERR_SHAPE;
@@ -396,7 +396,7 @@ int fp8_grouped_gemm_dgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K,
     st = offsets_status(group_offsets, G, M_pad, stream);
     if (st != FP8Q_OK) return st;
     if (!fp8q::launch_grouped_gemm_dgrad(G, M_pad, N, K, a, lda, sa, ldsa, group_offsets, w, sw, c, ldc,
-                                         c_dtype, static_cast<hipStream_t>(stream)))
+                                         c_dtype, stream))
         return FP8Q_ERR_UNSUPPORTED;
     return launch_status(stream);
 }
@@ -405,7 +405,7 @@ int fp8_grouped_gemm_wgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K,
                            const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
                            const uint8_t* b, int64_t ldb, const float* sb, int64_t ldsb,
                            const int32_t* group_offsets,
-                           float* c, int64_t ldc, void* stream)
+                           float* c, int64_t ldc, hipStream_t stream)
 {
     if (G < 1 || M_pad < 0 || N < 0 || K < 0 || M_pad % kTile) return FP8Q_ERR_SHAPE;
     if (G > kMaxGroups) return FP8Q_ERR_UNSUPPORTED;
@@ -423,7 +423,7 @@ int fp8_grouped_gemm_wgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K,
     st = offsets_status(group_offsets, G, M_pad, stream);
     if (st != FP8Q_OK) return st;
     if (!fp8q::launch_grouped_gemm_wgrad(G, M_pad, N, K, a, lda, sa, ldsa, b, ldb, sb, ldsb, group_offsets,
-                                         c, ldc, static_cast<hipStream_t>(stream)))
+                                         c, ldc, stream))
         return FP8Q_ERR_UNSUPPORTED;
     return launch_status(stream);
 }

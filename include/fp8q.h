@@ -76,6 +76,15 @@
 extern "C" {
 #endif
 
+/* A HIP stream (NULL: the default stream); the same type as the HIP
+ * runtime's hipStream_t, declared here so that this header needs no HIP
+ * header.  Data types, scale kinds and B layouts are passed as int, with the
+ * values of the enums below: a value outside an enum's list, which a C or
+ * foreign-function caller can pass, then reaches the validation as a defined
+ * int and is rejected (FP8Q_ERR_UNSUPPORTED); as an enum-typed parameter it
+ * would be undefined behaviour in the C++ implementation. */
+typedef struct ihipStream_t* hipStream_t;
+
 typedef enum {
     FP8Q_OK = 0,
     FP8Q_ERR_NULL = 1,        /* a required pointer is NULL */
@@ -114,7 +123,7 @@ typedef enum {
  */
 int fp8_quant_blockwise(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
                         int kind, uint8_t* q, int64_t ldq, float* s, int64_t lds,
-                        void* stream);
+                        hipStream_t stream);
 
 /*
  * fp8_quant_transpose -- one read of X[rows][cols] produces both
@@ -130,7 +139,7 @@ int fp8_quant_blockwise(const void* x, int x_dtype, int64_t rows, int64_t cols, 
 int fp8_quant_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
                         uint8_t* q_row, int64_t ldq_row, float* s_row, int64_t lds_row,
                         uint8_t* q_colT, int64_t ldq_colT, float* s_colT, int64_t lds_colT,
-                        void* stream);
+                        hipStream_t stream);
 
 /*
  * fp8_gemm_blockscaled -- C[M][N] = block-scaled FP8 product (see Numerics).
@@ -160,7 +169,7 @@ int fp8_gemm_blockscaled(int64_t M, int64_t N, int64_t K,
                          const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, int sa_kind,
                          const uint8_t* b, int64_t ldb, int b_layout,
                          const float* sb, int64_t ldsb, int sb_kind,
-                         void* c, int64_t ldc, int c_dtype, void* stream);
+                         void* c, int64_t ldc, int c_dtype, hipStream_t stream);
 
 /*
  * fp8_gemm_blockscaled_e4m3 -- the same product, stored quantized: the
@@ -184,7 +193,7 @@ int fp8_gemm_blockscaled_e4m3(int64_t M, int64_t N, int64_t K,
                               const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, int sa_kind,
                               const uint8_t* b, int64_t ldb, int b_layout,
                               const float* sb, int64_t ldsb, int sb_kind,
-                              uint8_t* q, int64_t ldq, float* s, int64_t lds, void* stream);
+                              uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t stream);
 
 /*
  * fp8_grouped_gemm -- MoE expert GEMM over padded groups.
@@ -210,7 +219,7 @@ int fp8_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K,
                      const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
                      const int32_t* group_offsets,
                      const uint8_t* b, const float* sb,
-                     void* c, int64_t ldc, int c_dtype, void* stream);
+                     void* c, int64_t ldc, int c_dtype, hipStream_t stream);
 
 /*
  * fp8_grouped_gemm_dgrad -- MoE expert dgrad over padded groups (Ling 2.0
@@ -236,7 +245,7 @@ int fp8_grouped_gemm_dgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K,
                            const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
                            const int32_t* group_offsets,
                            const uint8_t* w, const float* sw,
-                           void* c, int64_t ldc, int c_dtype, void* stream);
+                           void* c, int64_t ldc, int c_dtype, hipStream_t stream);
 
 /*
  * fp8_grouped_gemm_wgrad -- MoE expert weight gradient over padded groups
@@ -263,7 +272,7 @@ int fp8_grouped_gemm_wgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K,
                            const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
                            const uint8_t* b, int64_t ldb, const float* sb, int64_t ldsb,
                            const int32_t* group_offsets,
-                           float* c, int64_t ldc, void* stream);
+                           float* c, int64_t ldc, hipStream_t stream);
 
 /*
  * Power-of-two (E8M0) scales -- the micro-scaling variant of block scaling.
@@ -293,7 +302,7 @@ int fp8_grouped_gemm_wgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K,
  */
 int fp8_quant_blockwise_e8m0(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
                              int kind, uint8_t* q, int64_t ldq, uint8_t* e, int64_t lde,
-                             void* stream);
+                             hipStream_t stream);
 
 /*
  * fp8_quant_transpose_e8m0 -- fp8_quant_transpose with power-of-two scales:
@@ -304,7 +313,7 @@ int fp8_quant_blockwise_e8m0(const void* x, int x_dtype, int64_t rows, int64_t c
 int fp8_quant_transpose_e8m0(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t ldx,
                              uint8_t* q_row, int64_t ldq_row, uint8_t* e_row, int64_t lde_row,
                              uint8_t* q_colT, int64_t ldq_colT, uint8_t* e_colT, int64_t lde_colT,
-                             void* stream);
+                             hipStream_t stream);
 
 /*
  * fp8_gemm_e8m0 -- the block-scaled product (see Numerics) with SA, SB the
@@ -327,7 +336,7 @@ int fp8_gemm_e8m0(int64_t M, int64_t N, int64_t K,
                   const uint8_t* a, int64_t lda, const uint8_t* ea, int64_t ldea,
                   const uint8_t* b, int64_t ldb, int b_layout,
                   const uint8_t* eb, int64_t ldeb, int eb_kind,
-                  void* c, int64_t ldc, int c_dtype, void* stream);
+                  void* c, int64_t ldc, int c_dtype, hipStream_t stream);
 
 /*
  * fp8_adam_step -- one AdamW step with both moments held in FP8.
@@ -362,7 +371,7 @@ int fp8_gemm_e8m0(int64_t M, int64_t N, int64_t K,
  */
 int fp8_adam_step(int64_t n, float* p, const void* g, int g_dtype, uint8_t* mq, float* ms,
                   uint8_t* vq, float* vs, double lr, double beta1, double beta2, double eps,
-                  double weight_decay, int64_t step, void* stream);
+                  double weight_decay, int64_t step, hipStream_t stream);
 
 /* Human-readable name of a status code (static string). */
 const char* fp8q_status_string(int status);
