@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 
     // Persistent workgroups dealt to the 8 XCDs round-robin; XCD x owns a
     // contiguous range of tile ids, walked by its workgroups in lockstep in
-    // groups of kGroupM M-tiles (neighbouring workgroups share A and B panels
+    // groups of kGM M-tiles (neighbouring workgroups share A and B panels
     // in that XCD's L2).
     const int T = p.tiles_m * p.tiles_n;
     const int xcd = blockIdx.x & 7;
@@ -313,7 +313,10 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     const int nwg = (gridDim.x >> 3) + (xcd < (int)(gridDim.x & 7) ? 1 : 0);
     const int range_start = xcd * (T >> 3) + min(xcd, T & 7);
     int tiles_here = (T >> 3) + (xcd < (T & 7) ? 1 : 0);
-    const int span = kGroupM * p.tiles_n;
+    // (row-scaled B, the weight gradient: groups of 8 M-tiles measured 2%
+    // faster than 16; the other layouts keep 16)
+    constexpr int kGM = (GMODE == 0 && SB_MODE == SB_ROW) ? 8 : kGroupM;
+    const int span = kGM * p.tiles_n;
     const int64_t M = p.M, N = p.N, K = p.K;
     if constexpr (GMODE == 2) {
         int gn = 0;   // non-empty groups
@@ -392,8 +395,8 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         } else {
             const int pid = range_start + local + ordinal * nwg;
             const int group = pid / span;
-            const int first_m = group * kGroupM;
-            const int gsz = min(p.tiles_m - first_m, kGroupM);
+            const int first_m = group * kGM;
+            const int gsz = min(p.tiles_m - first_m, kGM);
             const int idx = pid - group * span;
             t.m0 = (int64_t)(first_m + idx % gsz) * TBM;
             t.n0 = (int64_t)(idx / gsz) * TBN;
