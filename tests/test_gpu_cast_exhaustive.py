@@ -4,10 +4,12 @@ The rule is code = E4M3(RN_fp32(x / s)) with s = amax / 448 (FP8-LM review,
 section 三, tensor scaling; E4M3 range +-448: "FP8-RL" article, section 一).
 The kernels do not divide per element: for s >= 2^-90 they form the quotient
 from the tile's correctly rounded reciprocal with one FMA correction
-(Markstein), below that they use the IEEE quotient, and they cast with a
-clamp to +-448 followed by the hardware's packed fp32 -> fp8 conversion.
-Those two steps are checked here bit for bit against the oracle, which
-divides and encodes by the definition:
+(Markstein), below that the IEEE quotient (or, in the quantize + transpose
+kernel, the corrected reciprocal of s 2^64 applied to x 2^64), and they cast
+with the hardware's packed fp32 -> fp8 conversion, clamping to +-448 first
+only where a quotient can exceed 448 (1 + 2^-23), i.e. where some tile of
+reach has a subnormal scale.  Those steps are checked here bit for bit
+against the oracle, which divides and encodes by the definition:
 
 (a) scale sweep: tiles whose one fixed element +-A sets amax (so s = A / 448),
     filled with every finite bf16 value x with A 2^-21 <= |x| <= A (every x
@@ -22,6 +24,10 @@ divides and encodes by the definition:
     fp32 bit pattern of magnitude <= 448 (2.28e9 values), so the clamp and
     the conversion are compared with the oracle's encoder on every value
     they can receive from a tile.
+
+(c) quotients above 448: amax values A whose own quotient RN(A / RN(A/448))
+    is 448 + 2^-15 (RN(A/448) rounded down; about one amax in twelve), which
+    the unclamped cast must still map to the largest finite code.
 
 Each data set goes through every kernel that quantizes with fp32 scales: the
 1x128 row kernel, the 128x128 block kernel and the per-tensor kernels where
@@ -221,3 +227,47 @@ def test_unit_scale_every_fp32_value_up_to_448():
         assert so.view(np.uint32)[0, 0] == np.float32(1.0).view(np.uint32)
         n_chunks += 1
     assert n_chunks == 136
+
+
+def _over_448(amaxes: np.ndarray) -> np.ndarray:
+    """The amax values whose quotient RN(A / RN(A / 448)) exceeds 448."""
+    A = amaxes.astype(np.float32)
+    return A[(A / (A / np.float32(448.0))) > np.float32(448.0)]
+
+
+def test_quotient_above_448_casts_to_largest_code():
+    """(c): every bf16 amax with a normal scale whose own quotient rounds to
+    448 + 2^-15, and 4096 such fp32 amax values, each in a tile with its bf16
+    window, through the row, quantize + transpose (both paths) and 128x128
+    kernels; the amax element's code is 0x7E (0xFE for -A)."""
+    lo = np.float32(448.0 * 2.0 ** -126)
+    bf = _over_448(_POS_F32[_POS_F32 >= lo])
+    assert bf.size > 2000
+    g = synthetic.rng(73)
+    bits = g.integers(int(lo.view(np.uint32)), 0x7F000000, size=65536, dtype=np.uint64).astype(np.uint32)
+    f32 = _over_448(bits.view(np.float32))[:4096]
+    assert f32.size == 4096
+    assert np.all(f32 / (f32 / np.float32(448.0)) == np.float32(448.0 + 2.0 ** -15))
+    for amaxes, bf16 in ((bf, True), (f32, False)):
+        frees = [_bf16_window(A * np.float32(0.5), A) for A in amaxes]
+        x = _tiles(amaxes, frees)
+        _check_rows(x, bf16=bf16)
+        qo, _ = oracle.quant_1x128(x)
+        first = np.concatenate([[0], np.cumsum([max(1, -(-F.size // 127)) for F in frees])[:-1]])
+        assert np.all(qo[first, 0] == 0x7E)
+    # 128x128 blocks: amax A at a seeded position of a block of its window
+    blocks = []
+    for i, A in enumerate(bf[:512]):
+        F = _bf16_window(A * np.float32(0.5), A)
+        blk = np.zeros(128 * 128, np.float32)
+        n = min(F.size, blk.size - 1)
+        blk[:n] = F[:n]
+        blk[-1] = A if i % 2 else -A
+        blocks.append(g.permutation(blk).reshape(128, 128))
+    x = np.concatenate(blocks)
+    qo, so = oracle.quant_128x128(x)
+    q, s = fq.fp8_quant_blockwise(_dev(x, True), fq.BLOCK_128x128)
+    torch.cuda.synchronize()
+    _same("block kernel codes", host(q), qo)
+    _same("block kernel scales", host(s), so)
+    assert not np.any((qo & 0x7F) == 0x7F)    # no NaN code
