@@ -636,7 +636,9 @@ def moe_grouped(fq, synthetic, dev, stream, reps=10):
     """Grouped MoE GEMMs on the seeded MoE workload of the parity tests:
     8192 tokens, hidden 2048, 128 experts of intermediate 768, top-8 Zipf(1.1)
     routing, groups padded to 128 rows.  For each expert layer the forward
-    (bf16 out), the backward's dgrad (expert weight read as stored, bf16 out)
+    (bf16 out), the forward stored quantized (E4M3 codes + 1x128 scales, set
+    against the bf16 forward plus a separate 1x128 quantization of its
+    output), the backward's dgrad (expert weight read as stored, bf16 out)
     and wgrad (per-expert token ranges, transposed re-quantized operands,
     fp32 out).  TFLOP/s count the real (unpadded) rows only; `frac_attainable`
     is max(t_MFMA, t_HBM) / time, with t_MFMA the real FLOPs at the FP8 peak
@@ -669,16 +671,20 @@ def moe_grouped(fq, synthetic, dev, stream, reps=10):
         c = torch.empty((M_pad, Nn), dtype=torch.bfloat16, device=dev)
         dx = torch.empty((M_pad, Kk), dtype=torch.bfloat16, device=dev)
         dw = torch.empty((G, Nn, Kk), dtype=torch.float32, device=dev)
+        qc = torch.empty((M_pad, Nn), dtype=torch.uint8, device=dev)
+        sc = torch.empty((M_pad, -(-Nn // 128)), dtype=torch.float32, device=dev)
         flops = 2.0 * real * Nn * Kk
         kb, nb = -(-Kk // 128), -(-Nn // 128)
         wbytes = G * Nn * Kk + G * nb * kb * 4
         nbytes = {
             "fwd": M_pad * Kk + M_pad * kb * 4 + wbytes + M_pad * Nn * 2,
+            "fwd_e4m3": M_pad * Kk + M_pad * kb * 4 + wbytes + M_pad * Nn + M_pad * nb * 4,
             "dgrad": M_pad * Nn + M_pad * nb * 4 + wbytes + M_pad * Kk * 2,
             "wgrad": (Nn + Kk) * M_pad + (Nn + Kk) * (M_pad // 128) * 4 + G * Nn * Kk * 4,
         }
         res = {"N": Nn, "K": Kk}
         for part, fn in (("fwd", lambda: fq.fp8_grouped_gemm(qa, sa, off, qw, sw, c=c)),
+                         ("fwd_e4m3", lambda: fq.fp8_grouped_gemm_e4m3(qa, sa, off, qw, sw, q=qc, s=sc)),
                          ("dgrad", lambda: fq.fp8_grouped_gemm_dgrad(qdy, sdy, off, qw, sw, c=dx)),
                          ("wgrad", lambda: fq.fp8_grouped_gemm_wgrad(qdyT, sdyT, qaT, saT, off, c=dw))):
             us = time_launches([fn], reps, stream)
@@ -688,8 +694,11 @@ def moe_grouped(fq, synthetic, dev, stream, reps=10):
             rec.update({"algorithmic_bytes": int(nbytes[part]), "t_mfma_us": round(t_mfma, 1),
                         "t_hbm_us": round(t_hbm, 1), "frac_attainable": round(max(t_mfma, t_hbm) / us, 4)})
             res[part] = rec
+        q_us = time_launches([lambda: fq.fp8_quant_blockwise(c, fq.ROW_1x128, q=qc, s=sc)], reps, stream)
+        res["quant_1x128_fwd_out_us"] = round(q_us, 2)
+        res["e4m3_saving_us"] = round(res["fwd"]["us"] + q_us - res["fwd_e4m3"]["us"], 2)
         out[name] = res
-        del a, w, dy, qa, sa, qw, sw, qdy, sdy, qdyT, sdyT, qaT, saT, c, dx, dw
+        del a, w, dy, qa, sa, qw, sw, qdy, sdy, qdyT, sdyT, qaT, saT, c, dx, dw, qc, sc
     return out
 
 

@@ -46,6 +46,8 @@ _lib.fp8_grouped_gemm.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _p
                                   _p, _p, _p, _i64, _int, _p]
 _lib.fp8_gemm_blockscaled_e4m3.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64, _int,
                                            _p, _i64, _int, _p, _i64, _int, _p, _i64, _p, _i64, _p]
+_lib.fp8_grouped_gemm_e4m3.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _p,
+                                       _p, _p, _p, _i64, _p, _i64, _p]
 _lib.fp8_grouped_gemm_dgrad.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _p,
                                         _p, _p, _p, _i64, _int, _p]
 _lib.fp8_grouped_gemm_wgrad.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _p, _i64,
@@ -58,7 +60,7 @@ _lib.fp8_gemm_e8m0.argtypes = [_i64, _i64, _i64, _p, _i64, _p, _i64,
 _d = ctypes.c_double
 _lib.fp8_adam_step.argtypes = [_i64, _p, _p, _int, _p, _p, _p, _p, _d, _d, _d, _d, _d, _i64, _p]
 for _f in ("fp8_quant_blockwise", "fp8_quant_transpose", "fp8_gemm_blockscaled",
-           "fp8_gemm_blockscaled_e4m3", "fp8_grouped_gemm", "fp8_grouped_gemm_dgrad",
+           "fp8_gemm_blockscaled_e4m3", "fp8_grouped_gemm", "fp8_grouped_gemm_e4m3", "fp8_grouped_gemm_dgrad",
            "fp8_grouped_gemm_wgrad", "fp8_quant_blockwise_e8m0", "fp8_quant_transpose_e8m0",
            "fp8_gemm_e8m0", "fp8_adam_step"):
     getattr(_lib, _f).restype = _int
@@ -66,7 +68,7 @@ _lib.fp8q_status_string.argtypes = [_int]
 _lib.fp8q_status_string.restype = ctypes.c_char_p
 
 SYMBOLS = ("fp8_quant_blockwise", "fp8_quant_transpose", "fp8_gemm_blockscaled",
-           "fp8_gemm_blockscaled_e4m3", "fp8_grouped_gemm", "fp8_grouped_gemm_dgrad", "fp8_grouped_gemm_wgrad",
+           "fp8_gemm_blockscaled_e4m3", "fp8_grouped_gemm", "fp8_grouped_gemm_e4m3", "fp8_grouped_gemm_dgrad", "fp8_grouped_gemm_wgrad",
            "fp8_quant_blockwise_e8m0", "fp8_quant_transpose_e8m0", "fp8_gemm_e8m0",
            "fp8_adam_step", "fp8q_status_string")
 
@@ -505,6 +507,43 @@ def fp8_grouped_gemm(a: torch.Tensor, sa: torch.Tensor, group_offsets: torch.Ten
                                _stream(a.device, stream))
     _check(st, "fp8_grouped_gemm")
     return c
+
+
+def fp8_grouped_gemm_e4m3(a: torch.Tensor, sa: torch.Tensor, group_offsets: torch.Tensor,
+                          b: torch.Tensor, sb: torch.Tensor, q: Optional[torch.Tensor] = None,
+                          s: Optional[torch.Tensor] = None, stream=None):
+    """``fp8_grouped_gemm`` stored quantized: returns ``(q, s)``, the E4M3
+    codes ``q[M_pad, N]`` and 1x128 scales ``s[M_pad, ceil(N/128)]`` of the
+    result (rows at or past off[G] are not written)."""
+    M_pad, K = a.shape
+    G, N, Kb = b.shape
+    if Kb != K:
+        raise ValueError("contraction sizes differ")
+    if group_offsets.dtype != torch.int32 or group_offsets.numel() != G + 1:
+        raise ValueError("group_offsets must be int32 with G+1 entries")
+    if not (b.is_contiguous() and sb.is_contiguous() and group_offsets.is_contiguous()):
+        raise ValueError("b, sb and group_offsets must be contiguous")
+    dev = _device(a, stream)
+    _on(dev, a=a, sa=sa, group_offsets=group_offsets, b=b, sb=sb, q=q, s=s)
+    _dtype("a", a, _CODE_DTYPES)
+    _dtype("b", b, _CODE_DTYPES)
+    _dtype("sa", sa, (torch.float32,))
+    _dtype("sb", sb, (torch.float32,))
+    _min_shape("sa", sa, M_pad, _cdiv(K, TILE))
+    _shape("sb", sb, (G, _cdiv(N, TILE), _cdiv(K, TILE)))
+    if q is None:
+        q = _empty_aligned(M_pad, N, torch.uint8, a.device, 16)
+    if s is None:
+        s = torch.empty((M_pad, _cdiv(N, TILE)), dtype=torch.float32, device=a.device)
+    _dtype("q", q, _CODE_DTYPES)
+    _dtype("s", s, (torch.float32,))
+    _min_shape("q", q, M_pad, N)
+    _min_shape("s", s, M_pad, _cdiv(N, TILE))
+    st = _lib.fp8_grouped_gemm_e4m3(G, M_pad, N, K, _ptr(a), _ld(a), _ptr(sa), _ld(sa),
+                                    _ptr(group_offsets), _ptr(b), _ptr(sb), _ptr(q), _ld(q), _ptr(s),
+                                    _ld(s), _stream(a.device, stream))
+    _check(st, "fp8_grouped_gemm_e4m3")
+    return q, s
 
 
 def fp8_grouped_gemm_dgrad(a: torch.Tensor, sa: torch.Tensor, group_offsets: torch.Tensor,

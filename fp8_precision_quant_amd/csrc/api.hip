@@ -374,6 +374,32 @@ int fp8_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K,
     return launch_status(stream);
 }
 
+int fp8_grouped_gemm_e4m3(int64_t G, int64_t M_pad, int64_t N, int64_t K,
+                          const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                          const int32_t* group_offsets,
+                          const uint8_t* b, const float* sb,
+                          uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t stream)
+{
+    if (G < 1 || M_pad < 0 || N < 0 || K < 0 || M_pad % kTile) return FP8Q_ERR_SHAPE;
+    if (G > kMaxGroups) return FP8Q_ERR_UNSUPPORTED;
+    if (M_pad == 0 || N == 0) return FP8Q_OK;
+    if (K == 0 || K % kTile) return FP8Q_ERR_UNSUPPORTED;
+    if (!group_offsets || !q || !s || !a || !sa || !b || !sb) return FP8Q_ERR_NULL;
+    const int64_t KB = K / kTile;
+    if (lda < K || ldq < N || ldsa < KB || lds < cdiv(N, kTile)) return FP8Q_ERR_SHAPE;
+    if (G >= kMaxIndex || (M_pad / kTile) * cdiv(N, 128) >= kMaxIndex) return FP8Q_ERR_SHAPE;
+    if (!aligned16(q) || ldq % 16 || !aligned16(a) || !aligned16(b) || lda % 16) return FP8Q_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(group_offsets) & 3u) return FP8Q_ERR_ALIGN;
+    int st = check_device();
+    if (st != FP8Q_OK) return st;
+    st = offsets_status(group_offsets, G, M_pad, stream);
+    if (st != FP8Q_OK) return st;
+    if (!fp8q::launch_grouped_gemm_e4m3(G, M_pad, N, K, a, lda, sa, ldsa, group_offsets, b, sb, q, ldq, s,
+                                        lds, stream))
+        return FP8Q_ERR_UNSUPPORTED;
+    return launch_status(stream);
+}
+
 int fp8_grouped_gemm_dgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K,
                            const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
                            const int32_t* group_offsets,

@@ -63,6 +63,12 @@ bool launch_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K, const u
                          int64_t lda, const float* sa, int64_t ldsa, const int32_t* offsets,
                          const uint8_t* b, const float* sb, void* c, int64_t ldc, int c_dtype,
                          hipStream_t st);
+// The MoE forward stored quantized (E4M3 codes + 1x128 scales); false if not
+// covered (K % 128 != 0, more than 1024 groups, or an operand of 2 GiB or more).
+bool launch_grouped_gemm_e4m3(int64_t G, int64_t M_pad, int64_t N, int64_t K, const uint8_t* a,
+                              int64_t lda, const float* sa, int64_t ldsa, const int32_t* offsets,
+                              const uint8_t* b, const float* sb, uint8_t* q, int64_t ldq, float* s,
+                              int64_t lds, hipStream_t st);
 
 // AdamW with E4M3 moments: the step's fp32 scalars, each derived on the host
 // in double from the hyperparameters and rounded once

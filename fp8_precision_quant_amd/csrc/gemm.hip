@@ -189,6 +189,27 @@ bool launch_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K, const u
     return launch_grouped_gemm_nk(g, c_dtype == FP8Q_BF16, false, st);
 }
 
+bool launch_grouped_gemm_e4m3(int64_t G, int64_t M_pad, int64_t N, int64_t K, const uint8_t* a,
+                              int64_t lda, const float* sa, int64_t ldsa, const int32_t* offsets,
+                              const uint8_t* b, const float* sb, uint8_t* q, int64_t ldq, float* s,
+                              int64_t lds, hipStream_t st)
+{
+    GemmArgs g{};
+    g.M = M_pad; g.N = N; g.K = K;
+    g.a = a; g.lda = lda; g.sa = sa; g.ldsa = ldsa;
+    g.b = b; g.ldb = K; g.sb = sb;
+    g.KB = (int)((K + BK - 1) / BK);
+    g.ldsb = g.KB;
+    g.c = q; g.ldc = ldq;
+    g.cs = s; g.ldcs = lds;
+    g.offsets = offsets;
+    g.G = (int)G;
+    g.b_group_stride = N * K;
+    g.sb_group_stride = ((N + 127) / 128) * (int64_t)g.KB;
+    g.num_cus = device_cu_count();
+    return launch_grouped_gemm_w4_e4m3(g, st);
+}
+
 bool launch_grouped_gemm_dgrad(int64_t G, int64_t M_pad, int64_t N, int64_t K, const uint8_t* a,
                                int64_t lda, const float* sa, int64_t ldsa, const int32_t* offsets,
                                const uint8_t* w, const float* sw, void* c, int64_t ldc, int c_dtype,

@@ -70,6 +70,8 @@ bool launch_gemm_w4_e8m0(const GemmArgs& g, int sb_mode, bool b_kn, bool out_bf1
 // dgrad, B read as stored [K][N]; K % 128 == 0); false if it does not cover
 // the call.
 bool launch_grouped_gemm_w4(const GemmArgs& g, bool out_bf16, bool b_kn, hipStream_t st);
+// ... the forward stored quantized (E4M3 codes + 1x128 scales); false if not covered.
+bool launch_grouped_gemm_w4_e4m3(const GemmArgs& g, hipStream_t st);
 // ... and over groups of K (MoE weight gradient); false if not covered.
 bool launch_grouped_wgrad_w4(const GemmArgs& g, hipStream_t st);
 // Grouped (MoE) launch of the same kernel: A row tiles select their expert

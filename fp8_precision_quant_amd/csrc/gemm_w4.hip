@@ -277,8 +277,8 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
     static_assert(!P2 || (GMODE == 0 && SA_MODE == SA_ROW && SB_MODE != SB_TENSOR && OUT != OUT_E4M3),
                   "power-of-two scales: dense, row-scaled A, row- or block-scaled B, fp32 or bf16 out");
     static_assert(!B_KN || (GMODE <= 1 && SB_MODE != SB_ROW), "[K][N] B: block or tensor scales, no groups of K");
-    static_assert(GMODE != 1 || (SA_MODE == SA_ROW && SB_MODE == SB_BLOCK && OUT != OUT_E4M3),
-                  "groups of rows: row-scaled A, block-scaled B, fp32 or bf16 out");
+    static_assert(GMODE != 1 || (SA_MODE == SA_ROW && SB_MODE == SB_BLOCK && (OUT != OUT_E4M3 || !B_KN)),
+                  "groups of rows: row-scaled A, block-scaled B; E4M3 out for [N][K] B (the forward)");
     static_assert(GMODE != 2 || (SA_MODE == SA_ROW && SB_MODE == SB_ROW && OUT == OUT_F32),
                   "groups of K: row-scaled A and B, fp32 out");
     static_assert(OUT != OUT_E4M3 || SB_MODE != SB_ROW, "quantize-on-store: uniform B scales");
@@ -962,7 +962,7 @@ static void w4_launch_out(const GemmArgs& g, int out, hipStream_t st)
             hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_BF16, GMODE, B_KN, P2>), grid, dim3(kW4Threads), 0, st, a);
     } else if (out == OUT_F32) {
         hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_F32, GMODE, B_KN, P2>), grid, dim3(kW4Threads), 0, st, a);
-    } else if constexpr (SB_MODE != SB_ROW && GMODE == 0 && !P2) {
+    } else if constexpr (SB_MODE != SB_ROW && (GMODE == 0 || (GMODE == 1 && !B_KN)) && !P2) {
         hipLaunchKernelGGL((gemm_w4_kernel<SA_MODE, SB_MODE, OUT_E4M3, GMODE, B_KN>), grid, dim3(kW4Threads), 0, st, a);
     }
 }
@@ -1026,6 +1026,20 @@ bool launch_grouped_gemm_w4(const GemmArgs& g, bool out_bf16, bool b_kn, hipStre
     const int out = out_bf16 ? OUT_BF16 : OUT_F32;
     if (b_kn) w4_launch_out<SA_ROW, SB_BLOCK, 1, true>(g, out, st);
     else w4_launch_out<SA_ROW, SB_BLOCK, 1>(g, out, st);
+    return true;
+}
+
+// The MoE forward stored quantized (E4M3 codes in p.c, 1x128 scales in
+// p.cs); K a multiple of 128, the operand limits of launch_grouped_gemm_w4;
+// false otherwise.
+bool launch_grouped_gemm_w4_e4m3(const GemmArgs& g, hipStream_t st)
+{
+    const int64_t lim = (int64_t)1 << 31;
+    if (g.K <= 0 || g.K % 128 != 0 || g.G < 1 || g.G > kMaxLdsGroups) return false;
+    if ((g.M + TBM) * g.lda >= lim || g.N * g.ldb >= lim || (g.M + TBM) * g.ldsa * 4 >= lim ||
+        g.sb_group_stride * 4 >= lim)
+        return false;
+    w4_launch_out<SA_ROW, SB_BLOCK, 1>(g, OUT_E4M3, st);
     return true;
 }
 

@@ -222,6 +222,29 @@ int fp8_grouped_gemm(int64_t G, int64_t M_pad, int64_t N, int64_t K,
                      void* c, int64_t ldc, int c_dtype, hipStream_t stream);
 
 /*
+ * fp8_grouped_gemm_e4m3 -- the same MoE expert GEMM stored quantized: E4M3
+ * codes of C and its 1x128 scales along N (the next layer's activation
+ * quantization, as fp8_gemm_blockscaled_e4m3; Ling 2.0 FP8 blog, "FP8 padding
+ * routing map" and "fine-grained quantization").
+ *
+ * With C the fp32 result of fp8_grouped_gemm for the same arguments, the
+ * codes and scales of rows [0, off[G]) are exactly those
+ * fp8_quant_blockwise(FP8Q_ROW_1x128) gives for C; rows at or past off[G]
+ * are not written.
+ *  a .. sb : as fp8_grouped_gemm.
+ *  q, ldq  : codes [M_pad][N], ldq >= N (multiple of 16, q 16-byte aligned).
+ *  s, lds  : scales s[m*lds + n/128], lds >= ceil(N/128).
+ * K must be a positive multiple of 128 (FP8Q_ERR_UNSUPPORTED otherwise), as
+ * must M_pad; FP8Q_ERR_UNSUPPORTED also for G > 1024 or an operand of 2 GiB
+ * or more.
+ */
+int fp8_grouped_gemm_e4m3(int64_t G, int64_t M_pad, int64_t N, int64_t K,
+                          const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                          const int32_t* group_offsets,
+                          const uint8_t* b, const float* sb,
+                          uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t stream);
+
+/*
  * fp8_grouped_gemm_dgrad -- MoE expert dgrad over padded groups (Ling 2.0
  * FP8 blog, "FP8 padding routing map" and "FP8 on-demand transpose weight").
  *

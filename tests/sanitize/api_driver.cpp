@@ -106,6 +106,12 @@ int main()
            "grouped K%16");
     expect(fp8_grouped_gemm(2, 128, 128, 128, P, 128, F, 1, reinterpret_cast<int32_t*>(U), P, F, P, 128, FP8Q_BF16,
                             nullptr), FP8Q_ERR_ALIGN, "grouped offsets align");
+    expect(fp8_grouped_gemm_e4m3(2, 128, 128, 200, P, 208, F, 2, O, P, F, P, 128, F, 1, nullptr), FP8Q_ERR_UNSUPPORTED,
+           "grouped e4m3 K%128");
+    expect(fp8_grouped_gemm_e4m3(2, 128, 300, 128, P, 128, F, 1, O, P, F, P, 304, F, 2, nullptr), FP8Q_ERR_SHAPE,
+           "grouped e4m3 lds");
+    expect(fp8_grouped_gemm_e4m3(2, 128, 128, 128, P, 128, F, 1, O, P, F, U, 128, F, 1, nullptr), FP8Q_ERR_ALIGN,
+           "grouped e4m3 q align");
     expect(fp8_grouped_gemm_dgrad(2, 128, 128, 128, P, 128, F, 0, O, P, F, P, 128, FP8Q_BF16, nullptr), FP8Q_ERR_SHAPE,
            "dgrad ldsa");
     expect(fp8_grouped_gemm_wgrad(2, 256, 128, 128, P, 256, F, 1, P, 256, F, 2, O, F, 128, nullptr), FP8Q_ERR_SHAPE,

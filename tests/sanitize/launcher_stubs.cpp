@@ -71,6 +71,12 @@ bool launch_grouped_gemm(int64_t, int64_t, int64_t, int64_t, const uint8_t*, int
 {
     reached("launch_grouped_gemm");
 }
+bool launch_grouped_gemm_e4m3(int64_t, int64_t, int64_t, int64_t, const uint8_t*, int64_t, const float*, int64_t,
+                              const int32_t*, const uint8_t*, const float*, uint8_t*, int64_t, float*, int64_t,
+                              hipStream_t)
+{
+    reached("launch_grouped_gemm_e4m3");
+}
 void launch_adam_fp8(int64_t, float*, const void*, int, uint8_t*, float*, uint8_t*, float*, const AdamScalars&,
                      hipStream_t)
 {

@@ -1,4 +1,5 @@
 """GPU parity of the grouped (MoE expert) GEMMs: fp8_grouped_gemm (forward),
+fp8_grouped_gemm_e4m3 (the forward stored as E4M3 codes with 1x128 scales),
 fp8_grouped_gemm_dgrad and fp8_grouped_gemm_wgrad (backward).
 
 Groups are padded with zero rows to multiples of 128 (Ling 2.0 FP8 blog,
@@ -8,7 +9,10 @@ group equals the dense GEMM with that expert's weights, pad rows are exactly
 zero, empty groups are skipped, and rows past the last group are untouched.
 The backward: dgrad reads each expert's weight as stored and must equal the
 oracle's per-group dgrad; wgrad sums each expert's tokens only (empty groups
-give exactly 0) from the transposed re-quantization of dY and X.
+give exactly 0) from the transposed re-quantization of dY and X.  The
+quantized forward must be byte for byte the GPU quantizer's output on the
+fp32 forward's rows [0, off[G]), leave the rest untouched, and be a valid
+quantization of the oracle's result (as for the dense quantize-on-store).
 Workload: 8192 tokens, hidden 2048, 128 experts of intermediate 768, top-8
 Zipf(1.1) routing, gate/up (N=1536, K=2048) and down (N=2048, K=768).
 """
@@ -279,3 +283,109 @@ def test_moe_wgrad_full_size_row_per_tile(moe_backward, which):
     _, R = oracle.grouped_gemm_wgrad(at, sat, bt, sbt, off, rows=rows, f64=True)
     for e in range(c.shape[0]):
         gemm_parity(c[e][rows], co[e], R[e])
+
+
+def _run_e4m3(a, sa, off, b, sb, q=None, s=None):
+    q, s = fq.fp8_grouped_gemm_e4m3(to_dev(a), to_dev(sa), to_dev(off.astype(np.int32)), to_dev(b),
+                                    to_dev(sb), q=q, s=s)
+    torch.cuda.synchronize()
+    return q, s
+
+
+def _e4m3_matches_quantized_fp32(a, sa, off, b, sb):
+    """Codes and scales of the quantized grouped forward against the GPU
+    quantizer run on the fp32 grouped forward, rows [0, off[G]): byte equal."""
+    q, s = _run_e4m3(a, sa, off, b, sb)
+    c = _run(a, sa, off, b, sb)
+    used = int(off[-1])
+    rq, rs = fq.fp8_quant_blockwise(c[:used], fq.ROW_1x128)
+    torch.cuda.synchronize()
+    assert torch.equal(q[:used], rq)
+    assert torch.equal(s[:used].view(torch.int32), rs.view(torch.int32))
+    return host(q), host(s)
+
+
+def _e4m3_valid(q, s, co, R):
+    """A valid 1x128 quantization of the oracle's result co (rows of q, s):
+    each tile's scale within the GEMM tolerance of its amax / 448, each
+    dequantized code within half an E4M3 step of co plus that tolerance."""
+    co = co.astype(np.float64)
+    n, N = co.shape
+    NB = -(-N // 128)
+    pad = NB * 128 - N
+    amax_o = np.abs(np.pad(co, ((0, 0), (0, pad)))).reshape(n, NB, 128).max(axis=2)
+    tol_t = 1e-3 * np.pad(R, ((0, 0), (0, pad))).reshape(n, NB, 128).max(axis=2)
+    assert np.all(np.abs(s[:, :NB].astype(np.float64) * 448 - amax_o) <= tol_t * 1.0001 + 1e-30)
+    s_full = np.repeat(s[:, :NB].astype(np.float64), 128, axis=1)[:, :N]
+    deq = oracle.e4m3_decode(q[:, :N]).astype(np.float64) * s_full
+    half_step = np.maximum(np.abs(co) * 2.0 ** -4, s_full * 2.0 ** -10)
+    assert np.all(np.abs(deq - co) <= half_step * 1.0001 + 1e-3 * R * 2 + 1e-30)
+
+
+# N = 300 leaves a ragged last scale tile; K = 384 and 128 are whole chunks
+@pytest.mark.parametrize("N,K", [(300, 384), (256, 128)])
+def test_e4m3_small_groups_with_empty_and_ragged(N, K):
+    counts = [100, 0, 260, 1, 0, 128]
+    G, KB = len(counts), K // 128
+    off = _groups(counts)
+    M = int(off[-1])
+    A = np.zeros((M, K), np.uint8)
+    sa = np.zeros((M, KB), np.float32)
+    for e, cnt in enumerate(counts):
+        A[off[e]:off[e] + cnt] = _codes((cnt, K), 210 + e)
+        sa[off[e]:off[e] + cnt] = _scales((cnt, KB), 220 + e)
+    B = _codes((G, N, K), 230)
+    sb = _scales((G, -(-N // 128), KB), 231)
+    q, s = _e4m3_matches_quantized_fp32(A, sa, off, B, sb)
+    co = oracle.grouped_gemm(A, sa, off, B, sb)
+    _, R = oracle.grouped_gemm(A, sa, off, B, sb, f64=True)
+    _e4m3_valid(q, s, co, R)
+    for e, cnt in enumerate(counts):                 # pad rows: zero codes, zero scales
+        assert np.all(q[off[e] + cnt:off[e + 1]] == 0)
+        assert np.all(s[off[e] + cnt:off[e + 1]] == 0)
+
+
+def test_e4m3_rows_past_last_group_and_columns_past_n_untouched():
+    G, N, K = 2, 200, 256
+    off = np.array([0, 128, 256])
+    M_pad = 512                              # the last 256 rows belong to no group
+    A = _codes((M_pad, K), 240)
+    sa = _scales((M_pad, 2), 241)
+    B = _codes((G, N, K), 242)
+    sb = _scales((G, 2, 2), 243)
+    qbuf = torch.full((M_pad, 224), 0x5A, dtype=torch.uint8, device=DEV)
+    sbuf = torch.full((M_pad, 3), -9.0, dtype=torch.float32, device=DEV)
+    q, s = _run_e4m3(A, sa, off, B, sb, q=qbuf[:, :N], s=sbuf[:, :2])
+    qh, sh = host(qbuf), host(sbuf)
+    assert np.all(qh[256:] == 0x5A) and np.all(qh[:, N:] == 0x5A)
+    assert np.all(sh[256:] == -9.0) and np.all(sh[:, 2:] == -9.0)
+    co = oracle.grouped_gemm(A[:256], sa[:256], off, B, sb)
+    _, R = oracle.grouped_gemm(A[:256], sa[:256], off, B, sb, f64=True)
+    _e4m3_valid(qh[:256, :N], sh[:256, :2], co, R)
+
+
+def test_e4m3_rejects_ragged_k():
+    counts = [128]
+    off = _groups(counts)
+    A, sa = _codes((128, 200), 250), _scales((128, 2), 251)
+    B, sb = _codes((1, 128, 200), 252), _scales((1, 1, 2), 253)
+    with pytest.raises(fq.Fp8qError, match="UNSUPPORTED"):
+        _run_e4m3(A, sa, off, B, sb)
+
+
+@pytest.mark.parametrize("which", ["gate_up", "down"])
+def test_moe_e4m3_full_size(moe_inputs, which):
+    """Both MoE expert GEMMs at full size (the launches the MoE leg of the
+    bench times): codes and scales byte-identical over every grouped row to
+    the GPU quantizer on the fp32 grouped forward; on one row of every
+    128-row tile, a valid quantization of the oracle's result."""
+    m, gu, dn = moe_inputs
+    qa, sa, qb, sb = gu if which == "gate_up" else dn
+    off = m.offsets.astype(np.int64)
+    q, s = _e4m3_matches_quantized_fp32(qa, sa, off, qb, sb)
+    rows = synthetic.rows_per_tile(qa.shape[0], 409)
+    co = oracle.grouped_gemm(qa, sa, off, qb, sb, rows=rows)
+    _, R = oracle.grouped_gemm(qa, sa, off, qb, sb, rows=rows, f64=True)
+    _e4m3_valid(q[rows], s[rows], co, R)
+    pad = m.token_index < 0
+    assert np.all(q[pad] == 0) and np.all(s[pad] == 0)

@@ -23,7 +23,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert names == sorted(["fp8_quant_blockwise", "fp8_quant_transpose", "fp8_gemm_blockscaled",
-                            "fp8_gemm_blockscaled_e4m3", "fp8_grouped_gemm", "fp8_grouped_gemm_dgrad", "fp8_grouped_gemm_wgrad",
+                            "fp8_gemm_blockscaled_e4m3", "fp8_grouped_gemm", "fp8_grouped_gemm_e4m3",
+                            "fp8_grouped_gemm_dgrad", "fp8_grouped_gemm_wgrad",
                             "fp8_quant_blockwise_e8m0", "fp8_quant_transpose_e8m0", "fp8_gemm_e8m0",
                             "fp8_adam_step", "fp8q_status_string"])
 
@@ -166,6 +167,34 @@ def test_gemm_e4m3_validation():
     assert call(a15=264) == fq.ERR_ALIGN                   # ldq % 16 != 0
     assert call(a14=A16 + 1) == fq.ERR_ALIGN
     assert call(a3=MIS) == fq.ERR_ALIGN
+
+
+def test_grouped_e4m3_validation():
+    f = L.fp8_grouped_gemm_e4m3
+    # G, M_pad, N, K, a, lda, sa, ldsa, off, b, sb, q, ldq, s, lds, stream
+    base = [4, 512, 256, 256, A16, 256, A16, 2, A16, A16, A16, A16, 256, A16, 2, None]
+    def call(**ch):
+        a = list(base)
+        for i, v in ch.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a0=0) == fq.ERR_SHAPE
+    assert call(a1=500) == fq.ERR_SHAPE                    # M_pad not a multiple of 128
+    assert call(a1=0, a4=None) == fq.OK                    # empty output
+    assert call(a2=0, a11=None) == fq.OK
+    assert call(a3=0) == fq.ERR_UNSUPPORTED                # K must be a positive multiple of 128
+    assert call(a3=200, a5=256) == fq.ERR_UNSUPPORTED
+    assert call(a8=None) == fq.ERR_NULL
+    assert call(a11=None) == fq.ERR_NULL
+    assert call(a13=None) == fq.ERR_NULL
+    assert call(a5=200) == fq.ERR_SHAPE                    # lda < K
+    assert call(a7=1) == fq.ERR_SHAPE                      # ldsa < K/128
+    assert call(a12=200) == fq.ERR_SHAPE                   # ldq < N
+    assert call(a14=1) == fq.ERR_SHAPE                     # lds < ceil(N/128)
+    assert call(a12=264) == fq.ERR_ALIGN                   # ldq % 16 != 0
+    assert call(a11=A16 + 1) == fq.ERR_ALIGN
+    assert call(a8=A16 + 2) == fq.ERR_ALIGN
+    assert call(a0=1025, a1=1025 * 128) == fq.ERR_UNSUPPORTED
 
 
 def test_grouped_dgrad_validation():
