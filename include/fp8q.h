@@ -54,7 +54,8 @@
  *  - Shapes may be any size >= 0 (ragged edge tiles are clipped); a call with
  *    an empty output returns FP8Q_OK without launching anything.  A GEMM
  *    with K == 0 writes zeros; its operand and scale pointers may then be
- *    NULL (they are not read).
+ *    NULL (they are not read).  (fp8_grouped_gemm_e4m3 is the exception: it
+ *    takes K as a positive multiple of 128 only.)
  *  - Arguments are validated on the host before any launch; a failing call
  *    returns its status and enqueues nothing.  After launching, a pending
  *    launch error is reported as FP8Q_ERR_LAUNCH.
