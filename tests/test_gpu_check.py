@@ -3,7 +3,8 @@ enqueued, a check kernel validates the group-offset contract (off[0] = 0,
 non-decreasing, every offset a multiple of 128, off[G] <= M_pad; the padded
 routing map of the Ling 2.0 FP8 blog, "FP8 padding routing map").  A
 violation returns FP8Q_ERR_SHAPE and enqueues no GEMM (the output keeps its
-sentinel); valid offsets give the same bytes as without the check.
+sentinel); valid offsets give the same bytes as without the check.  The
+forward is checked with both outputs (fp32, and E4M3 codes with scales).
 
 Every violating offset vector used here stays within [0, M_pad], and those
 given to the backward kernels are also non-decreasing, so the GEMM would
@@ -49,6 +50,11 @@ def _fwd(o, off, c):
     return fq.fp8_grouped_gemm(o["a"], o["sa"], off, o["b"], o["sb"], out_dtype=torch.float32, c=c)
 
 
+def _fwd_e4m3(o, off, c):
+    q, sc = c
+    return fq.fp8_grouped_gemm_e4m3(o["a"], o["sa"], off, o["b"], o["sb"], q=q, s=sc)
+
+
 def _dgrad(o, off, c):
     return fq.fp8_grouped_gemm_dgrad(o["dy"], o["sdy"], off, o["b"], o["sb"], out_dtype=torch.float32, c=c)
 
@@ -58,23 +64,39 @@ def _wgrad(o, off, c):
 
 
 def _out(kind):
+    if kind == "fwd_e4m3":
+        return (torch.full((M_PAD, N), 0x5A, dtype=torch.uint8, device=DEV),
+                torch.full((M_PAD, N // 128), -7.0, dtype=torch.float32, device=DEV))
     shape = {"fwd": (M_PAD, N), "dgrad": (M_PAD, K), "wgrad": (G, N, K)}[kind]
     return torch.full(shape, -7.0, dtype=torch.float32, device=DEV)
 
 
-RUN = {"fwd": _fwd, "dgrad": _dgrad, "wgrad": _wgrad}
+def _bytes(c):
+    parts = c if isinstance(c, tuple) else (c,)
+    return b"".join(host(t).tobytes() for t in parts)
 
 
-@pytest.mark.parametrize("kind", ["fwd", "dgrad", "wgrad"])
+def _untouched(c):
+    if isinstance(c, tuple):
+        return bool((c[0] == 0x5A).all()) and bool((c[1] == -7.0).all())
+    return bool((c == -7.0).all())
+
+
+RUN = {"fwd": _fwd, "fwd_e4m3": _fwd_e4m3, "dgrad": _dgrad, "wgrad": _wgrad}
+
+
+@pytest.mark.parametrize("kind", ["fwd", "fwd_e4m3", "dgrad", "wgrad"])
 def test_valid_offsets_run_unchanged(operands, kind, monkeypatch):
     off = _off([0, 128, 128, 384])                  # an empty middle group
     monkeypatch.delenv("FP8Q_CHECK", raising=False)
-    plain = RUN[kind](operands, off, _out(kind))
+    plain = _out(kind)
+    RUN[kind](operands, off, plain)
     torch.cuda.synchronize()
     monkeypatch.setenv("FP8Q_CHECK", "1")
-    checked = RUN[kind](operands, off, _out(kind))
+    checked = _out(kind)
+    RUN[kind](operands, off, checked)
     torch.cuda.synchronize()
-    assert np.array_equal(host(plain).view(np.uint32), host(checked).view(np.uint32))
+    assert _bytes(plain) == _bytes(checked)
 
 
 @pytest.mark.parametrize("values, what", [
@@ -82,14 +104,15 @@ def test_valid_offsets_run_unchanged(operands, kind, monkeypatch):
     ([0, 256, 128, 384], "decreasing offsets"),
     ([128, 256, 256, 384], "first offset not zero"),
 ])
-def test_forward_violations_are_reported(operands, values, what, monkeypatch):
+@pytest.mark.parametrize("kind", ["fwd", "fwd_e4m3"])
+def test_forward_violations_are_reported(operands, kind, values, what, monkeypatch):
     monkeypatch.setenv("FP8Q_CHECK", "1")
-    c = _out("fwd")
+    c = _out(kind)
     with pytest.raises(fq.Fp8qError) as err:
-        _fwd(operands, _off(values), c)
+        RUN[kind](operands, _off(values), c)
     assert err.value.status == fq.ERR_SHAPE, what
     torch.cuda.synchronize()
-    assert bool((c == -7.0).all()), "the GEMM ran despite " + what
+    assert _untouched(c), "the GEMM ran despite " + what
 
 
 @pytest.mark.parametrize("kind", ["dgrad", "wgrad"])
@@ -100,4 +123,4 @@ def test_backward_violation_is_reported(operands, kind, monkeypatch):
         RUN[kind](operands, _off([0, 100, 256, 384]), c)
     assert err.value.status == fq.ERR_SHAPE
     torch.cuda.synchronize()
-    assert bool((c == -7.0).all())
+    assert _untouched(c)
