@@ -194,6 +194,15 @@ __device__ __forceinline__ void w4_fmac(float& acc, float p, float s)
     asm volatile("v_fmac_f32_e32 %0, %1, %2" : "+v"(acc) : "v"(p), "v"(s) : "memory");
 }
 
+// max(m, |a|, |b|) for m >= 0 and finite a, b (exact; no NaN quieting, which
+// the compiler would otherwise add for values it cannot see the origin of)
+__device__ __forceinline__ float w4_max3_abs(float m, float a, float b)
+{
+    float d;
+    asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(d) : "v"(m), "v"(a), "v"(b));
+    return d;
+}
+
 __device__ __forceinline__ void w4_mul(float& d, float a, float b)
 {
     asm volatile("v_mul_f32_e32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b) : "memory");
@@ -672,15 +681,33 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
             // are left out of the amax.
             float mx[PMI];
             const int64_t ncol0 = cn0 + 64 * wq + 4 * kgrp;
+            if (cn0 + 64 * wq + 64 <= N) {
+                // all 64 columns inside: |x| maxima three operands at a time
+#pragma unroll
+                for (int i = 0; i < PMI; ++i) {
+                    float v = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < NNI; ++j) {
+                        v = w4_max3_abs(v, acc[i][j][0], acc[i][j][1]);
+                        v = w4_max3_abs(v, acc[i][j][2], acc[i][j][3]);
+                    }
+                    mx[i] = v;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < PMI; ++i) {
+                    float v = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < NNI; ++j)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (ncol0 + 16 * j + r < N) v = fmaxf(v, fabsf(acc[i][j][r]));
+                    mx[i] = v;
+                }
+            }
 #pragma unroll
             for (int i = 0; i < PMI; ++i) {
-                float v = 0.0f;
-#pragma unroll
-                for (int j = 0; j < NNI; ++j)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (ncol0 + 16 * j + r < N) v = fmaxf(v, fabsf(acc[i][j][r]));
-                v = fmaxf(v, __shfl_xor(v, 16));
+                const float v = fmaxf(mx[i], __shfl_xor(mx[i], 16));
                 mx[i] = fmaxf(v, __shfl_xor(v, 32));
                 if (kgrp == 0) RowMax[wq][16 * i + lrow] = mx[i];
             }
