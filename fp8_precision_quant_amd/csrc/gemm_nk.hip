@@ -82,6 +82,14 @@ __device__ __forceinline__ void ds_write128(uint32_t addr, v4f v)
     asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF) : "memory");
 }
 
+// max(m, |a|, |b|) for m >= 0 and finite a, b (exact; no NaN quieting)
+__device__ __forceinline__ float nk_max3_abs(float m, float a, float b)
+{
+    float d;
+    asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(d) : "v"(m), "v"(a), "v"(b));
+    return d;
+}
+
 template <int I>
 __device__ __forceinline__ v8i frag_nk(uint32_t r0, uint32_t r1)
 {
@@ -588,15 +596,33 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
                 // [K][N] B they are computed from bytes past the row's end).
                 float mx[4];
                 const int64_t ncol0 = cn0 + 64 * wq + 4 * kgrp;
+                if (cn0 + 64 * wq + 64 <= N) {
+                    // all 64 columns inside: |x| maxima three operands at a time
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float v = 0.0f;
+#pragma unroll
+                        for (int j = 0; j < NNI; ++j) {
+                            v = nk_max3_abs(v, acc[h * 4 + i][j][0], acc[h * 4 + i][j][1]);
+                            v = nk_max3_abs(v, acc[h * 4 + i][j][2], acc[h * 4 + i][j][3]);
+                        }
+                        mx[i] = v;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float v = 0.0f;
+#pragma unroll
+                        for (int j = 0; j < NNI; ++j)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (ncol0 + 16 * j + r < N) v = fmaxf(v, fabsf(acc[h * 4 + i][j][r]));
+                        mx[i] = v;
+                    }
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float v = 0.0f;
-#pragma unroll
-                    for (int j = 0; j < NNI; ++j)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (ncol0 + 16 * j + r < N) v = fmaxf(v, fabsf(acc[h * 4 + i][j][r]));
-                    v = fmaxf(v, __shfl_xor(v, 16));
+                    const float v = fmaxf(mx[i], __shfl_xor(mx[i], 16));
                     mx[i] = fmaxf(v, __shfl_xor(v, 32));
                 }
                 // row maxima of the two waves of a tile meet past the
