@@ -40,6 +40,16 @@ __device__ __forceinline__ uint32_t bf16_rne(float f)
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// bf16_rne(a) | bf16_rne(b) << 16 for finite a, b in one instruction (the
+// packed conversion rounds to nearest even; checked equal to bf16_rne over
+// every non-NaN fp32 pattern, denormals and infinities included)
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b)
+{
+    uint32_t d;
+    asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+    return d;
+}
+
 // Zero the bytes of a 16-byte chunk at or beyond `valid` (0..16).
 __device__ __forceinline__ uint4 mask_bytes(uint4 v, int valid)
 {

@@ -683,8 +683,8 @@ __global__ __launch_bounds__(kThreads) void gemm_nk_kernel(GemmArgs p)
                     const v4f v = acc[h * 4 + i][j];
                     if (n + 3 < N) {
                         if (OUT == OUT_BF16) {
-                            const uint32_t lo = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-                            const uint32_t hi = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+                            const uint32_t lo = bf16x2_rne(v[0], v[1]);
+                            const uint32_t hi = bf16x2_rne(v[2], v[3]);
                             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.c) + m * p.ldc + n) = make_uint2(lo, hi);
                         } else {
                             *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.c) + m * p.ldc + n) = v;

@@ -784,10 +784,10 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
 #pragma unroll
                     for (int pq = 0; pq < NNI / 2; ++pq) {
                         const v4f A = acc[i][2 * pq], B = acc[i][2 * pq + 1];
-                        const uint32_t a0 = bf16_rne(A[0]) | (bf16_rne(A[1]) << 16);
-                        const uint32_t a1 = bf16_rne(A[2]) | (bf16_rne(A[3]) << 16);
-                        const uint32_t b0 = bf16_rne(B[0]) | (bf16_rne(B[1]) << 16);
-                        const uint32_t b1 = bf16_rne(B[2]) | (bf16_rne(B[3]) << 16);
+                        const uint32_t a0 = bf16x2_rne(A[0], A[1]);
+                        const uint32_t a1 = bf16x2_rne(A[2], A[3]);
+                        const uint32_t b0 = bf16x2_rne(B[0], B[1]);
+                        const uint32_t b1 = bf16x2_rne(B[2], B[3]);
                         // swap 1 (lane ^ 32): kgrp 0, 1 keep block 2p and take
                         // its columns 4 kgrp + 8 from kgrp + 2; kgrp 2, 3 keep
                         // block 2p + 1 and take its columns 4 kgrp - 8
@@ -855,8 +855,8 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
                 const v4f v = acc[i][j];
                 if (n + 3 < N) {
                     if (OUT == OUT_BF16) {
-                        const uint32_t lo = bf16_rne(v[0]) | (bf16_rne(v[1]) << 16);
-                        const uint32_t hi = bf16_rne(v[2]) | (bf16_rne(v[3]) << 16);
+                        const uint32_t lo = bf16x2_rne(v[0], v[1]);
+                        const uint32_t hi = bf16x2_rne(v[2], v[3]);
                         *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(cbase) + m * p.ldc + n) = make_uint2(lo, hi);
                     } else if (GMODE == 2) {
                         // the MoE weight gradient streams its fp32 output
