@@ -732,24 +732,20 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
                 if (cn0 + 64 * wq + 64 <= N) {
                     // one 16-byte store per lane: the four lanes of a row
                     // (kgrp L holds the codes of columns 16j + 4L .. + 3,
-                    // j = 0..3) transpose their 4 x 4 dwords in two swaps
-                    // (lane ^ 32, then lane ^ 16), after which lane L holds
-                    // columns 16L .. 16L + 15
-                    const int L = kgrp, h = L >> 1, e = L & 1;
-                    // swap 1: keep the blocks 2h, 2h + 1, send the other two
-                    const uint32_t own0 = h ? code[2] : code[0], own1 = h ? code[3] : code[1];
-                    const uint32_t r0 = (uint32_t)__shfl_xor((int)(h ? code[0] : code[2]), 32);
-                    const uint32_t r1 = (uint32_t)__shfl_xor((int)(h ? code[1] : code[3]), 32);
-                    // swap 2: keep block L (sources L and L ^ 2), send block L ^ 1
-                    const uint32_t own_keep = e ? own1 : own0, r_keep = e ? r1 : r0;
-                    const uint32_t recv_own = (uint32_t)__shfl_xor((int)(e ? own0 : own1), 16);
-                    const uint32_t recv_r = (uint32_t)__shfl_xor((int)(e ? r0 : r1), 16);
-                    // dword s of the lane's 16 bytes comes from lane s: V[s ^ L]
-                    const uint32_t v0 = e ? recv_own : own_keep, v1 = e ? own_keep : recv_own;
-                    const uint32_t v2 = e ? recv_r : r_keep, v3 = e ? r_keep : recv_r;
+                    // j = 0..3) transpose their 4 x 4 dwords with the
+                    // half-wave and row swaps (no lane selects): after
+                    // swap 1 (lanes 0-31 <-> 32-63) lane L holds blocks 2h and
+                    // 2h + 1 (h = L >> 1), each as the dwords of lanes
+                    // L & 1 and (L & 1) + 2; after swap 2 (16-lane rows
+                    // 0 <-> 1, 2 <-> 3) it holds block L from lanes 0..3 in
+                    // order, i.e. columns 16L .. 16L + 15
+                    const auto s02 = __builtin_amdgcn_permlane32_swap(code[0], code[2], false, false);
+                    const auto s13 = __builtin_amdgcn_permlane32_swap(code[1], code[3], false, false);
+                    const auto w0 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+                    const auto w1 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
                     if (m < m_end)
-                        *reinterpret_cast<uint4*>(qrow + cn0 + 64 * wq + 16 * L) =
-                            h ? make_uint4(v2, v3, v0, v1) : make_uint4(v0, v1, v2, v3);
+                        *reinterpret_cast<uint4*>(qrow + cn0 + 64 * wq + 16 * kgrp) =
+                            make_uint4(w0[0], w0[1], w1[0], w1[1]);
                 } else if (m < m_end) {
 #pragma unroll
                 for (int j = 0; j < NNI; ++j) {
@@ -771,36 +767,31 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
         if constexpr (OUT == OUT_BF16) {
             if (cn0 + 64 * wq + 64 <= N) {
                 // 16-byte stores: for each pair of 16-column blocks (2p, 2p+1)
-                // the four lanes of a row (kgrp 0..3, four columns of each
-                // block) exchange halves in two swaps, lane ^ 32 then lane ^ 16,
-                // after which lane kgrp holds columns 32p + 8 kgrp .. + 7: half
-                // the store instructions of one 8-byte store per block
-                const bool lo = kgrp < 2;
-                const bool give_x = ((kgrp ^ (kgrp >> 1)) & 1) != 0;
-                const bool got_first = (kgrp & 1) != 0;
+                // the four lanes of a row (kgrp k, four columns of each block)
+                // exchange halves with the half-wave and row swaps (no lane
+                // selects), after which lane k holds columns 32p + 8k .. + 7:
+                // half the store instructions of one 8-byte store per block
 #pragma unroll
                 for (int i = 0; i < PMI; ++i) {
                     const int64_t m = cm0 + 16 * i + lrow;
 #pragma unroll
                     for (int pq = 0; pq < NNI / 2; ++pq) {
                         const v4f A = acc[i][2 * pq], B = acc[i][2 * pq + 1];
-                        const uint32_t a0 = bf16x2_rne(A[0], A[1]);
-                        const uint32_t a1 = bf16x2_rne(A[2], A[3]);
-                        const uint32_t b0 = bf16x2_rne(B[0], B[1]);
-                        const uint32_t b1 = bf16x2_rne(B[2], B[3]);
-                        // swap 1 (lane ^ 32): kgrp 0, 1 keep block 2p and take
-                        // its columns 4 kgrp + 8 from kgrp + 2; kgrp 2, 3 keep
-                        // block 2p + 1 and take its columns 4 kgrp - 8
-                        const uint32_t x0 = lo ? a0 : b0, x1 = lo ? a1 : b1;
-                        const uint32_t y0 = (uint32_t)__shfl_xor((int)(lo ? b0 : a0), 32);
-                        const uint32_t y1 = (uint32_t)__shfl_xor((int)(lo ? b1 : a1), 32);
-                        // swap 2 (lane ^ 16): each lane keeps the four columns
-                        // of its target and takes the other four
-                        const uint32_t k0 = give_x ? y0 : x0, k1 = give_x ? y1 : x1;
-                        const uint32_t t0 = (uint32_t)__shfl_xor((int)(give_x ? x0 : y0), 16);
-                        const uint32_t t1 = (uint32_t)__shfl_xor((int)(give_x ? x1 : y1), 16);
+                        // swap 1 (lanes 0-31 <-> 32-63): lanes of kgrp 0, 1
+                        // keep block 2p, kgrp 2, 3 block 2p + 1; each then
+                        // holds that block's columns 4(k & 1) (first) and
+                        // 4(k & 1) + 8 (second), two per dword
+                        const auto s0 = __builtin_amdgcn_permlane32_swap(bf16x2_rne(A[0], A[1]),
+                                                                         bf16x2_rne(B[0], B[1]), false, false);
+                        const auto s1 = __builtin_amdgcn_permlane32_swap(bf16x2_rne(A[2], A[3]),
+                                                                         bf16x2_rne(B[2], B[3]), false, false);
+                        // swap 2 (16-lane rows 0 <-> 1, 2 <-> 3): even k end
+                        // with columns 0-3 and 4-7 of the block half they
+                        // keep, odd k with columns 8-11 and 12-15
+                        const auto t0 = __builtin_amdgcn_permlane16_swap(s0[0], s0[1], false, false);
+                        const auto t1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
                         if (m >= m_end) continue;
-                        const uint4 w = got_first ? make_uint4(t0, t1, k0, k1) : make_uint4(k0, k1, t0, t1);
+                        const uint4 w = make_uint4(t0[0], t1[0], t0[1], t1[1]);
                         const int64_t n = cn0 + 64 * wq + 32 * pq + 8 * kgrp;
                         *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(cbase) + m * p.ldc + n) = w;
                     }
