@@ -705,10 +705,17 @@ __global__ __launch_bounds__(kW4Threads) __attribute__((amdgpu_waves_per_eu(1, 1
                     mx[i] = v;
                 }
             }
+            // over the row's four lanes: each swap leaves a lane its own
+            // value and its partner's (in either order), so the max of the
+            // pair needs no select (maxima of non-negative floats compared
+            // as their bit patterns)
 #pragma unroll
             for (int i = 0; i < PMI; ++i) {
-                const float v = fmaxf(mx[i], __shfl_xor(mx[i], 16));
-                mx[i] = fmaxf(v, __shfl_xor(v, 32));
+                const uint32_t b = __float_as_uint(mx[i]);
+                const auto h = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+                const uint32_t v = h[0] > h[1] ? h[0] : h[1];
+                const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+                mx[i] = __uint_as_float(r[0] > r[1] ? r[0] : r[1]);
                 if (kgrp == 0) RowMax[wq][16 * i + lrow] = mx[i];
             }
             __syncthreads();
